@@ -1,0 +1,216 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for one context-parallel rank's exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+ * bench.py may load or call this library. It shares no code, header, table or helper with the
+ * HIP path in context_ring_attention_amd/, and it never includes anything from there.
+ *
+ * Pages cited (titles as published):
+ *   [CPEP]  "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두 축"
+ *           (m1ser4ble.github.io blog post).
+ *   [CPMTI] "Context Parallelism for Scalable Million-Token Inference"
+ *           (xllm-io.github.io paper review of arXiv 2411.01783).
+ *
+ * Every function is the plain definition written out: no blocking, no online rescaling, no
+ * fusion. Arithmetic is fp64 on inputs widened exactly from their fp32 (or bf16-rounded fp32)
+ * values. Threads only split independent output rows (OpenMP); each row is computed serially.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Load-balanced sharding.  [CPMTI §4 "负载均衡分片策略" with Fig. 2; the figure itself is not in the
+ * page text]: every CP rank gets about equal attention compute and equal KV memory, and a batch
+ * may hold sequences of different lengths.  Reading taken (the figure is missing): a range
+ * [a, b) of length L is cut into 2N chunks, chunk c = [a + floor(c*L/2N), a + floor((c+1)*L/2N)),
+ * and rank r owns chunk r followed by chunk 2N-1-r.  Ranges are visited in the order given.
+ * The global index of (seq s, position p) is base[s] + p, where base[s] is the sum of the
+ * lengths of sequences 0..s-1 and the length of a sequence is the largest range end given for it.
+ * ------------------------------------------------------------------------------------------ */
+int orc_shard_tokens(int n_ranges, const int32_t* seq_id, const int64_t* range_begin,
+                     const int64_t* range_end, int cp_world, int rank, int32_t* tok_seq,
+                     int64_t* tok_pos, int64_t* tok_global, int64_t max_tokens,
+                     int64_t* n_tokens) {
+  if (n_ranges < 0 || cp_world < 1 || rank < 0 || rank >= cp_world) return -1;
+  int n_seq = 0;
+  for (int i = 0; i < n_ranges; ++i) {
+    int s = seq_id ? seq_id[i] : i;
+    if (s < 0 || range_begin[i] < 0 || range_end[i] < range_begin[i]) return -1;
+    if (s + 1 > n_seq) n_seq = s + 1;
+  }
+  int64_t* seq_len = (int64_t*)calloc((size_t)n_seq + 1, sizeof(int64_t));
+  int64_t* base = (int64_t*)calloc((size_t)n_seq + 1, sizeof(int64_t));
+  for (int i = 0; i < n_ranges; ++i) {
+    int s = seq_id ? seq_id[i] : i;
+    if (range_end[i] > seq_len[s]) seq_len[s] = range_end[i];
+  }
+  for (int s = 1; s <= n_seq; ++s) base[s] = base[s - 1] + seq_len[s - 1];
+
+  int64_t count = 0;
+  int64_t n_chunks = 2 * (int64_t)cp_world;
+  for (int i = 0; i < n_ranges; ++i) {
+    int s = seq_id ? seq_id[i] : i;
+    int64_t a = range_begin[i];
+    int64_t len = range_end[i] - range_begin[i];
+    int64_t picks[2] = {rank, n_chunks - 1 - rank};
+    for (int w = 0; w < 2; ++w) {
+      int64_t c = picks[w];
+      int64_t lo = a + (c * len) / n_chunks;
+      int64_t hi = a + ((c + 1) * len) / n_chunks;
+      for (int64_t p = lo; p < hi; ++p) {
+        if (count < max_tokens) {
+          if (tok_seq) tok_seq[count] = s;
+          if (tok_pos) tok_pos[count] = p;
+          if (tok_global) tok_global[count] = base[s] + p;
+        }
+        ++count;
+      }
+    }
+  }
+  free(seq_len);
+  free(base);
+  *n_tokens = count;
+  return count <= max_tokens ? 0 : 1;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Attention of query tokens over a set of keys.
+ *
+ * [CPEP §5.1]: the output of token t is softmax(q_t K^T) V over the keys it may see; under the
+ *   causal mask q_t sees k_1..k_t (itself included) and never a later key.
+ * [CPEP §5.2]: prefill has many query rows against the keys; decode has one new query against
+ *   the whole cached K/V.
+ * [CPEP §8.2]: in GQA, consecutive query heads share one K/V head (Q_0..Q_7 -> K_0, ...), so
+ *   head h uses KV head h / (N_H / N_KV).
+ * [CPMTI §3 "核心公式"]: Q is [T, N_H, D_H]; K and V are [T+P, N_KV, D_H].
+ *
+ * Readings (the pages leave these open): the scores carry an explicit scale (1/sqrt(D_H) in the
+ * configurations; scale = 1 is the page's literal formula); key j is visible to query t iff
+ * they belong to the same sequence and, when causal, pos(j) <= pos(t).  The key set passed in
+ * may be any subset of a sequence (one KV shard, one decode split): the result is then the
+ * partial attention over that subset, with LSE = m + ln(sum exp(s_j - m)) in natural log.  An
+ * empty visible set gives O = 0 and LSE = -inf.
+ *
+ * q: [tq, n_h, d_h], k, v: [tk, n_kv, d_h] (fp32 values, widened to fp64).
+ * rows (optional): the query tokens to compute; outputs are then [n_rows, n_h, d_h] / [n_rows, n_h].
+ * ------------------------------------------------------------------------------------------ */
+int orc_attention(const float* q, const float* k, const float* v, int64_t tq, int64_t tk,
+                  int n_h, int n_kv, int d_h, const int32_t* q_seq, const int64_t* q_pos,
+                  const int32_t* k_seq, const int64_t* k_pos, int causal, double scale,
+                  const int64_t* rows, int64_t n_rows, double* o, double* lse) {
+  if (n_h < 1 || n_kv < 1 || n_h % n_kv != 0 || d_h < 1) return -1;
+  int group = n_h / n_kv;
+  int64_t n_out = rows ? n_rows : tq;
+  int64_t total = n_out * (int64_t)n_h;
+  int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t idx = 0; idx < total; ++idx) {
+    int64_t r = idx / n_h;
+    int h = (int)(idx % n_h);
+    int64_t t = rows ? rows[r] : r;
+    if (t < 0 || t >= tq) {
+      bad = 1;
+      continue;
+    }
+    int g = h / group;
+    const float* qv = q + (t * n_h + h) * (int64_t)d_h;
+    double* out = o + (r * n_h + h) * (int64_t)d_h;
+    double* acc = (double*)calloc((size_t)d_h, sizeof(double));
+
+    /* pass 1: the largest visible score */
+    double m = -INFINITY;
+    int64_t visible = 0;
+    for (int64_t j = 0; j < tk; ++j) {
+      if (k_seq[j] != q_seq[t]) continue;
+      if (causal && k_pos[j] > q_pos[t]) continue;
+      const float* kv = k + (j * n_kv + g) * (int64_t)d_h;
+      double s = 0.0;
+      for (int d = 0; d < d_h; ++d) s += (double)qv[d] * (double)kv[d];
+      s *= scale;
+      if (s > m) m = s;
+      ++visible;
+    }
+    if (visible == 0) {
+      for (int d = 0; d < d_h; ++d) out[d] = 0.0;
+      lse[r * n_h + h] = -INFINITY;
+      free(acc);
+      continue;
+    }
+
+    /* pass 2: softmax weights and the weighted sum of values */
+    double l = 0.0;
+    for (int64_t j = 0; j < tk; ++j) {
+      if (k_seq[j] != q_seq[t]) continue;
+      if (causal && k_pos[j] > q_pos[t]) continue;
+      const float* kv = k + (j * n_kv + g) * (int64_t)d_h;
+      const float* vv = v + (j * n_kv + g) * (int64_t)d_h;
+      double s = 0.0;
+      for (int d = 0; d < d_h; ++d) s += (double)qv[d] * (double)kv[d];
+      s *= scale;
+      double w = exp(s - m);
+      l += w;
+      for (int d = 0; d < d_h; ++d) acc[d] += w * (double)vv[d];
+    }
+    for (int d = 0; d < d_h; ++d) out[d] = acc[d] / l;
+    lse[r * n_h + h] = m + log(l);
+    free(acc);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Merge of partial attention results.  [CPMTI §3 "核心公式" (Pass-Q ends with an All2All merge of
+ * partial attention results) and §5 "关键实现细节" item 3 (merge attention)]; the page does not
+ * print the formula but calls both ring variants lossless and exact [CPMTI §2 "解决方案概述"].
+ * Reading: the combine that is exact for any split of a row's visible keys,
+ *   M = max_i LSE_i,  w_i = exp(LSE_i - M),  LSE = M + ln(sum_i w_i),  O = sum_i w_i O_i / sum_i w_i,
+ * with M = -inf (no part saw a key) giving O = 0 and LSE = -inf.
+ * o_parts[i]: [rows, d_h], lse_parts[i]: [rows].
+ * ------------------------------------------------------------------------------------------ */
+void orc_merge(int n_parts, const double* const* o_parts, const double* const* lse_parts,
+               int64_t rows, int d_h, double* o, double* lse) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double M = -INFINITY;
+    for (int i = 0; i < n_parts; ++i)
+      if (lse_parts[i][r] > M) M = lse_parts[i][r];
+    if (M == -INFINITY) {
+      for (int d = 0; d < d_h; ++d) o[r * d_h + d] = 0.0;
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double wsum = 0.0;
+    for (int d = 0; d < d_h; ++d) o[r * d_h + d] = 0.0;
+    for (int i = 0; i < n_parts; ++i) {
+      double w = exp(lse_parts[i][r] - M);
+      wsum += w;
+      for (int d = 0; d < d_h; ++d) o[r * d_h + d] += w * o_parts[i][r * d_h + d];
+    }
+    for (int d = 0; d < d_h; ++d) o[r * d_h + d] /= wsum;
+    lse[r] = M + log(wsum);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Decode split bounds.  [CPMTI §5 "软件栈": Flash Decoding with 256 splits for decode.]
+ * Reading: split c of a request with L cached keys covers [floor(c*L/S), floor((c+1)*L/S)).
+ * ------------------------------------------------------------------------------------------ */
+void orc_split_bounds(int64_t len, int n_splits, int c, int64_t* lo, int64_t* hi) {
+  *lo = ((int64_t)c * len) / n_splits;
+  *hi = ((int64_t)(c + 1) * len) / n_splits;
+}

@@ -1,0 +1,109 @@
+"""Pins for the oracle's load-balanced shard map (integer, exact).
+
+Source: "Context Parallelism for Scalable Million-Token Inference" (xllm-io review), section 4,
+load-balanced sharding (Fig. 2): equal compute and equal KV memory per rank, variable-length
+batches supported. The chunk layout (2N chunks, rank r owns r and 2N-1-r) is the reading stated
+for the tiny ring workload; tests/golden/shard_map_t256_cp4.txt holds its worked values.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shard_map_t256_cp4.txt")
+
+
+def _golden():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def _visible_pairs(q_seq, q_pos, k_seq, k_pos):
+    """Brute-force count of causal (query, key) pairs of the same sequence."""
+    total = 0
+    for s0 in range(0, len(q_pos), 512):
+        qs = q_seq[s0:s0 + 512, None]
+        qp = q_pos[s0:s0 + 512, None]
+        total += int(np.sum((k_seq[None, :] == qs) & (k_pos[None, :] <= qp)))
+    return total
+
+
+def test_golden_t256_cp4_layout_and_pair_counts():
+    gold = _golden()
+    N = 4
+    shards = [oracle.shard_tokens([(0, 0, 256)], N, r) for r in range(N)]
+    for row in gold:
+        r = row[0]
+        seq, pos, glob = shards[r]
+        expect = np.r_[np.arange(row[1], row[2]), np.arange(row[3], row[4])]
+        assert np.array_equal(pos, expect)
+        assert np.array_equal(glob, expect)
+        assert np.all(seq == 0)
+        counts = []
+        for t in range(N):
+            s = (r - t) % N
+            ks, kp, _ = shards[s]
+            counts.append(_visible_pairs(seq, pos, ks, kp))
+        assert counts == row[5:9]
+        assert sum(counts) == row[9]
+
+
+@pytest.mark.parametrize("L,N", [(256, 4), (257, 4), (7, 4), (3, 2), (1000, 8), (1, 1), (0, 3)])
+def test_ranks_partition_every_range_with_balanced_counts(L, N):
+    allpos = []
+    sizes = []
+    for r in range(N):
+        seq, pos, glob = oracle.shard_tokens([(0, 0, L)], N, r)
+        allpos.append(pos)
+        sizes.append(len(pos))
+    allpos = np.concatenate(allpos) if allpos else np.zeros(0)
+    assert np.array_equal(np.sort(allpos), np.arange(L))
+    # floor chunk edges: chunk sizes differ by at most one, so ranks differ by at most two
+    assert max(sizes) - min(sizes) <= 2
+
+
+def test_equal_compute_per_rank_when_divisible():
+    L, N = 4096, 4
+    C = L // (2 * N)
+    shards = [oracle.shard_tokens([(0, 0, L)], N, r) for r in range(N)]
+    for r in range(N):
+        qs, qp, _ = shards[r]
+        ks = np.concatenate([shards[s][0] for s in range(N)])
+        kp = np.concatenate([shards[s][1] for s in range(N)])
+        assert _visible_pairs(qs, qp, ks, kp) == 2 * N * C * C + C
+
+
+def test_persistent_kv_layout_per_rank():
+    # cached prefix [0, P) and new tokens [P, P+T) are sharded separately
+    P, T, N = 120 * 1024, 8 * 1024, 4
+    for r in range(N):
+        qs, qp, _ = oracle.shard_tokens([(0, P, P + T)], N, r)
+        ks, kp, kg = oracle.shard_tokens([(0, 0, P), (0, P, P + T)], N, r)
+        assert len(qp) == 2048 and len(kp) == 32768
+        assert np.array_equal(kg, kp)
+        c_new = T // 8
+        assert qp[0] == P + r * c_new and qp[-1] == P + (8 - r) * c_new - 1
+        assert np.sum(kp < P) == 2 * 15360 and np.sum(kp >= P) == 2 * 1024
+
+
+def test_varlen_batch_global_index_and_segments():
+    lens = [64 * 1024, 192 * 1024, 256 * 1024, 512 * 1024]
+    N = 8
+    base = np.cumsum([0] + lens[:-1])
+    sizes = []
+    for r in (0, 5, 7):
+        seq, pos, glob = oracle.shard_tokens([(i, 0, L) for i, L in enumerate(lens)], N, r)
+        sizes.append(len(pos))
+        assert np.array_equal(glob, base[seq] + pos)
+        # per sequence, chunk r then chunk 2N-1-r of C = L / 2N tokens each
+        for i, L in enumerate(lens):
+            C = L // (2 * N)
+            expect = np.r_[np.arange(r * C, (r + 1) * C), np.arange((2 * N - 1 - r) * C, (2 * N - r) * C)]
+            assert np.array_equal(pos[seq == i], expect)
+    assert sizes == [131072] * 3
