@@ -1,0 +1,272 @@
+"""Thin ctypes binding of libcpattn.so (the C ABI of include/cpattn.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory (``tensor.data_ptr()``) and streams
+(``torch.cuda.current_stream().cuda_stream``). There is no CPU fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcpattn.so")
+
+CP_OK, CP_E_ARG, CP_E_SHAPE, CP_E_UNSUPPORTED, CP_E_CAPACITY, CP_E_HIP = 0, -1, -2, -3, -4, -5
+CP_F32, CP_BF16 = 0, 1
+CP_MAX_SEGMENTS = 64
+CP_MAX_MERGE_PARTS = 64
+
+EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
+            "cp_decode_workspace_bytes", "cp_ring_pass_kv", "cp_ring_pass_q",
+            "cp_status_string", "cp_last_error")
+
+
+class CpSegment(ctypes.Structure):
+    """cp_segment: shard rows [local_start, local_start+len) hold positions
+    [pos_start, pos_start+len) of sequence seq_id."""
+    _fields_ = [("seq_id", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("pos_start", ctypes.c_int64), ("len", ctypes.c_int64),
+                ("local_start", ctypes.c_int64)]
+
+    def as_tuple(self):
+        return (self.seq_id, self.pos_start, self.len, self.local_start)
+
+
+class CpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def _status_name(status: int) -> str:
+    names = {0: "CP_OK", -1: "CP_E_ARG", -2: "CP_E_SHAPE", -3: "CP_E_UNSUPPORTED",
+             -4: "CP_E_CAPACITY", -5: "CP_E_HIP"}
+    return names.get(status, f"status {status}")
+
+
+def load():
+    """Load libcpattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m "
+                           "context_ring_attention_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    i32, i64 = ctypes.c_int, ctypes.c_int64
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    segp = ctypes.POINTER(CpSegment)
+    f = ctypes.c_float
+    lib.cp_shard_map.argtypes = [i32, i32p, i64p, i64p, i32, i32, segp, i32,
+                                 ctypes.POINTER(ctypes.c_int), i64p, i64, i64p]
+    lib.cp_partial_attn.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, segp, i32, segp, i32,
+                                    i32, f, vp, vp, i32, vp]
+    lib.cp_merge_lse.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, i32, vp, vp]
+    lib.cp_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f, vp, vp, vp,
+                                      i32, vp, vp]
+    lib.cp_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.cp_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.cp_ring_pass_kv.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
+                                    i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
+                                    vp, i32, vp, vp]
+    lib.cp_ring_pass_q.argtypes = [i32, ctypes.POINTER(vp), i64p, ctypes.POINTER(segp),
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
+                                   i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   ctypes.POINTER(vp), i32, ctypes.POINTER(vp), vp]
+    for name in ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
+                 "cp_ring_pass_kv", "cp_ring_pass_q"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.cp_status_string.argtypes = [ctypes.c_int]
+    lib.cp_status_string.restype = ctypes.c_char_p
+    lib.cp_last_error.argtypes = []
+    lib.cp_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != CP_OK:
+        raise CpError(status, load().cp_last_error().decode())
+
+
+def last_error() -> str:
+    return load().cp_last_error().decode()
+
+
+# ----------------------------------------------------------------------------------- helpers
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    if t.dtype == torch.float32:
+        return CP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def segments(rows: Sequence[Sequence[int]]):
+    """ctypes array of CpSegment from (seq_id, pos_start, len, local_start) tuples."""
+    arr = (CpSegment * max(1, len(rows)))()
+    for i, (s, p, n, loc) in enumerate(rows):
+        arr[i] = CpSegment(int(s), 0, int(p), int(n), int(loc))
+    return arr, len(rows)
+
+
+def _segarg(segs):
+    if isinstance(segs, tuple) and len(segs) == 2 and isinstance(segs[1], int):
+        return segs
+    return segments(segs)
+
+
+# ----------------------------------------------------------------------------------- entry points
+def shard_map(ranges, cp_world: int, rank: int, with_tokens: bool = True):
+    """cp_shard_map. ranges: list of (seq_id, begin, end).
+
+    Returns (list of (seq_id, pos_start, len, local_start), int64 global token indices or None).
+    """
+    lib = load()
+    n = len(ranges)
+    seq = np.ascontiguousarray([r[0] for r in ranges], dtype=np.int32)
+    beg = np.ascontiguousarray([r[1] for r in ranges], dtype=np.int64)
+    end = np.ascontiguousarray([r[2] for r in ranges], dtype=np.int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    n_segs = ctypes.c_int(0)
+    n_tok = ctypes.c_int64(0)
+    st = lib.cp_shard_map(n, seq.ctypes.data_as(i32p), beg.ctypes.data_as(i64p),
+                          end.ctypes.data_as(i64p), cp_world, rank, None, 0, ctypes.byref(n_segs),
+                          None, 0, ctypes.byref(n_tok))
+    if st not in (CP_OK, CP_E_CAPACITY):
+        _check(st)
+    segs = (CpSegment * max(1, n_segs.value))()
+    toks = np.zeros(max(1, n_tok.value), np.int64) if with_tokens else None
+    st = lib.cp_shard_map(n, seq.ctypes.data_as(i32p), beg.ctypes.data_as(i64p),
+                          end.ctypes.data_as(i64p), cp_world, rank, segs, n_segs.value,
+                          ctypes.byref(n_segs), toks.ctypes.data_as(i64p) if with_tokens else None,
+                          n_tok.value, ctypes.byref(n_tok))
+    _check(st)
+    rows = [segs[i].as_tuple() for i in range(n_segs.value)]
+    return rows, (toks[: n_tok.value] if with_tokens else None)
+
+
+def partial_attn(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: float, o, lse,
+                 accumulate: bool = False, stream=None):
+    """cp_partial_attn. q: [tq, n_h, d], k/v: [tk, n_kv, d] (same dtype), o fp32, lse fp32."""
+    lib = load()
+    qa, nq = _segarg(q_segs)
+    ka, nk = _segarg(kv_segs)
+    tq, n_h, d = q.shape
+    tk, n_kv = k.shape[0], k.shape[1]
+    _check(lib.cp_partial_attn(_ptr(q), _ptr(k), _ptr(v), tq, tk, n_h, n_kv, d, _dtype_code(q),
+                               qa, nq, ka, nk, int(causal), float(softmax_scale), _ptr(o), _ptr(lse),
+                               int(accumulate), _stream(stream)))
+
+
+def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None):
+    """cp_merge_lse over fp32 parts [rows, d] (any shape whose last dim is d)."""
+    lib = load()
+    n = len(o_parts)
+    d = o_parts[0].shape[-1]
+    rows = o_parts[0].numel() // d
+    op = (ctypes.c_void_p * n)(*[_ptr(t) for t in o_parts])
+    lp = (ctypes.c_void_p * n)(*[_ptr(t) for t in lse_parts])
+    _check(lib.cp_merge_lse(n, op, lp, rows, d, _ptr(o_out), _dtype_code(o_out), _ptr(lse_out),
+                            _stream(stream)))
+
+
+def decode_workspace_bytes(batch: int, n_h: int, d_h: int, n_splits: int) -> int:
+    return load().cp_decode_workspace_bytes(batch, n_h, d_h, n_splits)
+
+
+def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softmax_scale: float,
+                   ws_o, ws_lse, o_out, lse_out=None, stream=None):
+    """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device."""
+    lib = load()
+    B, n_h, d = q.shape
+    n_kv = k_cache.shape[1]
+    _check(lib.cp_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
+                                 _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
+                                 float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
+                                 _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,
+                 softmax_scale: float, o_out, lse_out=None, o_parts=None, lse_parts=None,
+                 o_acc=None, lse_acc=None, stream=None):
+    """cp_ring_pass_kv for one rank. k_shards/v_shards/kv_segs: per shard id."""
+    lib = load()
+    N = len(k_shards)
+    qa, nq = _segarg(q_segs)
+    tq, n_h, d = q.shape
+    n_kv = k_shards[0].shape[1]
+    vp = ctypes.c_void_p
+    segp = ctypes.POINTER(CpSegment)
+    ks = (vp * N)(*[_ptr(t) for t in k_shards])
+    vs = (vp * N)(*[_ptr(t) for t in v_shards])
+    tk = (ctypes.c_int64 * N)(*[t.shape[0] for t in k_shards])
+    seg_objs = [_segarg(s) for s in kv_segs]
+    kvs = (segp * N)(*[ctypes.cast(a, segp) for a, _ in seg_objs])
+    nkv = (ctypes.c_int * N)(*[n for _, n in seg_objs])
+    op = (vp * N)(*[_ptr(t) for t in o_parts]) if o_parts is not None else None
+    lp = (vp * N)(*[_ptr(t) for t in lse_parts]) if lse_parts is not None else None
+    _check(lib.cp_ring_pass_kv(_ptr(q), tq, qa, nq, N, rank, ks, vs, tk, kvs, nkv, n_h, n_kv, d,
+                               _dtype_code(q), int(causal), float(softmax_scale), op, lp,
+                               _ptr(o_acc), _ptr(lse_acc), _ptr(o_out), _dtype_code(o_out),
+                               _ptr(lse_out), _stream(stream)))
+
+
+def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, softmax_scale: float,
+                o_parts, lse_parts, o_out, lse_out=None, stream=None):
+    """cp_ring_pass_q over all ranks. o_parts/lse_parts: N*N buffers, slot q*N + s."""
+    lib = load()
+    N = len(q_shards)
+    vp = ctypes.c_void_p
+    segp = ctypes.POINTER(CpSegment)
+    n_h, d = q_shards[0].shape[1], q_shards[0].shape[2]
+    n_kv = k_shards[0].shape[1]
+    qs = (vp * N)(*[_ptr(t) for t in q_shards])
+    tq = (ctypes.c_int64 * N)(*[t.shape[0] for t in q_shards])
+    qseg_objs = [_segarg(s) for s in q_segs]
+    qsg = (segp * N)(*[ctypes.cast(a, segp) for a, _ in qseg_objs])
+    nqs = (ctypes.c_int * N)(*[n for _, n in qseg_objs])
+    ks = (vp * N)(*[_ptr(t) for t in k_shards])
+    vs = (vp * N)(*[_ptr(t) for t in v_shards])
+    tk = (ctypes.c_int64 * N)(*[t.shape[0] for t in k_shards])
+    kseg_objs = [_segarg(s) for s in kv_segs]
+    ksg = (segp * N)(*[ctypes.cast(a, segp) for a, _ in kseg_objs])
+    nks = (ctypes.c_int * N)(*[n for _, n in kseg_objs])
+    op = (vp * (N * N))(*[_ptr(t) for t in o_parts])
+    lp = (vp * (N * N))(*[_ptr(t) for t in lse_parts])
+    oo = (vp * N)(*[_ptr(t) for t in o_out])
+    lo = (vp * N)(*[_ptr(t) for t in lse_out]) if lse_out is not None else None
+    _check(lib.cp_ring_pass_q(N, qs, tq, qsg, nqs, ks, vs, tk, ksg, nks, n_h, n_kv, d,
+                              _dtype_code(q_shards[0]), int(causal), float(softmax_scale), op, lp,
+                              oo, _dtype_code(o_out[0]), lo, _stream(stream)))

@@ -1,0 +1,94 @@
+// cp_internal.h -- types shared by the host API (api.cpp) and the gfx950 kernels.
+//
+// Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
+// 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpattn.h"
+
+namespace cpk {
+
+// Compact copy of cp_segment for kernel arguments (validated to fit int32 on the host).
+struct Seg {
+  int32_t seq;
+  int32_t pos;  // position of the first token of the run within its sequence
+  int32_t len;  // tokens in the run
+  int32_t loc;  // first shard row of the run
+};
+
+constexpr int kMaxSegs = CP_MAX_SEGMENTS;
+constexpr int kMaxParts = CP_MAX_MERGE_PARTS;
+
+// Arguments of one partial-attention launch. Rows of the Q shard are handled per KV head group
+// as a flat row space per Q segment: row r of segment i is token loc + r / group, query head
+// g*group + r % group (consecutive heads share KV head g, [CPEP §8.2]). Each workgroup takes one
+// tile of rows; tiles are numbered in processing order: slots 0..n_q_segs-1 visit the Q segments
+// in `order`, and inside a segment tiles go from the last (largest positions, most causal work)
+// to the first, so the heaviest tiles start first.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int32_t n_h;
+  int32_t n_kv;
+  int32_t group;       // n_h / n_kv
+  int32_t causal;
+  int32_t accumulate;
+  int32_t n_q_segs;
+  int32_t n_kv_segs;
+  int32_t total_tiles;
+  float scale;         // softmax scale
+  float scale_log2;    // softmax scale * log2(e)
+  int32_t tile_prefix[kMaxSegs + 1];  // tiles before processing slot i
+  int8_t order[kMaxSegs];             // Q segment of processing slot i
+  Seg qs[kMaxSegs];
+  Seg ks[kMaxSegs];
+};
+
+struct MergeParams {
+  const float* o_parts[kMaxParts];
+  const float* lse_parts[kMaxParts];
+  void* o_out;
+  float* lse_out;
+  int64_t rows;
+  int32_t n_parts;
+  int32_t d_h;
+  int32_t out_bf16;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int64_t* kv_offset;
+  const int64_t* kv_len;
+  float* ws_o;
+  float* ws_lse;
+  void* o_out;
+  float* lse_out;
+  int32_t batch;
+  int32_t n_h;
+  int32_t n_kv;
+  int32_t group;
+  int32_t n_splits;
+  int32_t out_bf16;
+  float scale;
+  float scale_log2;
+};
+
+// Launchers (defined next to their kernels). Each returns the HIP launch status.
+hipError_t launch_attn_f32(const AttnParams& p, int d_h, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream);
+
+// Rows per workgroup tile of each attention kernel (the host plans tiles with these).
+constexpr int kTileRowsF32 = 64;
+constexpr int kTileRowsBf16 = 256;
+
+}  // namespace cpk

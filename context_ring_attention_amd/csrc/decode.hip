@@ -1,0 +1,269 @@
+// decode.hip -- split-KV decode: one new query token per request against its cached K/V,
+// split S ways into partial (O, LSE) results that are then merged.
+//
+// [CPMTI §5 "软件栈"]: decode uses Flash Decoding with 256 splits; [CPMTI §4 "解码阶段CP"]: decode
+// runs ring Pass-Q, i.e. partials over KV shards merged afterwards; [CPEP §5.2]: at decode one
+// query reads the whole KV cache; [CPEP §8.2]: the query heads of a group share their KV head.
+//
+// The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
+// against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
+// 16-head block) and walks its keys in blocks of 32:
+//  - S^T = K q^T on v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads per MFMA, K rows loaded from
+//    HBM straight into the A operand (each lane reads 64 contiguous bytes of one key row), q^T
+//    held in registers;
+//  - the V block goes through LDS in its row-major layout and comes back as the V^T operand of
+//    O^T += V^T P^T via ds_read_b64_tr_b16;
+//  - the next block's K and V loads are issued before the current block's math.
+// The merge kernel then combines the S partials of each (request, head) with the same
+// LSE-weighted rule as cp_merge_lse.
+//
+// Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
+// 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
+#include "device_common.h"
+
+namespace cpk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct DecCfg {
+  static constexpr int kBK = 32;                 // keys per block
+  static constexpr int kStride = D * 2 + 16;     // padded LDS row (bytes)
+  static constexpr int kKSteps = D / 32;         // MFMA k-steps over the head dimension
+  static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
+  static constexpr int kChunks = D / 8;          // 16-byte chunks per key row
+  static constexpr int kVLoads = kBK * kChunks / 64;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+  using C = DecCfg<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char vs[C::kBK * C::kStride];
+
+  const int c = blockIdx.x;  // split
+  const int b = blockIdx.y;  // request
+  const int hblocks = (p.group + 15) / 16;
+  const int g = blockIdx.z / hblocks;
+  const int h0 = (blockIdx.z % hblocks) * 16;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;  // head column of the 16x16 blocks
+  const int grp = lane >> 4;  // 0..3: k slice of the operands, row group of the accumulator
+  const int64_t L = p.kv_len[b];
+  const int64_t base = p.kv_offset[b];
+  const int64_t lo = ((int64_t)c * L) / p.n_splits;
+  const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;
+  const int n = (int)(hi - lo);
+
+  const __bf16* __restrict__ Kc = static_cast<const __bf16*>(p.k);
+  const __bf16* __restrict__ Vc = static_cast<const __bf16*>(p.v);
+
+  // q^T operand: lane holds q[head h0+col][grp*(D/4) + st*8 + e]
+  const int hig = h0 + col;
+  const bool head_ok = hig < p.group;
+  const int head = g * p.group + (head_ok ? hig : 0);
+  bf16x8 qreg[C::kKSteps];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.n_h + head) * D + grp * (D / 4);
+#pragma unroll
+    for (int st = 0; st < C::kKSteps; ++st) {
+      qreg[st] = *reinterpret_cast<const bf16x8*>(qp + st * 8);
+      if (!head_ok) qreg[st] = bf16x8{};
+    }
+  }
+
+  // key-row loads of one 32-key block: K into operand registers, V into staging registers
+  bf16x8 kreg[2][C::kKSteps];
+  uint4 vreg[C::kVLoads];
+  auto load_block = [&](int kb0, bf16x8 (&kr)[2][C::kKSteps], uint4 (&vr)[C::kVLoads]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int key = kb0 + 16 * h + col;
+      key = key < n ? key : n - 1;
+      const __bf16* kp = Kc + ((base + lo + key) * p.n_kv + g) * D + grp * (D / 4);
+#pragma unroll
+      for (int st = 0; st < C::kKSteps; ++st) kr[h][st] = *reinterpret_cast<const bf16x8*>(kp + st * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVLoads; ++i) {
+      const int idx = i * 64 + lane;
+      int key = kb0 + idx / C::kChunks;
+      key = key < n ? key : n - 1;
+      const int ch = idx % C::kChunks;
+      vr[i] = *reinterpret_cast<const uint4*>(Vc + ((base + lo + key) * p.n_kv + g) * D + ch * 8);
+    }
+  };
+  auto store_v = [&](const uint4 (&vr)[C::kVLoads]) {
+#pragma unroll
+    for (int i = 0; i < C::kVLoads; ++i) {
+      const int idx = i * 64 + lane;
+      *reinterpret_cast<uint4*>(vs + (idx / C::kChunks) * C::kStride + (idx % C::kChunks) * 16) = vr[i];
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[C::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // tr-read addressing: lane group grp reads 4 key rows, 4 lanes per row, 4 d per lane
+  const int j16 = lane & 15;
+  const int tr_row = 4 * grp + (j16 >> 2);
+  const int tr_col = 4 * (j16 & 3);
+
+  if (n > 0) {
+    load_block(0, kreg, vreg);
+    store_v(vreg);
+  }
+  __syncthreads();
+  for (int kb0 = 0; kb0 < n; kb0 += C::kBK) {
+    const bool has_next = kb0 + C::kBK < n;
+    bf16x8 knext[2][C::kKSteps];
+    uint4 vnext[C::kVLoads];
+    if (has_next) load_block(kb0 + C::kBK, knext, vnext);
+
+    // S^T (keys x heads) for the two 16-key halves
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < C::kKSteps; ++st)
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[h][st], qreg[st], s[h], 0, 0, 0);
+    }
+    // keys past the split are masked
+    if (kb0 + C::kBK > n) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kb0 + 16 * h + 4 * grp + v >= n) s[h][v] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[h][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * p.scale_log2);  // the block always holds a visible key
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    bf16x8 pt;
+    float rs = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[h][v], p.scale_log2, -mnew));
+        rs += e;
+        pt[4 * h + v] = (__bf16)e;
+      }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T: operand k = 4h + v <-> key 16h + 4*grp + v
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) {
+      const int off = tr_row * C::kStride + (db * 16 + tr_col) * 2;
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vs + off));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vs + off + 16 * C::kStride));
+      const i16x8 both = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pt,
+                                                          oacc[db], 0, 0, 0);
+    }
+    __syncthreads();
+    if (has_next) {
+      store_v(vnext);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int st = 0; st < C::kKSteps; ++st) kreg[h][st] = knext[h][st];
+    }
+    __syncthreads();
+  }
+
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (!head_ok) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int64_t prow = ((int64_t)b * p.n_splits + c) * p.n_h + head;
+  float* wo = p.ws_o + prow * D;
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db) {
+    const float4 o4 = make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
+    *reinterpret_cast<float4*>(wo + db * 16 + 4 * grp) = o4;
+  }
+  if (grp == 0) p.ws_lse[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+}
+
+// Merge of the S split partials of each (request, head).
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const int r = blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;  // b * n_h + head
+  const int c4 = threadIdx.x % kLanesPerRow;
+  if (r >= p.batch * p.n_h) return;
+  const int b = r / p.n_h;
+  const int head = r % p.n_h;
+  const int64_t stride = (int64_t)p.n_h;
+  const float* lse = p.ws_lse + (int64_t)b * p.n_splits * p.n_h + head;
+  const float* o = p.ws_o + ((int64_t)b * p.n_splits * p.n_h + head) * D + c4 * 4;
+  float M = -INFINITY;
+  for (int c = 0; c < p.n_splits; ++c) M = fmaxf(M, lse[c * stride]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int c = 0; c < p.n_splits; ++c) {
+      const float li = lse[c * stride];
+      if (li == -INFINITY) continue;
+      const float w = expf(li - M);
+      const float4 v = *reinterpret_cast<const float4*>(o + c * stride * D);
+      wsum += w;
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t orow = (int64_t)r * D + c4 * 4;
+  if (OUT_BF16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o_out) + orow) = v;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.o_out) + orow) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  if (c4 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
+  const int hblocks = (p.group + 15) / 16;
+  const dim3 grid(p.n_splits, p.batch, p.n_kv * hblocks);
+  const int rows_per_block = 256 / (d_h / 4);
+  const dim3 mgrid((p.batch * p.n_h + rows_per_block - 1) / rows_per_block);
+  if (d_h == 64) {
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64), 0, stream, p);
+    if (p.out_bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<64, true>), mgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64), 0, stream, p);
+    if (p.out_bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpk

@@ -1,0 +1,54 @@
+// device_common.h -- small device helpers shared by the gfx950 attention kernels.
+//
+// Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
+// 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "cp_internal.h"
+
+namespace cpk {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Workgroup tile -> (Q segment, tile index inside the segment). Slots are visited in the order
+// the host chose; inside a slot the first workgroup takes the segment's last tile.
+__device__ inline void locate_tile(const AttnParams& p, int block, int& seg, int& tile) {
+  int slot = 0;
+  while (slot + 1 < p.n_q_segs && p.tile_prefix[slot + 1] <= block) ++slot;
+  seg = p.order[slot];
+  const int n_tiles = p.tile_prefix[slot + 1] - p.tile_prefix[slot];
+  tile = n_tiles - 1 - (block - p.tile_prefix[slot]);
+}
+
+// Keys of KV run `ks` visible to a query at position qpos of the same sequence: with the causal
+// mask a query sees keys at positions <= its own ([CPEP §5.1]); they form a prefix of the run.
+__device__ inline int visible_prefix(const Seg& ks, int qpos, int causal) {
+  if (!causal) return ks.len;
+  int n = qpos - ks.pos + 1;
+  return n < 0 ? 0 : (n > ks.len ? ks.len : n);
+}
+
+// Merge of a running partial (lse_prev) with a new one (lse_new): the same LSE-weighted combine
+// as the merge kernel, for two parts. Returns the weights of the two parts' outputs and the
+// merged LSE; if neither part saw a key both weights are 0 and the LSE stays -inf.
+__device__ inline void running_merge_weights(float lse_prev, float lse_new, float& w_prev,
+                                             float& w_new, float& lse_out) {
+  const float M = fmaxf(lse_prev, lse_new);
+  if (M == -INFINITY) {
+    w_prev = 0.f;
+    w_new = 0.f;
+    lse_out = -INFINITY;
+    return;
+  }
+  const float a = expf(lse_prev - M);
+  const float b = expf(lse_new - M);
+  const float s = a + b;
+  w_prev = a / s;
+  w_new = b / s;
+  lse_out = M + logf(s);
+}
+
+}  // namespace cpk

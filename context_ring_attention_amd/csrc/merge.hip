@@ -1,0 +1,75 @@
+// merge.hip -- lossless LSE-weighted merge of partial attention results.
+//
+// Per row (query token, head): M = max_i LSE_i, w_i = exp(LSE_i - M),
+// O = sum_i w_i O_i / sum_i w_i, LSE = M + ln sum_i w_i; a row no part saw gives O = 0,
+// LSE = -inf ([CPMTI §3 "核心公式": Pass-Q ends with an All2All merge of partial attention
+// results; §5 "关键实现细节" item 3; the ring variants are lossless and exact, §2).
+//
+// HBM-bound: D/4 lanes share a row and move 16 bytes each; parts whose LSE is -inf (they saw no
+// key of this row, which the load-balanced layout produces in every ring step) are not read.
+//
+// Pages cited: [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (review).
+#include "device_common.h"
+
+namespace cpk {
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int c4 = threadIdx.x % kLanesPerRow;
+  if (row >= p.rows) return;
+
+  float M = -INFINITY;
+  for (int i = 0; i < p.n_parts; ++i) M = fmaxf(M, p.lse_parts[i][row]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < p.n_parts; ++i) {
+      const float li = p.lse_parts[i][row];
+      if (li == -INFINITY) continue;
+      const float w = expf(li - M);
+      const float4 o = *reinterpret_cast<const float4*>(p.o_parts[i] + row * D + c4 * 4);
+      wsum += w;
+      acc.x = fmaf(w, o.x, acc.x);
+      acc.y = fmaf(w, o.y, acc.y);
+      acc.z = fmaf(w, o.z, acc.z);
+      acc.w = fmaf(w, o.w, acc.w);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  acc.x *= inv;
+  acc.y *= inv;
+  acc.z *= inv;
+  acc.w *= inv;
+  if (OUT_BF16) {
+    __bf16* out = static_cast<__bf16*>(p.o_out) + row * D + c4 * 4;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
+    *reinterpret_cast<bf16x4*>(out) = v;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.o_out) + row * D + c4 * 4) = acc;
+  }
+  if (c4 == 0 && p.lse_out) p.lse_out[row] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  const int rows_per_block = 256 / (p.d_h / 4);
+  const int64_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (p.d_h == 64) {
+    if (p.out_bf16)
+      hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, p);
+  } else {
+    if (p.out_bf16)
+      hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpk

@@ -1,0 +1,188 @@
+/*
+ * cpattn.h -- C ABI of the MI355X (gfx950) context-parallel ring attention library.
+ *
+ * One context-parallel (CP) rank's exact GQA attention: a query shard attends, block by block, to
+ * each key/value shard of the ring; each step yields a partial output plus its log-sum-exp, and
+ * the partials are merged without loss. Decode splits the KV cache and merges the same way.
+ *
+ * Pages cited (titles as published):
+ *   [CPEP]  "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두 축"
+ *           (m1ser4ble.github.io blog post).
+ *   [CPMTI] "Context Parallelism for Scalable Million-Token Inference"
+ *           (xllm-io.github.io review of arXiv 2411.01783).
+ *
+ * Conventions for every entry point:
+ *  - Memory is owned by the caller. The library never allocates, frees or synchronises device
+ *    memory; "device" pointers must point to memory on the current HIP device.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the default stream) and return. The
+ *    return value reports argument validation and launch errors only; faults during execution
+ *    show up at the caller's next synchronisation.
+ *  - On a negative status nothing was launched and no output was written; cp_last_error() holds
+ *    a message (thread-local).
+ *  - Layouts are dense and row-major: Q [T_q, N_H, D_H], K and V [T_k, N_KV, D_H] ([CPMTI §3
+ *    "核心公式"]). Query head h reads KV head h / (N_H / N_KV): consecutive heads share a KV head
+ *    ([CPEP §8.2]).
+ *  - Scores are softmax_scale * q.k; LSE is the natural-log log-sum-exp of those scores over the
+ *    keys a row saw. A row that saw no key has O = 0 and LSE = -inf.
+ *  - Supported: D_H in {64, 128}; inputs fp32 or bf16; token counts below 2^31.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CP_OK = 0,
+  CP_E_ARG = -1,         /* null pointer, negative size, bad enum value */
+  CP_E_SHAPE = -2,       /* inconsistent shapes (N_H % N_KV != 0, segment outside its shard, ...) */
+  CP_E_UNSUPPORTED = -3, /* valid but not implemented (D_H not 64/128, dtype combination) */
+  CP_E_CAPACITY = -4,    /* an output buffer or a fixed table is too small */
+  CP_E_HIP = -5          /* the HIP runtime reported an error at launch */
+} cp_status;
+
+typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+
+/* A run of tokens of one sequence stored contiguously in a shard: shard rows
+   [local_start, local_start + len) hold positions [pos_start, pos_start + len) of sequence
+   seq_id. Positions count from 0 at the first token of the sequence (cached tokens first). */
+typedef struct {
+  int32_t seq_id;
+  int32_t reserved; /* set to 0 */
+  int64_t pos_start;
+  int64_t len;
+  int64_t local_start;
+} cp_segment;
+
+/* Largest segment table cp_partial_attn accepts per shard (tables travel in kernel arguments). */
+#define CP_MAX_SEGMENTS 64
+/* Largest number of parts cp_merge_lse merges in one call. */
+#define CP_MAX_MERGE_PARTS 64
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_shard_map -- load-balanced sharding ([CPMTI §4 "负载均衡分片策略", Fig. 2]: each rank gets
+ * equal attention compute and equal KV memory; batches of different lengths are supported).
+ * Each range [range_begin[i], range_end[i]) of sequence seq_id[i] (seq_id NULL: sequence i) is
+ * cut into 2*cp_world chunks with edges begin + floor(c*L/(2*cp_world)); rank `rank` owns chunk
+ * `rank` and chunk 2*cp_world-1-rank. Ranges are visited in order, and each owned non-empty chunk
+ * becomes one segment, in that order. Host-only, integer, launches nothing.
+ *   segs_out:   host, caller-owned, capacity max_segs; *n_segs_out = segments needed.
+ *   tokens_out: optional (NULL ok), host, capacity max_tokens: for each local token in order, its
+ *               packed global index base[seq] + pos, where base[s] is the sum of the lengths of
+ *               sequences 0..s-1 and a sequence's length is the largest range_end given for it.
+ *               *n_tokens_out (optional) = local token count.
+ * Returns CP_E_CAPACITY (with the counts set) if a buffer is too small, CP_E_ARG on bad ranges.
+ * ------------------------------------------------------------------------------------------- */
+int cp_shard_map(int n_ranges, const int32_t* seq_id, const int64_t* range_begin,
+                 const int64_t* range_end, int cp_world, int rank, cp_segment* segs_out,
+                 int max_segs, int* n_segs_out, int64_t* tokens_out, int64_t max_tokens,
+                 int64_t* n_tokens_out);
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_partial_attn -- one ring step: exact attention of a Q shard over one KV shard, producing
+ * the partial output and its LSE ([CPMTI §3 "核心公式": each rank computes the partial attention
+ * of its local Q against the KV it holds; [CPEP §5.1] per-token attention and causal mask;
+ * [CPEP §4.1]/§6 block-wise attention with online softmax).
+ *   q: device [tq, n_h, d_h]; k, v: device [tk, n_kv, d_h]; dtype in_dtype (all three).
+ *   q_segs / kv_segs: host tables (at most CP_MAX_SEGMENTS each) describing which sequence and
+ *     positions every shard row holds; rows outside all segments are not read or written.
+ *   causal: key visible iff same sequence and key position <= query position; 0: same sequence.
+ *   o: device fp32 [tq, n_h, d_h]; lse: device fp32 [tq, n_h].
+ *   accumulate = 0: overwrite (o, lse) with this step's partial.
+ *   accumulate = 1: (o, lse) hold a running partial; merge this step into it in place.
+ * bf16 inputs run on MFMA with fp32 accumulation (probabilities rounded to bf16 before P.V);
+ * fp32 inputs run in fp32 arithmetic throughout.
+ * ------------------------------------------------------------------------------------------- */
+int cp_partial_attn(const void* q, const void* k, const void* v, int64_t tq, int64_t tk, int n_h,
+                    int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs, int n_q_segs,
+                    const cp_segment* kv_segs, int n_kv_segs, int causal, float softmax_scale,
+                    float* o, float* lse, int accumulate, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_merge_lse -- lossless merge of partial results ([CPMTI §3 "核心公式": Pass-Q ends with an
+ * All2All merge of partial attention; §5 "关键实现细节" item 3, merge attention; the variants are
+ * exact, §2 "解决方案概述"). Per row: M = max_i LSE_i, w_i = exp(LSE_i - M),
+ * O = sum_i w_i O_i / sum_i w_i, LSE = M + ln(sum_i w_i); rows no part saw give O = 0, LSE = -inf.
+ *   o_parts, lse_parts: host arrays of n_parts (1..CP_MAX_MERGE_PARTS) device pointers to fp32
+ *     [rows, d_h] and [rows]. rows = T_q * N_H.
+ *   o_out: device [rows, d_h] in out_dtype (fp32 or bf16, round to nearest even);
+ *   lse_out: device fp32 [rows] (may be NULL). o_out may alias o_parts[0] when out_dtype is fp32.
+ * ------------------------------------------------------------------------------------------- */
+int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                 int64_t rows, int d_h, void* o_out, cp_dtype out_dtype, float* lse_out,
+                 void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_decode_splitkv -- decode attention, one new query token per request against its KV cache,
+ * split n_splits ways and merged ([CPMTI §5 "软件栈": Flash Decoding with 256 splits; §4 decode
+ * uses ring Pass-Q; [CPEP §5.2] decode: one q against the whole cache).
+ *   q: device [batch, n_h, d_h]; k_cache, v_cache: device [sum L_b, n_kv, d_h], request b at rows
+ *     [kv_offset[b], kv_offset[b] + kv_len[b]); kv_offset, kv_len: device int64 [batch].
+ *   Split c of request b covers cache rows [floor(c*L_b/S), floor((c+1)*L_b/S)); every cached key
+ *   is visible (the query comes after the cache).
+ *   ws_o: device fp32 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
+ *     the per-split partials (caller-owned workspace of cp_decode_workspace_bytes bytes, laid out
+ *     ws_o first, then ws_lse at byte offset batch*n_splits*n_h*d_h*4).
+ *   o_out: device [batch, n_h, d_h] in out_dtype; lse_out: device fp32 [batch, n_h] (may be NULL).
+ * in_dtype must be CP_BF16. 1 <= n_splits <= 1024.
+ * ------------------------------------------------------------------------------------------- */
+int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                      int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
+                      float* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
+                      void* stream);
+size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits);
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_ring_pass_kv -- one rank's ring Pass-KV on one device ([CPMTI §3 "核心公式": each rank keeps
+ * its Q shard while KV shards travel the ring for N-1 rounds; §3 Fig. 3). At step t the rank
+ * holds KV shard (rank - t) mod cp_world and runs cp_partial_attn on it.
+ *   k_shards, v_shards, tk, kv_segs, n_kv_segs: host arrays indexed by shard id [cp_world].
+ *   Mode "partials" (o_parts != NULL): step t writes o_parts[t] / lse_parts[t] (device fp32
+ *     [tq*n_h*d_h] / [tq*n_h]); the N partials are then merged with cp_merge_lse into o_out.
+ *   Mode "running" (o_parts == NULL): steps accumulate into o_acc / lse_acc (device fp32), and
+ *     o_out receives the result in out_dtype (o_out may equal o_acc when out_dtype is fp32).
+ *   lse_out may be NULL.
+ * ------------------------------------------------------------------------------------------- */
+int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
+                    int cp_world, int rank, const void* const* k_shards,
+                    const void* const* v_shards, const int64_t* tk,
+                    const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
+                    int d_h, cp_dtype in_dtype, int causal, float softmax_scale,
+                    float* const* o_parts, float* const* lse_parts, float* o_acc, float* lse_acc,
+                    void* o_out, cp_dtype out_dtype, float* lse_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * cp_ring_pass_q -- ring Pass-Q over all cp_world ranks on one device ([CPMTI §3 "核心公式": KV
+ * shards stay on their rank while Q shards travel the ring for N-1 rounds, then an All2All
+ * returns every partial to its Q owner, where they are merged). At step t the rank owning KV
+ * shard s hosts Q shard q = (s - t) mod cp_world; the partial lands in slot q*cp_world + s (on
+ * one device the All2All is this placement). Each Q shard's cp_world partials are then merged in
+ * ascending s into o_out[q] / lse_out[q].
+ *   q_shards, tq, q_segs, n_q_segs: host arrays [cp_world] (Q shard per rank).
+ *   k_shards ... n_kv_segs: host arrays [cp_world] (KV shard per rank).
+ *   o_parts, lse_parts: host arrays [cp_world*cp_world] of device fp32 buffers, slot q*N + s
+ *     sized for Q shard q.
+ *   o_out, lse_out: host arrays [cp_world] of device outputs (lse_out may be NULL, or hold NULLs).
+ * ------------------------------------------------------------------------------------------- */
+int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
+                   const cp_segment* const* q_segs, const int* n_q_segs,
+                   const void* const* k_shards, const void* const* v_shards, const int64_t* tk,
+                   const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
+                   int d_h, cp_dtype in_dtype, int causal, float softmax_scale,
+                   float* const* o_parts, float* const* lse_parts, void* const* o_out,
+                   cp_dtype out_dtype, float* const* lse_out, void* stream);
+
+/* Human-readable name of a cp_status value. */
+const char* cp_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* cp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CPATTN_H */

@@ -1,0 +1,83 @@
+"""Builders of ring workloads for the parity tests and the bench.
+
+The HIP side takes its shard layout from the library's cp_shard_map and the oracle side from the
+oracle's own shard map (the two are checked bit-exact elsewhere); both draw Q/K/V from the seeded
+generators in synth_inputs, per global token index.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import synth_inputs as si
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(name: str):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+class Shard:
+    """One rank's tokens: product segments (for the library) and device tensors."""
+
+    def __init__(self, segs, tokens):
+        self.segs = segs          # list of (seq_id, pos_start, len, local_start)
+        self.tokens = tokens      # global packed token index per local row
+        self.q = self.k = self.v = None
+
+
+def product_shards(ranges, N, ranks=None):
+    from context_ring_attention_amd import binding as cp
+    ranks = range(N) if ranks is None else ranks
+    return {r: Shard(*cp.shard_map(ranges, N, r)) for r in ranks}
+
+
+def device_tensor(seed, tid, tokens, shape, std, dtype, device="cuda"):
+    x = si.normal_tokens(seed, tid, tokens, shape, std)
+    xd, _ = si.to_dtype(x, dtype)
+    return xd.contiguous().to(device)
+
+
+def oracle_view(seed, tid, tokens, shape, std, dtype):
+    """The exact fp32 values the device holds for these tokens (bf16-rounded when bf16)."""
+    x = si.normal_tokens(seed, tid, tokens, shape, std)
+    _, xf = si.to_dtype(x, dtype)
+    return xf.numpy()
+
+
+def seq_pos_of(ranges, tokens):
+    """(seq, pos) of packed global token indices under the same base rule as the shard map."""
+    lens = {}
+    for s, b, e in ranges:
+        lens[s] = max(lens.get(s, 0), e)
+    ids = sorted(lens)
+    bases = np.cumsum([0] + [lens[i] for i in ids[:-1]])
+    tokens = np.asarray(tokens, np.int64)
+    idx = np.searchsorted(bases, tokens, side="right") - 1
+    seq = np.asarray(ids, np.int64)[idx]
+    pos = tokens - bases[idx]
+    return seq.astype(np.int32), pos
+
+
+def sample_rows(segs, n_random, seed):
+    """Local rows to check at full size: first and last row of every segment plus random rows."""
+    rows = set()
+    for _, _, n, loc in segs:
+        rows.add(loc)
+        rows.add(loc + n - 1)
+        rows.add(loc + n // 2)
+    total = sum(n for _, _, n, _ in segs)
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.integers(0, total, n_random))
+    return np.array(sorted(rows), np.int64)
+
+
+def scale_of(d_h: int) -> float:
+    return 1.0 / math.sqrt(d_h)

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, the
+host-only shard map matches the oracle bit for bit, and invalid arguments are rejected with the
+documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from context_ring_attention_amd import binding as cp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = cp.load()
+    names = _declared_functions()
+    assert set(names) >= {"cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv"}
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(cp.EXPORTED)
+
+
+def _oracle_segments(ranges, N, r):
+    seq, pos, glob = oracle.shard_tokens(ranges, N, r)
+    return seq, pos, glob
+
+
+def _expand(segs):
+    seq, pos, loc = [], [], []
+    for s, p, n, l in segs:
+        seq += [s] * n
+        pos += list(range(p, p + n))
+        loc += list(range(l, l + n))
+    return np.array(seq, np.int64), np.array(pos, np.int64), np.array(loc, np.int64)
+
+
+CASES = [
+    ([(0, 0, 256)], 4),                                         # the tiny ring
+    ([(0, 0, 128 * 1024)], 4),                                  # 128K at CP4
+    ([(0, 0, 120 * 1024), (0, 120 * 1024, 128 * 1024)], 4),     # cached prefix + new tokens
+    ([(0, 120 * 1024, 128 * 1024)], 4),                         # the new tokens alone
+    ([(i, 0, L) for i, L in enumerate([64 * 1024, 192 * 1024, 256 * 1024, 512 * 1024])], 8),
+    ([(0, 0, 257), (1, 0, 3), (2, 0, 0), (3, 5, 13)], 4),        # ragged and degenerate ranges
+    ([(2, 0, 10), (0, 0, 7)], 3),                               # ids out of order, a missing id
+    ([(0, 0, 1)], 1),
+]
+
+
+@pytest.mark.parametrize("ranges,N", CASES)
+def test_shard_map_bit_exact_against_oracle(ranges, N):
+    for r in range(N):
+        segs, toks = cp.shard_map(ranges, N, r)
+        seq, pos, loc = _expand(segs)
+        oseq, opos, oglob = _oracle_segments(ranges, N, r)
+        assert np.array_equal(seq, oseq) and np.array_equal(pos, opos)
+        assert np.array_equal(loc, np.arange(len(loc)))
+        assert np.array_equal(toks, oglob)
+        assert all(n > 0 for _, _, n, _ in segs)   # empty chunks are not emitted
+
+
+def test_shard_map_capacity_and_argument_errors():
+    lib = cp.load()
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    b = np.array([0], np.int64)
+    e = np.array([256], np.int64)
+    n_segs = ctypes.c_int(0)
+    n_tok = ctypes.c_int64(0)
+    segs = (cp.CpSegment * 1)()
+    st = lib.cp_shard_map(1, None, b.ctypes.data_as(i64p), e.ctypes.data_as(i64p), 4, 1, segs, 1,
+                          ctypes.byref(n_segs), None, 0, ctypes.byref(n_tok))
+    assert st == cp.CP_E_CAPACITY and n_segs.value == 2 and n_tok.value == 64
+    st = lib.cp_shard_map(1, None, b.ctypes.data_as(i64p), e.ctypes.data_as(i64p), 4, 4, segs, 1,
+                          ctypes.byref(n_segs), None, 0, None)
+    assert st == cp.CP_E_ARG and "rank" in cp.last_error()
+    bad_e = np.array([-1], np.int64)
+    st = lib.cp_shard_map(1, None, b.ctypes.data_as(i64p), bad_e.ctypes.data_as(i64p), 4, 0, segs, 1,
+                          ctypes.byref(n_segs), None, 0, None)
+    assert st == cp.CP_E_ARG
+
+
+def _partial(**kw):
+    lib = cp.load()
+    seg, n = cp.segments([(0, 0, 16, 0)])
+    args = dict(q=16, k=16, v=16, tq=16, tk=16, n_h=4, n_kv=1, d_h=64, dt=cp.CP_BF16, qs=seg, nq=n,
+                ks=seg, nk=n, causal=1, scale=0.125, o=16, lse=16, acc=0)
+    args.update(kw)
+    return lib.cp_partial_attn(args["q"], args["k"], args["v"], args["tq"], args["tk"], args["n_h"],
+                               args["n_kv"], args["d_h"], args["dt"], args["qs"], args["nq"],
+                               args["ks"], args["nk"], args["causal"], args["scale"], args["o"],
+                               args["lse"], args["acc"], None)
+
+
+def test_partial_attn_rejects_bad_arguments_without_launching():
+    assert _partial(n_h=6, n_kv=4) == cp.CP_E_SHAPE
+    assert _partial(d_h=96) == cp.CP_E_UNSUPPORTED
+    assert _partial(dt=7) == cp.CP_E_ARG
+    assert _partial(scale=0.0) == cp.CP_E_ARG
+    assert _partial(scale=float("nan")) == cp.CP_E_ARG
+    assert _partial(acc=2) == cp.CP_E_ARG
+    assert _partial(q=0) == cp.CP_E_ARG
+    assert _partial(q=8) == cp.CP_E_ARG            # not 16-byte aligned
+    big, n = cp.segments([(0, 0, 17, 0)])
+    assert _partial(qs=big, nq=n) == cp.CP_E_SHAPE   # runs past the shard
+    assert "outside the shard" in cp.last_error()
+    many, n = cp.segments([(0, i, 1, 0) for i in range(65)])
+    assert _partial(ks=many, nk=n) == cp.CP_E_CAPACITY
+    neg, n = cp.segments([(-1, 0, 1, 0)])
+    assert _partial(ks=neg, nk=n) == cp.CP_E_SHAPE
+    assert _partial(tq=1 << 31) == cp.CP_E_UNSUPPORTED
+    # nothing to do is not an error (no launch either)
+    assert _partial(nq=0) == cp.CP_OK
+
+
+def test_merge_and_decode_reject_bad_arguments():
+    lib = cp.load()
+    vp = ctypes.c_void_p
+    parts = (vp * 1)(16)
+    assert lib.cp_merge_lse(0, parts, parts, 8, 64, 16, cp.CP_F32, None, None) == cp.CP_E_CAPACITY
+    assert lib.cp_merge_lse(65, parts, parts, 8, 64, 16, cp.CP_F32, None, None) == cp.CP_E_CAPACITY
+    assert lib.cp_merge_lse(1, parts, parts, 8, 80, 16, cp.CP_F32, None, None) == cp.CP_E_UNSUPPORTED
+    assert lib.cp_merge_lse(1, parts, parts, 8, 64, 16, cp.CP_BF16, None, None) == cp.CP_E_ARG  # alias
+    assert lib.cp_merge_lse(1, parts, parts, 0, 64, 32, cp.CP_F32, None, None) == cp.CP_OK
+    dec = lib.cp_decode_splitkv
+    assert dec(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_F32, 256, 0.1, 16, 16, 16, cp.CP_F32, None,
+               None) == cp.CP_E_UNSUPPORTED
+    assert dec(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 0, 0.1, 16, 16, 16, cp.CP_F32, None,
+               None) == cp.CP_E_UNSUPPORTED
+    assert dec(16, 16, 16, 16, 16, 2, 16, 3, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16, cp.CP_F32, None,
+               None) == cp.CP_E_SHAPE
+    assert dec(0, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16, cp.CP_F32, None,
+               None) == cp.CP_E_ARG
+    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 + 1) * 4
+    assert lib.cp_status_string(cp.CP_E_HIP) == b"CP_E_HIP"

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on the same seeded inputs.
+
+Tolerances (max-abs): fp32 inputs 1e-5 on O and LSE; bf16 inputs 2e-2 on O and 1e-3 on LSE.
+Rows that saw no key must be O = 0, LSE = -inf on both sides. Small cases compare every element
+(several workgroup tiles, ragged chunk lengths); full-size workloads compare sampled rows, each
+against the oracle's exact result over its full visible key set.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from ring_cases import device_tensor, log, oracle_view, product_shards, sample_rows, scale_of
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_ring_attention_amd import binding
+    binding.load()
+
+
+def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
+    tol_o, tol_l = TOL[dtype]
+    o_g = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
+    l_g = lse_gpu.float().cpu().numpy().astype(np.float64).reshape(lse_ref.shape)
+    inf_g, inf_r = np.isneginf(l_g), np.isneginf(lse_ref)
+    assert np.array_equal(inf_g, inf_r), f"{what}: empty-row pattern differs"
+    assert np.all(np.isfinite(o_g)), f"{what}: non-finite output"
+    assert np.all(o_g[inf_r] == 0.0), f"{what}: empty rows must be zero"
+    err_o = float(np.max(np.abs(o_g - o_ref))) if o_ref.size else 0.0
+    fin = ~inf_r
+    err_l = float(np.max(np.abs(l_g[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    log(f"  {what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} rows={lse_ref.size} empty={int(inf_r.sum())}")
+    assert err_o <= tol_o and err_l <= tol_l, what
+
+
+def _oracle_keys(ranges, N, shard_ids, seed, n_kv, d, std, dtype):
+    ks, vs, sq, ps = [], [], [], []
+    for s in shard_ids:
+        seq, pos, glob = oracle.shard_tokens(ranges, N, s)
+        ks.append(oracle_view(seed, si.TID_K, glob, (n_kv, d), std, dtype))
+        vs.append(oracle_view(seed, si.TID_V, glob, (n_kv, d), std, dtype))
+        sq.append(seq)
+        ps.append(pos)
+    return np.concatenate(ks), np.concatenate(vs), np.concatenate(sq), np.concatenate(ps)
+
+
+def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, mode="partials",
+                check_partials=True, n_sample=None, std=None):
+    from context_ring_attention_amd import binding as cp
+    ranges = [(i, 0, L) for i, L in enumerate(seqs)]
+    std = std if std is not None else (1.0 / np.sqrt(d) if dtype == "f32" else 1.0)
+    scale = scale_of(d)
+    ranks = list(range(N)) if ranks is None else ranks
+    sh = product_shards(ranges, N)
+    for s in sh.values():
+        s.k = device_tensor(seed, si.TID_K, s.tokens, (n_kv, d), std, dtype)
+        s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype)
+    for r in ranks:
+        log(f"pass-kv seqs={seqs} N={N} rank={r} n_h={n_h} n_kv={n_kv} d={d} {dtype} mode={mode} causal={causal}")
+        q = device_tensor(seed, si.TID_Q, sh[r].tokens, (n_h, d), std, dtype)
+        tq = q.shape[0]
+        o_out = torch.empty(tq, n_h, d, dtype=torch.float32, device="cuda")
+        lse_out = torch.empty(tq, n_h, dtype=torch.float32, device="cuda")
+        kw = {}
+        if mode == "partials":
+            kw["o_parts"] = [torch.full((tq, n_h, d), float("nan"), device="cuda") for _ in range(N)]
+            kw["lse_parts"] = [torch.empty(tq, n_h, device="cuda") for _ in range(N)]
+        else:
+            kw["o_acc"] = torch.empty(tq, n_h, d, device="cuda")
+            kw["lse_acc"] = torch.empty(tq, n_h, device="cuda")
+        cp.ring_pass_kv(q, sh[r].segs, r, [sh[s].k for s in range(N)], [sh[s].v for s in range(N)],
+                        [sh[s].segs for s in range(N)], causal, scale, o_out, lse_out, **kw)
+        torch.cuda.synchronize()
+
+        q_seq, q_pos, q_glob = oracle.shard_tokens(ranges, N, r)
+        qf = oracle_view(seed, si.TID_Q, q_glob, (n_h, d), std, dtype)
+        rows = sample_rows(sh[r].segs, n_sample, seed + r) if n_sample else None
+        kf, vf, kseq, kpos = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype)
+        o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
+                                        scale, rows=rows)
+        sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
+        assert_close(o_out[sel], lse_out[sel], o_ref, l_ref, dtype, f"rank {r} merged")
+        if mode == "partials" and check_partials:
+            for t in range(N):
+                s = (r - t) % N
+                kf, vf, kseq, kpos = _oracle_keys(ranges, N, [s], seed, n_kv, d, std, dtype)
+                o_p, l_p = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
+                                            scale, rows=rows)
+                assert_close(kw["o_parts"][t][sel], kw["lse_parts"][t][sel], o_p, l_p, dtype,
+                             f"rank {r} step {t} (kv shard {s})")
+
+
+# --------------------------------------------------------------------------- small, every element
+def test_tiny_ring_fp32_all_ranks():
+    """The tiny ring: T=256, 4 query heads, 1 KV head, D=64, fp32, CP=4, all partials + merge."""
+    run_pass_kv([256], 4, 4, 1, 64, "f32")
+
+
+def test_tiny_ring_fp32_running_merge():
+    run_pass_kv([256], 4, 4, 1, 64, "f32", mode="running")
+
+
+def test_fp32_ragged_multi_sequence_d128_gqa():
+    run_pass_kv([77, 300, 5], 3, 8, 2, 128, "f32", seed=1)
+
+
+def test_bf16_ring_ragged_two_sequences():
+    run_pass_kv([1000, 2333], 4, 16, 1, 128, "bf16", ranks=[0, 3])
+
+
+def test_bf16_ring_running_merge_bf16_d64_gqa4():
+    run_pass_kv([700, 1500], 4, 8, 2, 64, "bf16", seed=2, mode="running", ranks=[1, 2])
+
+
+def test_bf16_degenerate_shapes():
+    run_pass_kv([1], 1, 16, 1, 128, "bf16", seed=3)                   # a single token, no ring
+    run_pass_kv([3, 9, 1], 2, 4, 4, 64, "bf16", seed=4)               # MHA, empty chunks
+    run_pass_kv([500], 2, 2, 1, 128, "bf16", seed=5, causal=False)    # no mask
+
+
+def test_bf16_seed1_second_draw():
+    run_pass_kv([2048], 4, 16, 1, 128, "bf16", seed=1, ranks=[2], check_partials=False)
+
+
+# --------------------------------------------------------------------------- Pass-Q
+def run_pass_q(P, T, N, n_h, n_kv, d, dtype="bf16", seed=0, n_sample=None, check_partials=True):
+    from context_ring_attention_amd import binding as cp
+    std = 1.0
+    scale = scale_of(d)
+    q_ranges = [(0, P, P + T)]
+    kv_ranges = [(0, 0, P), (0, P, P + T)]
+    qsh = product_shards(q_ranges, N)
+    ksh = product_shards(kv_ranges, N)
+    for s in ksh.values():
+        s.k = device_tensor(seed, si.TID_K, s.tokens, (n_kv, d), std, dtype)
+        s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype)
+    qs = [device_tensor(seed, si.TID_Q, qsh[r].tokens, (n_h, d), std, dtype) for r in range(N)]
+    log(f"pass-q P={P} T={T} N={N} n_h={n_h} d={d}")
+    o_parts = [torch.full((qs[i // N].shape[0], n_h, d), float("nan"), device="cuda") for i in range(N * N)]
+    lse_parts = [torch.empty(qs[i // N].shape[0], n_h, device="cuda") for i in range(N * N)]
+    o_out = [torch.empty(x.shape[0], n_h, d, device="cuda") for x in qs]
+    lse_out = [torch.empty(x.shape[0], n_h, device="cuda") for x in qs]
+    cp.ring_pass_q(qs, [qsh[r].segs for r in range(N)], [ksh[s].k for s in range(N)],
+                   [ksh[s].v for s in range(N)], [ksh[s].segs for s in range(N)], True, scale,
+                   o_parts, lse_parts, o_out, lse_out)
+    torch.cuda.synchronize()
+    kf, vf, kseq, kpos = _oracle_keys(kv_ranges, N, range(N), seed, n_kv, d, std, dtype)
+    for qi in range(N):
+        q_seq, q_pos, q_glob = oracle.shard_tokens(q_ranges, N, qi)
+        qf = oracle_view(seed, si.TID_Q, q_glob, (n_h, d), std, dtype)
+        rows = sample_rows(qsh[qi].segs, n_sample, seed + qi) if n_sample else None
+        sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
+        o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, True, scale,
+                                        rows=rows)
+        assert_close(o_out[qi][sel], lse_out[qi][sel], o_ref, l_ref, dtype, f"q shard {qi} merged")
+        if check_partials and qi == N - 1:
+            for s in range(N):
+                kf1, vf1, ks1, kp1 = _oracle_keys(kv_ranges, N, [s], seed, n_kv, d, std, dtype)
+                o_p, l_p = oracle.attention(qf, kf1, vf1, n_h, n_kv, q_seq, q_pos, ks1, kp1, True,
+                                            scale, rows=rows)
+                assert_close(o_parts[qi * N + s][sel], lse_parts[qi * N + s][sel], o_p, l_p, dtype,
+                             f"slot [{qi}][{s}]")
+
+
+def test_pass_q_persistent_kv_small():
+    run_pass_q(P=3000, T=520, N=4, n_h=16, n_kv=1, d=128)
+
+
+# --------------------------------------------------------------------------- merge kernel
+@pytest.mark.parametrize("n_parts,rows,d,out", [(1, 37, 64, "f32"), (3, 1000, 128, "f32"),
+                                                (17, 513, 128, "bf16"), (64, 129, 64, "bf16")])
+def test_merge_lse_against_oracle(n_parts, rows, d, out):
+    from context_ring_attention_amd import binding as cp
+    log(f"merge n_parts={n_parts} rows={rows} d={d} out={out}")
+    o, lse = si.random_partials(7 + n_parts, n_parts, rows, d)
+    o_dev = [o[i].contiguous().cuda() for i in range(n_parts)]
+    l_dev = [lse[i].contiguous().cuda() for i in range(n_parts)]
+    o_out = torch.empty(rows, d, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
+    l_out = torch.empty(rows, device="cuda")
+    cp.merge_lse(o_dev, l_dev, o_out, l_out)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge([o[i].double().numpy() for i in range(n_parts)],
+                                [lse[i].double().numpy() for i in range(n_parts)])
+    tol = 2e-2 if out == "bf16" else 1e-5
+    o_g = o_out.float().cpu().numpy()
+    l_g = l_out.cpu().numpy()
+    assert np.array_equal(np.isneginf(l_g), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(o_g - o_ref)) <= tol
+    assert np.max(np.abs(l_g[fin] - l_ref[fin])) <= 1e-5
+    assert np.all(o_g[~fin] == 0)
+
+
+def test_merge_in_place_fp32():
+    from context_ring_attention_amd import binding as cp
+    o, lse = si.random_partials(3, 4, 300, 128)
+    o_dev = [o[i].contiguous().cuda() for i in range(4)]
+    l_dev = [lse[i].contiguous().cuda() for i in range(4)]
+    cp.merge_lse(o_dev, l_dev, o_dev[0], None)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.merge([o[i].double().numpy() for i in range(4)], [lse[i].double().numpy() for i in range(4)])
+    assert np.max(np.abs(o_dev[0].cpu().numpy() - o_ref)) <= 1e-5
+
+
+# --------------------------------------------------------------------------- decode
+def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=None):
+    from context_ring_attention_amd import binding as cp
+    lengths = np.asarray(lengths, np.int64)
+    B = len(lengths)
+    offs = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
+    total = int(lengths.sum())
+    log(f"decode B={B} n_splits={n_splits} total_keys={total} n_h={n_h} n_kv={n_kv} d={d}")
+    scale = scale_of(d)
+    toks = np.arange(total)
+    kc = device_tensor(seed, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
+    vc = device_tensor(seed, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
+    q = device_tensor(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, n_splits) // 4, device="cuda")
+    ws_o = ws[: B * n_splits * n_h * d]
+    ws_l = ws[B * n_splits * n_h * d:]
+    o_out = torch.empty(B, n_h, d, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
+    l_out = torch.empty(B, n_h, device="cuda")
+    cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lengths).cuda(),
+                      n_splits, scale, ws_o, ws_l, o_out, l_out)
+    torch.cuda.synchronize()
+    qf = oracle_view(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+    ws_o = ws_o.view(B, n_splits, n_h, d)
+    ws_l = ws_l.view(B, n_splits, n_h)
+    for b in range(B):
+        lo, L = int(offs[b]), int(lengths[b])
+        kf = oracle_view(seed, si.TID_K, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
+        vf = oracle_view(seed, si.TID_V, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
+        qs_ = np.zeros(1, np.int32)
+        qp_ = np.array([L], np.int64)
+        o_ref, l_ref = oracle.attention(qf[b:b + 1], kf, vf, n_h, n_kv, qs_, qp_, np.zeros(L, np.int32),
+                                        np.arange(L), False, scale)
+        dt = "bf16"
+        assert_close(o_out[b:b + 1], l_out[b:b + 1], o_ref, l_ref, dt, f"request {b} (L={L})")
+        splits = oracle.split_bounds(L, n_splits)
+        for c in (check_splits or []):
+            a, e = splits[c]
+            o_p, l_p = oracle.attention(qf[b:b + 1], kf[a:e], vf[a:e], n_h, n_kv, qs_, qp_,
+                                        np.zeros(e - a, np.int32), np.arange(a, e), False, scale)
+            assert_close(ws_o[b, c:c + 1], ws_l[b, c:c + 1], o_p, l_p, dt, f"request {b} split {c}")
+
+
+def test_decode_small_ragged():
+    run_decode([3000, 1, 100, 4097, 257], 16, 1, 128, 256, check_splits=[0, 1, 99, 255])
+
+
+def test_decode_gqa_d64_bf16_out():
+    run_decode([999, 64, 2500], 8, 2, 64, 16, seed=1, out="bf16", check_splits=[0, 15])
+
+
+def test_decode_more_than_16_heads_per_group():
+    run_decode([700, 33], 40, 2, 128, 8, seed=2, check_splits=[3])
