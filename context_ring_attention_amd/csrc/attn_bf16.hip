@@ -41,16 +41,32 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 template <int D>
 struct Bf16Cfg {
   static constexpr int kRows = kTileRowsBf16;   // query rows per workgroup
-  static constexpr int kThreads = 256;
+  static constexpr int kWaves = 8;              // 32 query rows per wave
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kBN = 64;                // keys per LDS tile
-  static constexpr int kStride = D * 2 + 16;    // padded LDS row (bytes)
-  static constexpr int kTileBytes = kBN * kStride;
+  // Padded LDS rows. K rows are read 16 bytes at a time by 16 lanes on 16 different rows: a
+  // stride of 4 (mod 64) dwords puts those rows on disjoint bank quads. V rows are read by the
+  // transposing loads, 4 lanes x 8 bytes on each of 4 rows per half-wave: a stride of 16
+  // (mod 64) dwords puts those four 64-byte runs on disjoint banks.
+  static constexpr int kStrideK = D * 2 + 16;
+  static constexpr int kStrideV = D * 2 + 64;
+  static constexpr int kStageBytes = kBN * (kStrideK + kStrideV);
   static constexpr int kChunks = D / 8;         // 16-byte chunks per key row
   static constexpr int kRowsPerPass = kThreads / kChunks;
   static constexpr int kPasses = kBN / kRowsPerPass;
   static constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 32;       // 32-row blocks of O^T
+  static_assert(kRows == kWaves * 32, "one 32-row query block per wave");
 };
+
+// The running max is only moved when a tile raises it by more than this many base-2 units, so
+// probabilities stay <= 2^8 (exact in fp32 and with bf16's full exponent range) and the O^T
+// accumulators are rescaled a handful of times per row instead of once per tile. Any stale max
+// gives the same result in exact arithmetic: LSE and O are computed against the max in use.
+constexpr float kRescaleThreshold = 8.0f;
+
+// s_waitcnt immediate for "vmcnt(0)" on gfx9-family targets (expcnt and lgkmcnt left at max).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ inline bf16x8 lds_read_b128(const unsigned char* base, int byte_off) {
   return *reinterpret_cast<const bf16x8*>(base + byte_off);
@@ -62,14 +78,14 @@ __device__ inline i16x4 lds_read_tr(const unsigned char* base, int byte_off) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnParams p) {
+__global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;   // query column of this lane in a 32x32 block
+  const int col = lane & 31;   // query column of this lane in the 32x32 blocks
   const int half = lane >> 5;  // which 8-wide k slice (and which 4-row group of the output)
   const int g = blockIdx.y;    // KV head
 
@@ -87,23 +103,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnParams p) {
   const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
 
-  // ---- this lane's two query rows and their Q^T operands -------------------------------
-  int qpos[2];
-  bool live[2];
-  int64_t qrow[2];
-  bf16x8 qreg[2][C::kKSteps];
+  // ---- this lane's query row and its Q^T operand ------------------------------------------
+  const int r = tile_row0 + wave * 32 + col;
+  const bool live = r < rows;
+  const int rc = live ? r : rows - 1;
+  const int qtok = rc / p.group;
+  const int qpos = qs.pos + qtok;
+  const int64_t qrow = (int64_t)(qs.loc + qtok) * p.n_h + g * p.group + rc % p.group;
+  bf16x8 qreg[C::kKSteps];
+  {
+    const __bf16* qp = Q + qrow * D + half * (D / 2);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = tile_row0 + wave * 64 + b * 32 + col;
-    live[b] = r < rows;
-    const int rc = live[b] ? r : rows - 1;
-    const int tok = rc / p.group;
-    qpos[b] = qs.pos + tok;
-    qrow[b] = (int64_t)(qs.loc + tok) * p.n_h + g * p.group + rc % p.group;
-    const __bf16* qp = Q + qrow[b] * D + half * (D / 2);
-#pragma unroll
-    for (int s = 0; s < C::kKSteps; ++s) qreg[b][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+    for (int s = 0; s < C::kKSteps; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
   }
+  // Retire the Q loads here: otherwise the wait analysis keeps them pending at the tile loop's
+  // header and makes the first QK^T of every tile also wait for the next tile's prefetch.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- KV tile iteration: runs of the same sequence, prefix visible to the last query ----
   auto run_visible = [&](int j) -> int {
@@ -115,48 +130,55 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnParams p) {
   while (j < p.n_kv_segs && run_visible(j) == 0) ++j;
   int kt = 0;
 
+  // K/V tile staging: each thread moves 16-byte chunks; a wave covers whole 256-byte key rows.
+  static_assert(C::kPasses == 1 || C::kPasses == 2, "one or two staging passes per tile");
   const int ld_chunk = tid % C::kChunks;
   const int ld_row0 = tid / C::kChunks;
-  uint4 kbuf[C::kPasses], vbuf[C::kPasses];
-  auto global_load = [&](int jj, int kk) {
-    const Seg ks = p.ks[jj];
-#pragma unroll
-    for (int ps = 0; ps < C::kPasses; ++ps) {
-      int key = kk + ld_row0 + ps * C::kRowsPerPass;
-      key = key < ks.len ? key : ks.len - 1;  // rows past the run are masked; stay in bounds
-      const int64_t off = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + ld_chunk * 8;
-      kbuf[ps] = *reinterpret_cast<const uint4*>(K + off);
-      vbuf[ps] = *reinterpret_cast<const uint4*>(V + off);
-    }
-  };
-  auto lds_store = [&](int stage) {
-    unsigned char* kt_s = smem + (stage * 2) * C::kTileBytes;
-    unsigned char* vt_s = kt_s + C::kTileBytes;
-#pragma unroll
-    for (int ps = 0; ps < C::kPasses; ++ps) {
-      const int r = ld_row0 + ps * C::kRowsPerPass;
-      *reinterpret_cast<uint4*>(kt_s + r * C::kStride + ld_chunk * 16) = kbuf[ps];
-      *reinterpret_cast<uint4*>(vt_s + r * C::kStride + ld_chunk * 16) = vbuf[ps];
-    }
-  };
+  const int64_t kv_row_stride = (int64_t)p.n_kv * D;
+  const __bf16* Kg = K + (int64_t)g * D + ld_chunk * 8;
+  const __bf16* Vg = V + (int64_t)g * D + ld_chunk * 8;
+  uint4 kb0, kb1, vb0, vb1;  // next tile, in flight during the current tile's math
+#define CP_TILE_LOAD(JJ, KK)                                                      \
+  {                                                                               \
+    const Seg ks_ = p.ks[JJ];                                                     \
+    const int key0 = min((KK) + ld_row0, ks_.len - 1);                            \
+    const int64_t o0 = (int64_t)(ks_.loc + key0) * kv_row_stride;                 \
+    kb0 = *reinterpret_cast<const uint4*>(Kg + o0);                               \
+    vb0 = *reinterpret_cast<const uint4*>(Vg + o0);                               \
+    if constexpr (C::kPasses == 2) {                                              \
+      const int key1 = min((KK) + ld_row0 + C::kRowsPerPass, ks_.len - 1);        \
+      const int64_t o1 = (int64_t)(ks_.loc + key1) * kv_row_stride;               \
+      kb1 = *reinterpret_cast<const uint4*>(Kg + o1);                             \
+      vb1 = *reinterpret_cast<const uint4*>(Vg + o1);                             \
+    }                                                                             \
+  }
+#define CP_TILE_STORE(STAGE)                                                      \
+  {                                                                               \
+    unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                        \
+    unsigned char* vt_s = kt_s + C::kBN * C::kStrideK;                            \
+    *reinterpret_cast<uint4*>(kt_s + ld_row0 * C::kStrideK + ld_chunk * 16) = kb0; \
+    *reinterpret_cast<uint4*>(vt_s + ld_row0 * C::kStrideV + ld_chunk * 16) = vb0; \
+    if constexpr (C::kPasses == 2) {                                              \
+      *reinterpret_cast<uint4*>(kt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideK + ld_chunk * 16) = kb1; \
+      *reinterpret_cast<uint4*>(vt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideV + ld_chunk * 16) = vb1; \
+    }                                                                             \
+  }
 
-  float m[2] = {-INFINITY, -INFINITY};  // running max, base-2 scaled units
-  float l[2] = {0.f, 0.f};              // running sum (this half-wave's keys)
-  f32x16 oacc[2][C::kDBlocks];
+  float m = -INFINITY;  // max in use, base-2 scaled units (same in both half-waves)
+  float l = 0.f;        // running sum over this half-wave's keys
+  f32x16 oacc[C::kDBlocks];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[b][db][v] = 0.f;
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
 
   if (j < p.n_kv_segs) {
-    global_load(j, kt);
-    lds_store(0);
+    CP_TILE_LOAD(j, kt);
+    CP_TILE_STORE(0);
   }
   __syncthreads();
 
-  // V^T operand addressing for ds_read_b64_tr_b16 (see header): lane group of 16 -> 8 d-rows
+  // V^T operand addressing for ds_read_b64_tr_b16: each 16-lane group covers 16 d-rows
   const int grp = lane >> 4;          // 0..3
   const int dsub = grp & 1;           // which 16 of the 32 d-rows
   const int j16 = lane & 15;
@@ -173,99 +195,91 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnParams p) {
       nkt = 0;
     }
     const bool has_next = nj < p.n_kv_segs;
-    if (has_next) global_load(nj, nkt);
+    if (has_next) CP_TILE_LOAD(nj, nkt);
 
     const Seg ks = p.ks[j];
-    const unsigned char* Kt = smem + (stage * 2) * C::kTileBytes;
-    const unsigned char* Vt = Kt + C::kTileBytes;
+    const unsigned char* Kt = smem + stage * C::kStageBytes;
+    const unsigned char* Vt = Kt + C::kBN * C::kStrideK;
 
-    // ---- S^T = K Q^T for both query blocks and both 32-key halves of the tile ----
-    f32x16 s[2][2];
+    // ---- S^T = K Q^T: two 32-key halves of the tile against this wave's 32 queries ----
+    f32x16 s[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[b][kb][v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
     for (int st = 0; st < C::kKSteps; ++st) {
       const int coff = (half * (D / 2) + st * 8) * 2;
-      const bf16x8 a0 = lds_read_b128(Kt, col * C::kStride + coff);
-      const bf16x8 a1 = lds_read_b128(Kt, (32 + col) * C::kStride + coff);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[b][st], s[b][0], 0, 0, 0);
-        s[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[b][st], s[b][1], 0, 0, 0);
-      }
+      const bf16x8 a0 = lds_read_b128(Kt, col * C::kStrideK + coff);
+      const bf16x8 a1 = lds_read_b128(Kt, (32 + col) * C::kStrideK + coff);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[st], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[st], s[1], 0, 0, 0);
     }
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
     const int n_full = p.causal ? max(0, min(ks.len, qpos_lo - ks.pos + 1)) : ks.len;
     if (kt + C::kBN > n_full) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int ko = kt + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool vis = ko < ks.len && (!p.causal || ks.pos + ko <= qpos[b]);
-            if (!vis) s[b][kb][v] = -INFINITY;
-          }
-    }
-
-    // ---- online softmax (base 2) ----
-    bf16x8 pb[2][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[b], mx * p.scale_log2);
-      const float msafe = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[b] - msafe);
-      m[b] = mnew;
-      float rs = 0.f;
+      // key ko of the run is visible iff ko < len and (not causal or pos + ko <= qpos):
+      // ko < lim with lim = min(len, qpos - pos + 1) (or len without the causal mask)
+      const int lim = p.causal ? min(ks.len, qpos - ks.pos + 1) : ks.len;
+      const int base = kt + 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[b][kb][v], p.scale_log2, -msafe));
-          s[b][kb][v] = e;
-          rs += e;
+          const int ko = base + kb * 32 + 8 * (v >> 2) + (v & 3);
+          s[kb][v] = ko < lim ? s[kb][v] : -INFINITY;
         }
-      l[b] = l[b] * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[b][db][v] *= alpha;
-      // P^T operand of k-step t: keys 16t + 8(e/4) + 4*half + e%4 == accumulator entries 8(t%2)+e
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[b][t][e] = (__bf16)s[b][t >> 1][8 * (t & 1) + e];
     }
+
+    // ---- online softmax (base 2, lazily moved max) ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0; mnew = m -> 1
+      if (mnew != -INFINITY) {
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        m = mnew;
+      }
+    }
+    const float msafe = m == -INFINITY ? 0.f : m;
+    bf16x8 pb[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -msafe));
+        rs += e;
+        // P^T operand of k-step t: keys 16t + 8(e/4) + 4*half + e%4 == entries 8(t%2) + e
+        pb[2 * kb + (v >> 3)][v & 7] = (__bf16)e;
+      }
+    l += rs;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int db = 0; db < C::kDBlocks; ++db) {
-        const int off = (16 * t + tr_key) * C::kStride + (db * 32 + tr_dcol) * 2;
+        const int off = (16 * t + tr_key) * C::kStrideV + (db * 32 + tr_dcol) * 2;
         const i16x4 lo = lds_read_tr(Vt, off);
-        const i16x4 hi = lds_read_tr(Vt, off + 8 * C::kStride);
+        const i16x4 hi = lds_read_tr(Vt, off + 8 * C::kStrideV);
         const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[b][t], oacc[b][db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t], oacc[db], 0, 0, 0);
       }
     }
 
-    if (has_next) lds_store(stage ^ 1);
+    if (has_next) CP_TILE_STORE(stage ^ 1);
     __syncthreads();
     stage ^= 1;
     j = nj;
@@ -273,39 +287,45 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnParams p) {
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2, optional merge into the running result
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const float lt = l[b] + __shfl_xor(l[b], 32);
-    if (!live[b]) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_new = lt > 0.f ? (m[b] + __log2f(lt)) * kLn2 : -INFINITY;
-    float wp = 0.f, wn = 1.f, lse_out = lse_new;
-    if (p.accumulate) running_merge_weights(p.lse[qrow[b]], lse_new, wp, wn, lse_out);
-    const float sc = wn * inv;
-    float* orow = p.o + qrow[b] * D;
+  const float lt = l + __shfl_xor(l, 32);
+  if (!live) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_new = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  float wp = 0.f, wn = 1.f, lse_out = lse_new;
+  float* orow = p.o + qrow * D;
+  float4 prev[C::kDBlocks * 4];
+  if (p.accumulate) {
+    running_merge_weights(p.lse[qrow], lse_new, wp, wn, lse_out);
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int d0 = db * 32 + 8 * vq + 4 * half;
-        float4 o4 = make_float4(oacc[b][db][4 * vq] * sc, oacc[b][db][4 * vq + 1] * sc,
-                                oacc[b][db][4 * vq + 2] * sc, oacc[b][db][4 * vq + 3] * sc);
-        if (p.accumulate) {
-          const float4 prev = *reinterpret_cast<const float4*>(orow + d0);
-          o4.x = fmaf(wp, prev.x, o4.x);
-          o4.y = fmaf(wp, prev.y, o4.y);
-          o4.z = fmaf(wp, prev.z, o4.z);
-          o4.w = fmaf(wp, prev.w, o4.w);
-        }
-        *reinterpret_cast<float4*>(orow + d0) = o4;
-      }
-    if (half == 0) p.lse[qrow[b]] = lse_out;
+      for (int vq = 0; vq < 4; ++vq)
+        prev[db * 4 + vq] = *reinterpret_cast<const float4*>(orow + db * 32 + 8 * vq + 4 * half);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::kDBlocks * 4; ++i) prev[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const float sc = wn * inv;
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const float4 pv = prev[db * 4 + vq];
+      float4 o4;
+      o4.x = fmaf(wp, pv.x, oacc[db][4 * vq] * sc);
+      o4.y = fmaf(wp, pv.y, oacc[db][4 * vq + 1] * sc);
+      o4.z = fmaf(wp, pv.z, oacc[db][4 * vq + 2] * sc);
+      o4.w = fmaf(wp, pv.w, oacc[db][4 * vq + 3] * sc);
+      *reinterpret_cast<float4*>(orow + db * 32 + 8 * vq + 4 * half) = o4;
+    }
+  if (half == 0) p.lse[qrow] = lse_out;
+#undef CP_TILE_LOAD
+#undef CP_TILE_STORE
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream) {
   const dim3 grid(p.total_tiles, p.n_kv);
-  const dim3 block(256);
+  const dim3 block(Bf16Cfg<128>::kThreads);
   if (d_h == 64)
     hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, stream, p);
   else

@@ -31,7 +31,11 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 template <int D>
 struct DecCfg {
   static constexpr int kBK = 32;                 // keys per block
-  static constexpr int kStride = D * 2 + 16;     // padded LDS row (bytes)
+  // Padded LDS rows: K rows are read 16 bytes per lane by 16 lanes on 16 rows (stride 4 mod 64
+  // dwords keeps them on disjoint bank quads); V rows by the transposing loads, 8 rows x 32
+  // bytes per half-wave (stride 8 mod 64 dwords keeps the eight runs disjoint).
+  static constexpr int kStrideK = D * 2 + 16;
+  static constexpr int kStrideV = D * 2 + 32;
   static constexpr int kKSteps = D / 32;         // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
   static constexpr int kChunks = D / 8;          // 16-byte chunks per key row
@@ -41,7 +45,8 @@ struct DecCfg {
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char vs[C::kBK * C::kStride];
+  __shared__ __attribute__((aligned(16))) unsigned char ks[C::kBK * C::kStrideK];
+  __shared__ __attribute__((aligned(16))) unsigned char vs[C::kBK * C::kStrideV];
 
   const int c = blockIdx.x;  // split
   const int b = blockIdx.y;  // request
@@ -74,32 +79,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
   }
 
-  // key-row loads of one 32-key block: K into operand registers, V into staging registers
-  bf16x8 kreg[2][C::kKSteps];
-  uint4 vreg[C::kVLoads];
-  auto load_block = [&](int kb0, bf16x8 (&kr)[2][C::kKSteps], uint4 (&vr)[C::kVLoads]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int key = kb0 + 16 * h + col;
-      key = key < n ? key : n - 1;
-      const __bf16* kp = Kc + ((base + lo + key) * p.n_kv + g) * D + grp * (D / 4);
-#pragma unroll
-      for (int st = 0; st < C::kKSteps; ++st) kr[h][st] = *reinterpret_cast<const bf16x8*>(kp + st * 8);
-    }
+  // Loads of one 32-key block: every instruction reads four whole key rows (16 lanes x 16 bytes
+  // per row), for K and for V; the rows are staged in LDS in their row-major layout.
+  uint4 kreg[C::kVLoads], vreg[C::kVLoads];
+  auto load_block = [&](int kb0, uint4 (&kr)[C::kVLoads], uint4 (&vr)[C::kVLoads]) {
 #pragma unroll
     for (int i = 0; i < C::kVLoads; ++i) {
       const int idx = i * 64 + lane;
       int key = kb0 + idx / C::kChunks;
       key = key < n ? key : n - 1;
-      const int ch = idx % C::kChunks;
-      vr[i] = *reinterpret_cast<const uint4*>(Vc + ((base + lo + key) * p.n_kv + g) * D + ch * 8);
+      const int64_t off = ((base + lo + key) * p.n_kv + g) * D + (idx % C::kChunks) * 8;
+      kr[i] = *reinterpret_cast<const uint4*>(Kc + off);
+      vr[i] = *reinterpret_cast<const uint4*>(Vc + off);
     }
   };
-  auto store_v = [&](const uint4 (&vr)[C::kVLoads]) {
+  auto store_block = [&](const uint4 (&kr)[C::kVLoads], const uint4 (&vr)[C::kVLoads]) {
 #pragma unroll
     for (int i = 0; i < C::kVLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<uint4*>(vs + (idx / C::kChunks) * C::kStride + (idx % C::kChunks) * 16) = vr[i];
+      const int row = idx / C::kChunks, c16 = (idx % C::kChunks) * 16;
+      *reinterpret_cast<uint4*>(ks + row * C::kStrideK + c16) = kr[i];
+      *reinterpret_cast<uint4*>(vs + row * C::kStrideV + c16) = vr[i];
     }
   };
 
@@ -115,23 +115,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
   if (n > 0) {
     load_block(0, kreg, vreg);
-    store_v(vreg);
+    store_block(kreg, vreg);
   }
   __syncthreads();
   for (int kb0 = 0; kb0 < n; kb0 += C::kBK) {
     const bool has_next = kb0 + C::kBK < n;
-    bf16x8 knext[2][C::kKSteps];
-    uint4 vnext[C::kVLoads];
-    if (has_next) load_block(kb0 + C::kBK, knext, vnext);
+    if (has_next) load_block(kb0 + C::kBK, kreg, vreg);
 
-    // S^T (keys x heads) for the two 16-key halves
+    // S^T (keys x heads) for the two 16-key halves; K operand: key row col, d slice of grp
     f32x4 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < C::kKSteps; ++st)
-        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[h][st], qreg[st], s[h], 0, 0, 0);
+      for (int st = 0; st < C::kKSteps; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            ks + (16 * h + col) * C::kStrideK + (grp * (D / 4) + st * 8) * 2);
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[st], s[h], 0, 0, 0);
+      }
     }
     // keys past the split are masked
     if (kb0 + C::kBK > n) {
@@ -168,23 +169,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     // O^T += V^T P^T: operand k = 4h + v <-> key 16h + 4*grp + v
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db) {
-      const int off = tr_row * C::kStride + (db * 16 + tr_col) * 2;
+      const int off = tr_row * C::kStrideV + (db * 16 + tr_col) * 2;
       const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vs + off));
       const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vs + off + 16 * C::kStride));
+          (__attribute__((address_space(3))) i16x4*)(vs + off + 16 * C::kStrideV));
       const i16x8 both = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pt,
                                                           oacc[db], 0, 0, 0);
     }
     __syncthreads();
-    if (has_next) {
-      store_v(vnext);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int st = 0; st < C::kKSteps; ++st) kreg[h][st] = knext[h][st];
-    }
+    if (has_next) store_block(kreg, vreg);
     __syncthreads();
   }
 
@@ -202,25 +197,36 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   if (grp == 0) p.ws_lse[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-// Merge of the S split partials of each (request, head).
+// Merge of the S split partials of each (request, head): one workgroup per (request, head);
+// 256 / (D/4) groups of D/4 lanes take every kGroups-th split, then combine through LDS.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
-  constexpr int kLanesPerRow = D / 4;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const int r = blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;  // b * n_h + head
-  const int c4 = threadIdx.x % kLanesPerRow;
-  if (r >= p.batch * p.n_h) return;
+  constexpr int kLanes = D / 4;
+  constexpr int kGroups = 256 / kLanes;
+  __shared__ float red_m[kGroups];
+  __shared__ float red_w[kGroups];
+  __shared__ float4 red_o[kGroups][kLanes];
+  const int r = blockIdx.x;  // b * n_h + head
   const int b = r / p.n_h;
   const int head = r % p.n_h;
+  const int grp = threadIdx.x / kLanes;
+  const int c4 = threadIdx.x % kLanes;
   const int64_t stride = (int64_t)p.n_h;
   const float* lse = p.ws_lse + (int64_t)b * p.n_splits * p.n_h + head;
   const float* o = p.ws_o + ((int64_t)b * p.n_splits * p.n_h + head) * D + c4 * 4;
+
   float M = -INFINITY;
-  for (int c = 0; c < p.n_splits; ++c) M = fmaxf(M, lse[c * stride]);
+  for (int c = grp; c < p.n_splits; c += kGroups) M = fmaxf(M, lse[c * stride]);
+  if (c4 == 0) red_m[grp] = M;
+  __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int i = 1; i < kGroups; ++i) M = fmaxf(M, red_m[i]);
+
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int c = 0; c < p.n_splits; ++c) {
+    for (int c = grp; c < p.n_splits; c += kGroups) {
       const float li = lse[c * stride];
       if (li == -INFINITY) continue;
       const float w = expf(li - M);
@@ -231,6 +237,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
       acc.z = fmaf(w, v.z, acc.z);
       acc.w = fmaf(w, v.w, acc.w);
     }
+  }
+  red_o[grp][c4] = acc;
+  if (c4 == 0) red_w[grp] = wsum;
+  __syncthreads();
+  if (grp != 0) return;
+  wsum = 0.f;
+  acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) {  // fixed order: deterministic
+    wsum += red_w[i];
+    const float4 v = red_o[i][c4];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t orow = (int64_t)r * D + c4 * 4;
@@ -248,8 +269,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
   const int hblocks = (p.group + 15) / 16;
   const dim3 grid(p.n_splits, p.batch, p.n_kv * hblocks);
-  const int rows_per_block = 256 / (d_h / 4);
-  const dim3 mgrid((p.batch * p.n_h + rows_per_block - 1) / rows_per_block);
+  const dim3 mgrid(p.batch * p.n_h);
   if (d_h == 64) {
     hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64), 0, stream, p);
     if (p.out_bf16)
