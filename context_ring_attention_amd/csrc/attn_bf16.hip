@@ -37,6 +37,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+// Native vector for 16-byte staging (arrays of HIP's uint4 struct are not promoted to registers).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Bf16Cfg {
@@ -137,30 +139,30 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
   const int64_t kv_row_stride = (int64_t)p.n_kv * D;
   const __bf16* Kg = K + (int64_t)g * D + ld_chunk * 8;
   const __bf16* Vg = V + (int64_t)g * D + ld_chunk * 8;
-  uint4 kb0, kb1, vb0, vb1;  // next tile, in flight during the current tile's math
+  u32x4 kb0, kb1, vb0, vb1;  // next tile, in flight during the current tile's math
 #define CP_TILE_LOAD(JJ, KK)                                                      \
   {                                                                               \
     const Seg ks_ = p.ks[JJ];                                                     \
     const int key0 = min((KK) + ld_row0, ks_.len - 1);                            \
     const int64_t o0 = (int64_t)(ks_.loc + key0) * kv_row_stride;                 \
-    kb0 = *reinterpret_cast<const uint4*>(Kg + o0);                               \
-    vb0 = *reinterpret_cast<const uint4*>(Vg + o0);                               \
+    kb0 = *reinterpret_cast<const u32x4*>(Kg + o0);                               \
+    vb0 = *reinterpret_cast<const u32x4*>(Vg + o0);                               \
     if constexpr (C::kPasses == 2) {                                              \
       const int key1 = min((KK) + ld_row0 + C::kRowsPerPass, ks_.len - 1);        \
       const int64_t o1 = (int64_t)(ks_.loc + key1) * kv_row_stride;               \
-      kb1 = *reinterpret_cast<const uint4*>(Kg + o1);                             \
-      vb1 = *reinterpret_cast<const uint4*>(Vg + o1);                             \
+      kb1 = *reinterpret_cast<const u32x4*>(Kg + o1);                             \
+      vb1 = *reinterpret_cast<const u32x4*>(Vg + o1);                             \
     }                                                                             \
   }
 #define CP_TILE_STORE(STAGE)                                                      \
   {                                                                               \
     unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                        \
     unsigned char* vt_s = kt_s + C::kBN * C::kStrideK;                            \
-    *reinterpret_cast<uint4*>(kt_s + ld_row0 * C::kStrideK + ld_chunk * 16) = kb0; \
-    *reinterpret_cast<uint4*>(vt_s + ld_row0 * C::kStrideV + ld_chunk * 16) = vb0; \
+    *reinterpret_cast<u32x4*>(kt_s + ld_row0 * C::kStrideK + ld_chunk * 16) = kb0; \
+    *reinterpret_cast<u32x4*>(vt_s + ld_row0 * C::kStrideV + ld_chunk * 16) = vb0; \
     if constexpr (C::kPasses == 2) {                                              \
-      *reinterpret_cast<uint4*>(kt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideK + ld_chunk * 16) = kb1; \
-      *reinterpret_cast<uint4*>(vt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideV + ld_chunk * 16) = vb1; \
+      *reinterpret_cast<u32x4*>(kt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideK + ld_chunk * 16) = kb1; \
+      *reinterpret_cast<u32x4*>(vt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideV + ld_chunk * 16) = vb1; \
     }                                                                             \
   }
 

@@ -27,6 +27,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+// Native vector for 16-byte staging (arrays of HIP's uint4 struct are not promoted to registers).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct DecCfg {
@@ -81,27 +83,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
   // Loads of one 32-key block: every instruction reads four whole key rows (16 lanes x 16 bytes
   // per row), for K and for V; the rows are staged in LDS in their row-major layout.
-  uint4 kreg[C::kVLoads], vreg[C::kVLoads];
-  auto load_block = [&](int kb0, uint4 (&kr)[C::kVLoads], uint4 (&vr)[C::kVLoads]) {
-#pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int idx = i * 64 + lane;
-      int key = kb0 + idx / C::kChunks;
-      key = key < n ? key : n - 1;
-      const int64_t off = ((base + lo + key) * p.n_kv + g) * D + (idx % C::kChunks) * 8;
-      kr[i] = *reinterpret_cast<const uint4*>(Kc + off);
-      vr[i] = *reinterpret_cast<const uint4*>(Vc + off);
-    }
-  };
-  auto store_block = [&](const uint4 (&kr)[C::kVLoads], const uint4 (&vr)[C::kVLoads]) {
-#pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int idx = i * 64 + lane;
-      const int row = idx / C::kChunks, c16 = (idx % C::kChunks) * 16;
-      *reinterpret_cast<uint4*>(ks + row * C::kStrideK + c16) = kr[i];
-      *reinterpret_cast<uint4*>(vs + row * C::kStrideV + c16) = vr[i];
-    }
-  };
+  u32x4 kr[C::kVLoads], vr[C::kVLoads];
+  const __bf16* Kr = Kc + (base + lo) * p.n_kv * D + (int64_t)g * D;
+  const __bf16* Vr = Vc + (base + lo) * p.n_kv * D + (int64_t)g * D;
+  const int64_t row_stride = (int64_t)p.n_kv * D;
+#define CP_DEC_LOAD(KB0)                                                             \
+  _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
+    const int idx = i * 64 + lane;                                                   \
+    const int key = min((KB0) + idx / C::kChunks, n - 1);                            \
+    const int64_t off = key * row_stride + (idx % C::kChunks) * 8;                   \
+    kr[i] = *reinterpret_cast<const u32x4*>(Kr + off);                               \
+    vr[i] = *reinterpret_cast<const u32x4*>(Vr + off);                               \
+  }
+#define CP_DEC_STORE()                                                               \
+  _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
+    const int idx = i * 64 + lane;                                                   \
+    const int row = idx / C::kChunks, c16 = (idx % C::kChunks) * 16;                 \
+    *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];                 \
+    *reinterpret_cast<u32x4*>(vs + row * C::kStrideV + c16) = vr[i];                 \
+  }
 
   float m = -INFINITY, l = 0.f;
   f32x4 oacc[C::kDBlocks];
@@ -113,14 +113,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int tr_row = 4 * grp + (j16 >> 2);
   const int tr_col = 4 * (j16 & 3);
 
+  // retire the q loads before the block loop (keeps the loop's prefetch out of its waits)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   if (n > 0) {
-    load_block(0, kreg, vreg);
-    store_block(kreg, vreg);
+    CP_DEC_LOAD(0);
+    CP_DEC_STORE();
   }
   __syncthreads();
   for (int kb0 = 0; kb0 < n; kb0 += C::kBK) {
     const bool has_next = kb0 + C::kBK < n;
-    if (has_next) load_block(kb0 + C::kBK, kreg, vreg);
+    if (has_next) CP_DEC_LOAD(kb0 + C::kBK);
 
     // S^T (keys x heads) for the two 16-key halves; K operand: key row col, d slice of grp
     f32x4 s[2];
@@ -179,9 +181,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
                                                           oacc[db], 0, 0, 0);
     }
     __syncthreads();
-    if (has_next) store_block(kreg, vreg);
+    if (has_next) CP_DEC_STORE();
     __syncthreads();
   }
+#undef CP_DEC_LOAD
+#undef CP_DEC_STORE
 
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
