@@ -1,0 +1,92 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+Each output row checked is compared with the oracle's exact result over the row's full visible
+key set; rows are sampled (first, middle and last token of every segment plus random tokens,
+all query heads of each), since the oracle cannot redo 10-200 TFLOP of attention.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from ring_cases import device_tensor, log, oracle_view, product_shards, sample_rows, scale_of
+from test_parity_gpu import assert_close, run_pass_kv, run_pass_q
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_full_prefill_128k_cp4_all_ranks_running():
+    cfg = si.CONFIGS["prefill_128k_cp4"]
+    run_pass_kv(cfg["seqs"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], "bf16", seed=0,
+                mode="running", n_sample=12)
+
+
+def test_full_prefill_128k_cp4_partials_seed1():
+    cfg = si.CONFIGS["prefill_128k_cp4"]
+    run_pass_kv(cfg["seqs"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], "bf16", seed=1,
+                mode="partials", ranks=[1], n_sample=6, check_partials=True)
+
+
+def test_full_persistent_kv_pass_q():
+    cfg = si.CONFIGS["persistent_kv_8k_on_120k"]
+    run_pass_q(cfg["cached"], cfg["new"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"],
+               n_sample=10, check_partials=True)
+
+
+def test_full_prefill_1m_varlen_cp8():
+    cfg = si.CONFIGS["prefill_1m_varlen_cp8"]
+    run_pass_kv(cfg["seqs"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], "bf16", seed=0,
+                mode="running", ranks=[0, 7], n_sample=6)
+
+
+def test_full_decode_b32_256_splits():
+    from context_ring_attention_amd import binding as cp
+    cfg = si.CONFIGS["decode_b32_32k_128k"]
+    B, n_h, n_kv, d, S = cfg["batch"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["n_splits"]
+    lens = si.decode_lengths(0, B, cfg["len_lo"], cfg["len_hi"])
+    assert lens.min() >= cfg["len_lo"] and lens.max() <= cfg["len_hi"]
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    total = int(lens.sum())
+    log(f"decode full: B={B} total keys {total}")
+    toks = np.arange(total)
+    kc = device_tensor(0, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
+    vc = device_tensor(0, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
+    q = device_tensor(0, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, S) // 4, device="cuda")
+    ws_o, ws_l = ws[: B * S * n_h * d], ws[B * S * n_h * d:]
+    o = torch.empty(B, n_h, d, device="cuda")
+    l = torch.empty(B, n_h, device="cuda")
+    scale = scale_of(d)
+    cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lens).cuda(), S,
+                      scale, ws_o, ws_l, o, l)
+    torch.cuda.synchronize()
+    qf = oracle_view(0, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+    ws_o = ws_o.view(B, S, n_h, d)
+    ws_l = ws_l.view(B, S, n_h)
+    rng = np.random.default_rng(0)
+    for b in range(B):
+        lo, L = int(offs[b]), int(lens[b])
+        kf = oracle_view(0, si.TID_K, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
+        vf = oracle_view(0, si.TID_V, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
+        zs = np.zeros(1, np.int32)
+        qp = np.array([L], np.int64)
+        kseq = np.zeros(L, np.int32)
+        kpos = np.arange(L)
+        o_ref, l_ref = oracle.attention(qf[b:b + 1], kf, vf, n_h, n_kv, zs, qp, kseq, kpos, False, scale)
+        assert_close(o[b:b + 1], l[b:b + 1], o_ref, l_ref, "bf16", f"request {b} (L={L})")
+        if b % 8 == 0:
+            bounds = oracle.split_bounds(L, S)
+            for c in (0, int(rng.integers(1, S - 1)), S - 1):
+                a, e = bounds[c]
+                o_p, l_p = oracle.attention(qf[b:b + 1], kf[a:e], vf[a:e], n_h, n_kv, zs, qp,
+                                            kseq[a:e], kpos[a:e], False, scale)
+                assert_close(ws_o[b, c:c + 1], ws_l[b, c:c + 1], o_p, l_p, "bf16", f"request {b} split {c}")

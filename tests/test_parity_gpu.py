@@ -63,6 +63,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
     for s in sh.values():
         s.k = device_tensor(seed, si.TID_K, s.tokens, (n_kv, d), std, dtype)
         s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype)
+    all_keys = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype)
     for r in ranks:
         log(f"pass-kv seqs={seqs} N={N} rank={r} n_h={n_h} n_kv={n_kv} d={d} {dtype} mode={mode} causal={causal}")
         q = device_tensor(seed, si.TID_Q, sh[r].tokens, (n_h, d), std, dtype)
@@ -73,7 +74,9 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         if mode == "partials":
             kw["o_parts"] = [torch.full((tq, n_h, d), float("nan"), device="cuda") for _ in range(N)]
             kw["lse_parts"] = [torch.empty(tq, n_h, device="cuda") for _ in range(N)]
-        else:
+        elif mode == "running":          # in place, as bench.py runs it
+            kw["o_acc"], kw["lse_acc"] = o_out, lse_out
+        else:                            # separate running buffers, final copy through the merge
             kw["o_acc"] = torch.empty(tq, n_h, d, device="cuda")
             kw["lse_acc"] = torch.empty(tq, n_h, device="cuda")
         cp.ring_pass_kv(q, sh[r].segs, r, [sh[s].k for s in range(N)], [sh[s].v for s in range(N)],
@@ -83,7 +86,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         q_seq, q_pos, q_glob = oracle.shard_tokens(ranges, N, r)
         qf = oracle_view(seed, si.TID_Q, q_glob, (n_h, d), std, dtype)
         rows = sample_rows(sh[r].segs, n_sample, seed + r) if n_sample else None
-        kf, vf, kseq, kpos = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype)
+        kf, vf, kseq, kpos = all_keys
         o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
                                         scale, rows=rows)
         sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
@@ -106,6 +109,7 @@ def test_tiny_ring_fp32_all_ranks():
 
 def test_tiny_ring_fp32_running_merge():
     run_pass_kv([256], 4, 4, 1, 64, "f32", mode="running")
+    run_pass_kv([256], 4, 4, 1, 64, "f32", mode="running_out", ranks=[3])
 
 
 def test_fp32_ragged_multi_sequence_d128_gqa():
