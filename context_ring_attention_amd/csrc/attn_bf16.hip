@@ -9,23 +9,24 @@
 //
 // How (MI355X-first design; the pages name FlashAttention-3 on H100 as prior art only):
 //  - GQA packing: the G = N_H / N_KV query heads of a KV group are flattened with the tokens into
-//    one row space (row = token * G + head). A workgroup of 4 waves owns 256 rows; every K/V tile
+//    one row space (row = token * G + head). A workgroup of 8 waves owns 256 rows; every K/V tile
 //    it stages in LDS serves all of them (for G = 16 that is 16 tokens x 16 heads).
 //  - Orientation S^T = K Q^T: v_mfma_f32_32x32x16_bf16 with K as the A operand (rows = keys)
 //    and Q^T as the B operand (columns = queries). In the 32x32 accumulator a lane holds 16 keys
 //    of one query, so a query's row max needs only one exchange between the two half-waves.
-//  - Each wave keeps two 32-query blocks: their Q^T operands stay in registers for the whole
-//    kernel and every K or V operand read from LDS feeds two MFMAs.
+//    Each wave owns one 32-query block whose Q^T operand stays in registers.
 //  - P.V as O^T = V^T P^T: the probabilities, rounded to bf16, are already laid out as the
 //    B operand; V^T comes straight from the row-major V tile with ds_read_b64_tr_b16, whose
 //    16-lane transpose turns four key rows into per-lane key vectors.
-//  - Online softmax in base 2 with scale*log2(e) folded into one FMA, fp32 accumulators, LSE
-//    returned in natural log.
+//  - Software pipeline: while the VALUs run the softmax of tile n, the MFMA pipe already works
+//    on QK^T of tile n+1; K/V tiles live in three LDS stages (tile n being consumed, tile n+1
+//    ready for QK^T, tile n+2 arriving from registers loaded during the previous tile).
+//  - Online softmax in base 2 with scale*log2(e) folded into one FMA; the running max only moves
+//    when a tile raises it by more than 2^8, so the O^T accumulators are rarely rescaled; fp32
+//    accumulators, LSE returned in natural log.
 //  - Masks are computed from segment positions, never stored. Tiles entirely visible to every
 //    row of the workgroup skip the mask; runs of other sequences and keys past the causal
 //    frontier are never loaded.
-//  - K/V tiles are double-buffered in LDS; the next tile's global loads are issued before the
-//    current tile's math.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
@@ -40,10 +41,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 // Native vector for 16-byte staging (arrays of HIP's uint4 struct are not promoted to registers).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <int D, int WAVES>
 struct Bf16Cfg {
-  static constexpr int kRows = kTileRowsBf16;   // query rows per workgroup
-  static constexpr int kWaves = 8;              // 32 query rows per wave
+  static constexpr int kWaves = WAVES;          // 32 query rows per wave
+  static constexpr int kRows = 32 * WAVES;      // query rows per workgroup
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBN = 64;                // keys per LDS tile
   // Padded LDS rows. K rows are read 16 bytes at a time by 16 lanes on 16 different rows: a
@@ -53,16 +54,16 @@ struct Bf16Cfg {
   static constexpr int kStrideK = D * 2 + 16;
   static constexpr int kStrideV = D * 2 + 64;
   static constexpr int kStageBytes = kBN * (kStrideK + kStrideV);
+  static constexpr int kStages = 3;
   static constexpr int kChunks = D / 8;         // 16-byte chunks per key row
   static constexpr int kRowsPerPass = kThreads / kChunks;
   static constexpr int kPasses = kBN / kRowsPerPass;
   static constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 32;       // 32-row blocks of O^T
-  static_assert(kRows == kWaves * 32, "one 32-row query block per wave");
 };
 
 // The running max is only moved when a tile raises it by more than this many base-2 units, so
-// probabilities stay <= 2^8 (exact in fp32 and with bf16's full exponent range) and the O^T
+// probabilities stay <= 2^8 (exact in fp32 and within bf16's exponent range) and the O^T
 // accumulators are rescaled a handful of times per row instead of once per tile. Any stale max
 // gives the same result in exact arithmetic: LSE and O are computed against the max in use.
 constexpr float kRescaleThreshold = 8.0f;
@@ -79,10 +80,27 @@ __device__ inline i16x4 lds_read_tr(const unsigned char* base, int byte_off) {
       (__attribute__((address_space(3))) i16x4*)(base + byte_off));
 }
 
-template <int D>
-__global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
-  using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::kStageBytes];
+// Position of a K/V tile: run j of the KV shard (j == n_kv_segs means "no tile"), key offset kt
+// inside the run, and the run's fields, carried along so that scalar loads of the run table
+// (whose waits would also drain every outstanding LDS read) only happen at run boundaries.
+struct TilePos {
+  int j;
+  int kt;
+  int vis;  // keys of the run visible to the workgroup's last query
+  int loc, pos, len;
+};
+
+// Max of x over the two half-waves (lane l and lane l ^ 32) without going through LDS.
+__device__ inline float halfwave_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams p) {
+  using C = Bf16Cfg<D, WAVES>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStages * C::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,52 +137,71 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
     for (int s = 0; s < C::kKSteps; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
   }
   // Retire the Q loads here: otherwise the wait analysis keeps them pending at the tile loop's
-  // header and makes the first QK^T of every tile also wait for the next tile's prefetch.
+  // header and makes the QK^T of every tile also wait for the next tile's prefetch.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // ---- KV tile iteration: runs of the same sequence, prefix visible to the last query ----
-  auto run_visible = [&](int j) -> int {
-    const Seg ks = p.ks[j];
-    if (ks.seq != qs.seq) return 0;
-    return visible_prefix(ks, qpos_hi, p.causal);
+  // ---- KV tiles: runs of the same sequence, the prefix visible to the last query ----------
+  auto first_run_from = [&](int j) -> TilePos {
+    for (; j < p.n_kv_segs; ++j) {
+      const Seg ks = p.ks[j];
+      if (ks.seq != qs.seq) continue;
+      const int vis = visible_prefix(ks, qpos_hi, p.causal);
+      if (vis > 0) return TilePos{j, 0, vis, ks.loc, ks.pos, ks.len};
+    }
+    return TilePos{p.n_kv_segs, 0, 0, 0, 0, 1};
   };
-  int j = 0;
-  while (j < p.n_kv_segs && run_visible(j) == 0) ++j;
-  int kt = 0;
+  auto next_tile = [&](TilePos t) -> TilePos {
+    if (t.j >= p.n_kv_segs) return t;
+    if (t.kt + C::kBN < t.vis) {
+      t.kt += C::kBN;
+      return t;
+    }
+    return first_run_from(t.j + 1);
+  };
 
-  // K/V tile staging: each thread moves 16-byte chunks; a wave covers whole 256-byte key rows.
-  static_assert(C::kPasses == 1 || C::kPasses == 2, "one or two staging passes per tile");
+  // K/V staging: each thread moves 16-byte chunks; a wave covers whole key rows.
   const int ld_chunk = tid % C::kChunks;
   const int ld_row0 = tid / C::kChunks;
   const int64_t kv_row_stride = (int64_t)p.n_kv * D;
   const __bf16* Kg = K + (int64_t)g * D + ld_chunk * 8;
   const __bf16* Vg = V + (int64_t)g * D + ld_chunk * 8;
-  u32x4 kb0, kb1, vb0, vb1;  // next tile, in flight during the current tile's math
-#define CP_TILE_LOAD(JJ, KK)                                                      \
+  u32x4 kst[C::kPasses], vst[C::kPasses];  // a tile on its way from HBM to LDS
+#define CP_TILE_LOAD(T)                                                           \
   {                                                                               \
-    const Seg ks_ = p.ks[JJ];                                                     \
-    const int key0 = min((KK) + ld_row0, ks_.len - 1);                            \
-    const int64_t o0 = (int64_t)(ks_.loc + key0) * kv_row_stride;                 \
-    kb0 = *reinterpret_cast<const u32x4*>(Kg + o0);                               \
-    vb0 = *reinterpret_cast<const u32x4*>(Vg + o0);                               \
-    if constexpr (C::kPasses == 2) {                                              \
-      const int key1 = min((KK) + ld_row0 + C::kRowsPerPass, ks_.len - 1);        \
-      const int64_t o1 = (int64_t)(ks_.loc + key1) * kv_row_stride;               \
-      kb1 = *reinterpret_cast<const u32x4*>(Kg + o1);                             \
-      vb1 = *reinterpret_cast<const u32x4*>(Vg + o1);                             \
+    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                   \
+      const int key = min((T).kt + ld_row0 + ps * C::kRowsPerPass, (T).len - 1);  \
+      const int64_t o = (int64_t)((T).loc + key) * kv_row_stride;                 \
+      kst[ps] = *reinterpret_cast<const u32x4*>(Kg + o);                          \
+      vst[ps] = *reinterpret_cast<const u32x4*>(Vg + o);                          \
     }                                                                             \
   }
 #define CP_TILE_STORE(STAGE)                                                      \
   {                                                                               \
     unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                        \
     unsigned char* vt_s = kt_s + C::kBN * C::kStrideK;                            \
-    *reinterpret_cast<u32x4*>(kt_s + ld_row0 * C::kStrideK + ld_chunk * 16) = kb0; \
-    *reinterpret_cast<u32x4*>(vt_s + ld_row0 * C::kStrideV + ld_chunk * 16) = vb0; \
-    if constexpr (C::kPasses == 2) {                                              \
-      *reinterpret_cast<u32x4*>(kt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideK + ld_chunk * 16) = kb1; \
-      *reinterpret_cast<u32x4*>(vt_s + (ld_row0 + C::kRowsPerPass) * C::kStrideV + ld_chunk * 16) = vb1; \
+    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                   \
+      const int rr = ld_row0 + ps * C::kRowsPerPass;                              \
+      *reinterpret_cast<u32x4*>(kt_s + rr * C::kStrideK + ld_chunk * 16) = kst[ps]; \
+      *reinterpret_cast<u32x4*>(vt_s + rr * C::kStrideV + ld_chunk * 16) = vst[ps]; \
     }                                                                             \
   }
+
+  // S^T = K Q^T of the tile in stage `st`: two 32-key halves against this wave's 32 queries.
+  auto qk = [&](int st, f32x16 (&s)[2]) {
+    const unsigned char* Kt = smem + st * C::kStageBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int k = 0; k < C::kKSteps; ++k) {
+      const int coff = (half * (D / 2) + k * 8) * 2;
+      const bf16x8 a0 = lds_read_b128(Kt, col * C::kStrideK + coff);
+      const bf16x8 a1 = lds_read_b128(Kt, (32 + col) * C::kStrideK + coff);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[k], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[k], s[1], 0, 0, 0);
+    }
+  };
 
   float m = -INFINITY;  // max in use, base-2 scaled units (same in both half-waves)
   float l = 0.f;        // running sum over this half-wave's keys
@@ -174,12 +211,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
 
-  if (j < p.n_kv_segs) {
-    CP_TILE_LOAD(j, kt);
-    CP_TILE_STORE(0);
-  }
-  __syncthreads();
-
   // V^T operand addressing for ds_read_b64_tr_b16: each 16-lane group covers 16 d-rows
   const int grp = lane >> 4;          // 0..3
   const int dsub = grp & 1;           // which 16 of the 32 d-rows
@@ -187,44 +218,46 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
   const int tr_key = 4 * half + (j16 >> 2);
   const int tr_dcol = dsub * 16 + 4 * (j16 & 3);
 
-  int stage = 0;
-  while (j < p.n_kv_segs) {
-    // next tile (uniform across the workgroup)
-    int nj = j, nkt = kt + C::kBN;
-    if (nkt >= run_visible(j)) {
-      nj = j + 1;
-      while (nj < p.n_kv_segs && run_visible(nj) == 0) ++nj;
-      nkt = 0;
+  // ---- prologue: tiles 0 and 1 into stages 0 and 1, tile 2 in flight, QK^T of tile 0 ----
+  TilePos cur = first_run_from(0);
+  TilePos nxt = next_tile(cur);
+  TilePos nn = next_tile(nxt);
+  const bool any = cur.j < p.n_kv_segs;
+  if (any) {
+    CP_TILE_LOAD(cur);
+    CP_TILE_STORE(0);
+  }
+  if (nxt.j < p.n_kv_segs) {
+    CP_TILE_LOAD(nxt);
+    CP_TILE_STORE(1);
+  }
+  if (nn.j < p.n_kv_segs) CP_TILE_LOAD(nn);
+  __syncthreads();
+  f32x16 s_next[2];
+  if (any) qk(0, s_next);
+
+  int st_cur = 0;  // stage of tile cur; tile nxt is in st_cur+1, tile nn goes to st_cur+2 (mod 3)
+  while (cur.j < p.n_kv_segs) {
+    const int st_nxt = st_cur == 2 ? 0 : st_cur + 1;
+    const int st_nn = st_nxt == 2 ? 0 : st_nxt + 1;
+    // tile nn: registers -> LDS (its stage was last read by tile cur-1, before the last barrier)
+    const TilePos n3 = next_tile(nn);
+    if (nn.j < p.n_kv_segs) {
+      CP_TILE_STORE(st_nn);
+      if (n3.j < p.n_kv_segs) CP_TILE_LOAD(n3);
     }
-    const bool has_next = nj < p.n_kv_segs;
-    if (has_next) CP_TILE_LOAD(nj, nkt);
 
-    const Seg ks = p.ks[j];
-    const unsigned char* Kt = smem + stage * C::kStageBytes;
-    const unsigned char* Vt = Kt + C::kBN * C::kStrideK;
-
-    // ---- S^T = K Q^T: two 32-key halves of the tile against this wave's 32 queries ----
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-    for (int st = 0; st < C::kKSteps; ++st) {
-      const int coff = (half * (D / 2) + st * 8) * 2;
-      const bf16x8 a0 = lds_read_b128(Kt, col * C::kStrideK + coff);
-      const bf16x8 a1 = lds_read_b128(Kt, (32 + col) * C::kStrideK + coff);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[st], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[st], s[1], 0, 0, 0);
-    }
+    for (int kb = 0; kb < 2; ++kb) s[kb] = s_next[kb];
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
-    const int n_full = p.causal ? max(0, min(ks.len, qpos_lo - ks.pos + 1)) : ks.len;
-    if (kt + C::kBN > n_full) {
+    const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
+    if (cur.kt + C::kBN > n_full) {
       // key ko of the run is visible iff ko < len and (not causal or pos + ko <= qpos):
       // ko < lim with lim = min(len, qpos - pos + 1) (or len without the causal mask)
-      const int lim = p.causal ? min(ks.len, qpos - ks.pos + 1) : ks.len;
-      const int base = kt + 4 * half;
+      const int lim = p.causal ? min(cur.len, qpos - cur.pos + 1) : cur.len;
+      const int base = cur.kt + 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -240,7 +273,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+    mx = halfwave_max(mx) * p.scale_log2;
     if (__any(mx > m + kRescaleThreshold)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0; mnew = m -> 1
@@ -253,6 +286,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
         m = mnew;
       }
     }
+    // QK^T of the next tile goes to the MFMA pipe while this tile's exponentials run on the
+    // VALUs (same basic block, so the two interleave). Issued unconditionally: after the last
+    // tile the stage holds stale keys and the result is never used.
+    qk(st_nxt, s_next);
+
     const float msafe = m == -INFINITY ? 0.f : m;
     bf16x8 pb[4];
     float rs = 0.f;
@@ -268,6 +306,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
     l += rs;
 
     // ---- O^T += V^T P^T ----
+    const unsigned char* Vt = smem + st_cur * C::kStageBytes + C::kBN * C::kStrideK;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -281,12 +320,15 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
       }
     }
 
-    if (has_next) CP_TILE_STORE(stage ^ 1);
+    // every wave is done with stage st_cur, and tile nn is visible in stage st_nn
     __syncthreads();
-    stage ^= 1;
-    j = nj;
-    kt = nkt;
+    cur = nxt;
+    nxt = nn;
+    nn = n3;
+    st_cur = st_nxt;
   }
+#undef CP_TILE_LOAD
+#undef CP_TILE_STORE
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2, optional merge into the running result
   const float lt = l + __shfl_xor(l, 32);
@@ -321,17 +363,16 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnParams p) {
       *reinterpret_cast<float4*>(orow + db * 32 + 8 * vq + 4 * half) = o4;
     }
   if (half == 0) p.lse[qrow] = lse_out;
-#undef CP_TILE_LOAD
-#undef CP_TILE_STORE
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream) {
   const dim3 grid(p.total_tiles, p.n_kv);
-  const dim3 block(Bf16Cfg<128>::kThreads);
+  constexpr int W = kTileRowsBf16 / 32;
+  const dim3 block(W * 64);
   if (d_h == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, W>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, W>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -89,6 +89,9 @@ hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream);
 
 // Rows per workgroup tile of each attention kernel (the host plans tiles with these).
 constexpr int kTileRowsF32 = 64;
-constexpr int kTileRowsBf16 = 256;
+#ifndef CP_BF16_TILE_ROWS
+#define CP_BF16_TILE_ROWS 256
+#endif
+constexpr int kTileRowsBf16 = CP_BF16_TILE_ROWS;
 
 }  // namespace cpk
