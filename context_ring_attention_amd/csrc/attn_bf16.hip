@@ -233,11 +233,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   }
   if (nn.j < p.n_kv_segs) CP_TILE_LOAD(nn);
   __syncthreads();
-  f32x16 s_next[2];
-  if (any) qk(0, s_next);
-
   int st_cur = 0;  // stage of tile cur; tile nxt is in st_cur+1, tile nn goes to st_cur+2 (mod 3)
-  while (cur.j < p.n_kv_segs) {
+  // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's.
+  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2]) {
     const int st_nxt = st_cur == 2 ? 0 : st_cur + 1;
     const int st_nn = st_nxt == 2 ? 0 : st_nxt + 1;
     // tile nn: registers -> LDS (its stage was last read by tile cur-1, before the last barrier)
@@ -246,10 +244,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
       CP_TILE_STORE(st_nn);
       if (n3.j < p.n_kv_segs) CP_TILE_LOAD(n3);
     }
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = s_next[kb];
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
     const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
@@ -289,7 +283,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     // QK^T of the next tile goes to the MFMA pipe while this tile's exponentials run on the
     // VALUs (same basic block, so the two interleave). Issued unconditionally: after the last
     // tile the stage holds stale keys and the result is never used.
-    qk(st_nxt, s_next);
+    qk(st_nxt, s_nx);
 
     const float msafe = m == -INFINITY ? 0.f : m;
     bf16x8 pb[4];
@@ -326,6 +320,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     nxt = nn;
     nn = n3;
     st_cur = st_nxt;
+  };
+  // Two steps per trip with the score buffers swapping roles (no register copies).
+  f32x16 sa[2], sb[2];
+  if (any) qk(0, sa);
+  while (cur.j < p.n_kv_segs) {
+    step(sa, sb);
+    if (cur.j >= p.n_kv_segs) break;
+    step(sb, sa);
   }
 #undef CP_TILE_LOAD
 #undef CP_TILE_STORE
