@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_prefill_128k_cp4_counters.md")
 
 
 def parse():
@@ -64,6 +65,28 @@ def visible_pairs(q_segs, kv_segs, causal=True):
                 continue
             total += int(np.clip(p - kp + 1, 0, kn).sum()) if causal else qn * kn
     return total
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the partial-attention kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None
+    line = [l for l in text.splitlines() if l.startswith("traffic_record:")]
+    if not line:
+        return None
+    rec = json.loads(line[-1].split(":", 1)[1])
+    h = hashlib.sha256()
+    for f in rec["files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec
 
 
 class Timer:
@@ -309,10 +332,16 @@ def main():
     avg_ms = float(np.mean(launch_ms))
     avg_flops = float(np.mean(launch_flops))
     achieved = avg_flops / (avg_ms * 1e-3) / 1e12
+    rec = recorded_traffic()
+    traffic = None if rec is None else rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "attn_bf16_kernel<128> (cp_partial_attn)",
                 "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": avg_flops}
+    if rec is not None:
+        roofline["traffic_detail"] = {"unit": "bytes per launch", "read": rec["fetch_bytes_per_launch"],
+                                      "write": rec["write_bytes_per_launch"],
+                                      "source": os.path.relpath(COUNTERS_MD, ROOT)}
     log(f"cp_partial_attn: avg {avg_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s, "
         f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
 
