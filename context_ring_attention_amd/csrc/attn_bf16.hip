@@ -90,13 +90,6 @@ struct TilePos {
   int loc, pos, len;
 };
 
-// Max of x over the two half-waves (lane l and lane l ^ 32) without going through LDS.
-__device__ inline float halfwave_max(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-}
-
 template <int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES>;
@@ -267,7 +260,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = halfwave_max(mx) * p.scale_log2;
+    mx = max_xor32(mx) * p.scale_log2;
     if (__any(mx > m + kRescaleThreshold)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0; mnew = m -> 1

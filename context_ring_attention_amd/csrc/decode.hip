@@ -8,14 +8,15 @@
 // The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
 // against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
 // 16-head block) and walks its keys in blocks of 32:
-//  - S^T = K q^T on v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads per MFMA, K rows loaded from
-//    HBM straight into the A operand (each lane reads 64 contiguous bytes of one key row), q^T
-//    held in registers;
-//  - the V block goes through LDS in its row-major layout and comes back as the V^T operand of
-//    O^T += V^T P^T via ds_read_b64_tr_b16;
-//  - the next block's K and V loads are issued before the current block's math.
+//  - K and V blocks are loaded with whole-row 16-byte accesses and staged in LDS in their
+//    row-major layout;
+//  - S^T = K q^T on v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads per MFMA, q^T held in
+//    registers;
+//  - V comes back from LDS as the V^T operand of O^T += V^T P^T via ds_read_b64_tr_b16;
+//  - the next block's K and V loads are issued before the current block's math, and the first
+//    block's loads are in flight together with the query's.
 // The merge kernel then combines the S partials of each (request, head) with the same
-// LSE-weighted rule as cp_merge_lse.
+// LSE-weighted rule as cp_merge_lse, reading each head's partials as one contiguous block.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
@@ -42,19 +43,39 @@ struct DecCfg {
   static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
   static constexpr int kChunks = D / 8;          // 16-byte chunks per key row
   static constexpr int kVLoads = kBK * kChunks / 64;
+#ifdef CP_DEC_K_DIRECT
+  static constexpr bool kKDirect = true;
+#else
+  static constexpr bool kKDirect = false;
+#endif
 };
 
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char ks[C::kBK * C::kStrideK];
+  __shared__ __attribute__((aligned(16))) unsigned char ks[C::kKDirect ? 16 : C::kBK * C::kStrideK];
   __shared__ __attribute__((aligned(16))) unsigned char vs[C::kBK * C::kStrideV];
 
-  const int c = blockIdx.x;  // split
-  const int b = blockIdx.y;  // request
+  const int c = blockIdx.x % p.n_splits;  // split (fastest: neighbours stream adjacent keys)
+  // Requests are taken longest first, so the last workgroups to be dispatched are the shortest
+  // splits and the tail of the launch stays short. For batches of up to 64 requests, lane i ranks
+  // request i by length (ties by index) and the workgroup picks the request of rank blockIdx/S.
+  int b = blockIdx.x / p.n_splits;
+  if (p.batch <= 64) {
+    const int want = b;
+    const int i = threadIdx.x;
+    const int64_t li = i < p.batch ? p.kv_len[i] : -1;
+    int rank = 0;
+    for (int j = 0; j < p.batch; ++j) {
+      const int64_t lj = p.kv_len[j];
+      rank += (lj > li) || (lj == li && j < i);
+    }
+    const unsigned long long hit = __ballot(i < p.batch && rank == want);
+    b = __ffsll(hit) - 1;
+  }
   const int hblocks = (p.group + 15) / 16;
-  const int g = blockIdx.z / hblocks;
-  const int h0 = (blockIdx.z % hblocks) * 16;
+  const int g = blockIdx.y / hblocks;
+  const int h0 = (blockIdx.y % hblocks) * 16;
   const int lane = threadIdx.x;
   const int col = lane & 15;  // head column of the 16x16 blocks
   const int grp = lane >> 4;  // 0..3: k slice of the operands, row group of the accumulator
@@ -67,40 +88,55 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const __bf16* __restrict__ Kc = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ Vc = static_cast<const __bf16*>(p.v);
 
-  // q^T operand: lane holds q[head h0+col][grp*(D/4) + st*8 + e]
+  // q^T operand: lane holds q[head h0+col][st*32 + grp*8 + e] (the K operand uses the same
+  // permutation of the head dimension, so the MFMA's reduction covers every d once)
   const int hig = h0 + col;
   const bool head_ok = hig < p.group;
   const int head = g * p.group + (head_ok ? hig : 0);
   bf16x8 qreg[C::kKSteps];
   {
-    const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.n_h + head) * D + grp * (D / 4);
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.n_h + head) * D + grp * 8;
 #pragma unroll
     for (int st = 0; st < C::kKSteps; ++st) {
-      qreg[st] = *reinterpret_cast<const bf16x8*>(qp + st * 8);
+      qreg[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
       if (!head_ok) qreg[st] = bf16x8{};
     }
   }
 
-  // Loads of one 32-key block: every instruction reads four whole key rows (16 lanes x 16 bytes
-  // per row), for K and for V; the rows are staged in LDS in their row-major layout.
-  u32x4 kr[C::kVLoads], vr[C::kVLoads];
+  // Loads of one 32-key block. V (and K through LDS): every instruction reads four whole key
+  // rows (16 lanes x 16 bytes per row). K direct: lane (grp, col) reads 16 bytes of key row col
+  // (+16 for the second half) at d offset st*32 + grp*8, as the MFMA A operand, so each load
+  // instruction covers 64 contiguous bytes of 16 rows.
   const __bf16* Kr = Kc + (base + lo) * p.n_kv * D + (int64_t)g * D;
   const __bf16* Vr = Vc + (base + lo) * p.n_kv * D + (int64_t)g * D;
   const int64_t row_stride = (int64_t)p.n_kv * D;
-#define CP_DEC_LOAD(KB0)                                                             \
+  u32x4 kr[C::kVLoads], vr[C::kVLoads];
+  bf16x8 kop[2][C::kKSteps];  // K operand of the block being computed (direct mode)
+  bf16x8 knx[2][C::kKSteps];  // K operand of the next block (direct mode)
+#define CP_DEC_LOAD_V(KB0)                                                           \
   _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
     const int idx = i * 64 + lane;                                                   \
     const int key = min((KB0) + idx / C::kChunks, n - 1);                            \
     const int64_t off = key * row_stride + (idx % C::kChunks) * 8;                   \
-    kr[i] = *reinterpret_cast<const u32x4*>(Kr + off);                               \
     vr[i] = *reinterpret_cast<const u32x4*>(Vr + off);                               \
+    if constexpr (!C::kKDirect) kr[i] = *reinterpret_cast<const u32x4*>(Kr + off);   \
+  }
+#define CP_DEC_LOAD_K(KB0, DST)                                                      \
+  if constexpr (C::kKDirect) {                                                       \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                  \
+      const int key = min((KB0) + 16 * h + col, n - 1);                              \
+      const __bf16* kp = Kr + key * row_stride + grp * 8;                            \
+      _Pragma("unroll") for (int st = 0; st < C::kKSteps; ++st)                      \
+        DST[h][st] = *reinterpret_cast<const bf16x8*>(kp + st * 32);                 \
+    }                                                                                \
   }
 #define CP_DEC_STORE()                                                               \
   _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
     const int idx = i * 64 + lane;                                                   \
     const int row = idx / C::kChunks, c16 = (idx % C::kChunks) * 16;                 \
-    *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];                 \
     *reinterpret_cast<u32x4*>(vs + row * C::kStrideV + c16) = vr[i];                 \
+    if constexpr (!C::kKDirect)                                                      \
+      *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];               \
   }
 
   float m = -INFINITY, l = 0.f;
@@ -113,16 +149,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int tr_row = 4 * grp + (j16 >> 2);
   const int tr_col = 4 * (j16 & 3);
 
-  // retire the q loads before the block loop (keeps the loop's prefetch out of its waits)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
   if (n > 0) {
-    CP_DEC_LOAD(0);
-    CP_DEC_STORE();
+    CP_DEC_LOAD_V(0);
+    CP_DEC_LOAD_K(0, kop);
   }
+  // retire the q and first-block loads together before the block loop (keeps the loop's
+  // prefetch out of its waits)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (n > 0) CP_DEC_STORE();
   __syncthreads();
   for (int kb0 = 0; kb0 < n; kb0 += C::kBK) {
     const bool has_next = kb0 + C::kBK < n;
-    if (has_next) CP_DEC_LOAD(kb0 + C::kBK);
+    if (has_next) {
+      CP_DEC_LOAD_V(kb0 + C::kBK);
+      CP_DEC_LOAD_K(kb0 + C::kBK, knx);
+    }
 
     // S^T (keys x heads) for the two 16-key halves; K operand: key row col, d slice of grp
     f32x4 s[2];
@@ -131,8 +172,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < C::kKSteps; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            ks + (16 * h + col) * C::kStrideK + (grp * (D / 4) + st * 8) * 2);
+        bf16x8 a;
+        if constexpr (C::kKDirect)
+          a = kop[h][st];
+        else
+          a = *reinterpret_cast<const bf16x8*>(ks + (16 * h + col) * C::kStrideK + (st * 32 + grp * 8) * 2);
         s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[st], s[h], 0, 0, 0);
       }
     }
@@ -149,8 +193,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[h][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float mnew = fmaxf(m, mx * p.scale_log2);  // the block always holds a visible key
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
@@ -181,17 +224,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
                                                           oacc[db], 0, 0, 0);
     }
     __syncthreads();
-    if (has_next) CP_DEC_STORE();
+    if (has_next) {
+      CP_DEC_STORE();
+      if constexpr (C::kKDirect) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int st = 0; st < C::kKSteps; ++st) kop[h][st] = knx[h][st];
+      }
+    }
     __syncthreads();
   }
-#undef CP_DEC_LOAD
+#undef CP_DEC_LOAD_V
+#undef CP_DEC_LOAD_K
 #undef CP_DEC_STORE
 
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
   if (!head_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const int64_t prow = ((int64_t)b * p.n_splits + c) * p.n_h + head;
+  // workspace layout [batch][n_h][n_splits][D]: a head's partials are contiguous
+  const int64_t prow = ((int64_t)b * p.n_h + head) * p.n_splits + c;
   float* wo = p.ws_o + prow * D;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) {
@@ -201,8 +254,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   if (grp == 0) p.ws_lse[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-// Merge of the S split partials of each (request, head): one workgroup per (request, head);
-// 256 / (D/4) groups of D/4 lanes take every kGroups-th split, then combine through LDS.
+// Merge of the S split partials of each (request, head): one workgroup per (request, head),
+// whose partials are one contiguous [S][D] block. 256 / (D/4) groups of D/4 lanes take every
+// kGroups-th split with an online (running-max) combine, so all loads issue without waiting for
+// a global max; the groups are then combined through LDS in a fixed order.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
   constexpr int kLanes = D / 4;
@@ -211,39 +266,42 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   __shared__ float red_w[kGroups];
   __shared__ float4 red_o[kGroups][kLanes];
   const int r = blockIdx.x;  // b * n_h + head
-  const int b = r / p.n_h;
-  const int head = r % p.n_h;
   const int grp = threadIdx.x / kLanes;
   const int c4 = threadIdx.x % kLanes;
-  const int64_t stride = (int64_t)p.n_h;
-  const float* lse = p.ws_lse + (int64_t)b * p.n_splits * p.n_h + head;
-  const float* o = p.ws_o + ((int64_t)b * p.n_splits * p.n_h + head) * D + c4 * 4;
+  const float* lse = p.ws_lse + (int64_t)r * p.n_splits;
+  const float* o = p.ws_o + (int64_t)r * p.n_splits * D + c4 * 4;
 
-  float M = -INFINITY;
-  for (int c = grp; c < p.n_splits; c += kGroups) M = fmaxf(M, lse[c * stride]);
+  float M = -INFINITY, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int c = grp; c < p.n_splits; c += kGroups) {
+    const float li = lse[c];
+    const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)c * D);
+    if (li == -INFINITY) continue;
+    if (li > M) {  // move the running max; earlier weights shrink by exp(M_old - M_new)
+      const float a = expf(M - li);  // M = -inf -> 0
+      wsum *= a;
+      acc.x *= a;
+      acc.y *= a;
+      acc.z *= a;
+      acc.w *= a;
+      M = li;
+    }
+    const float w = expf(li - M);
+    wsum += w;
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
   if (c4 == 0) red_m[grp] = M;
   __syncthreads();
-  M = red_m[0];
+  float Mt = red_m[0];
 #pragma unroll
-  for (int i = 1; i < kGroups; ++i) M = fmaxf(M, red_m[i]);
-
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int c = grp; c < p.n_splits; c += kGroups) {
-      const float li = lse[c * stride];
-      if (li == -INFINITY) continue;
-      const float w = expf(li - M);
-      const float4 v = *reinterpret_cast<const float4*>(o + c * stride * D);
-      wsum += w;
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
-    }
-  }
-  red_o[grp][c4] = acc;
-  if (c4 == 0) red_w[grp] = wsum;
+  for (int i = 1; i < kGroups; ++i) Mt = fmaxf(Mt, red_m[i]);
+  const float a = (M == -INFINITY) ? 0.f : expf(M - Mt);
+  red_o[grp][c4] = make_float4(acc.x * a, acc.y * a, acc.z * a, acc.w * a);
+  if (c4 == 0) red_w[grp] = wsum * a;
   __syncthreads();
   if (grp != 0) return;
   wsum = 0.f;
@@ -267,12 +325,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     *reinterpret_cast<float4*>(static_cast<float*>(p.o_out) + orow) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  if (c4 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+  if (c4 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
   const int hblocks = (p.group + 15) / 16;
-  const dim3 grid(p.n_splits, p.batch, p.n_kv * hblocks);
+  const dim3 grid(p.n_splits * p.batch, p.n_kv * hblocks);
   const dim3 mgrid(p.batch * p.n_h);
   if (d_h == 64) {
     hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64), 0, stream, p);

@@ -51,4 +51,19 @@ __device__ inline void running_merge_weights(float lse_prev, float lse_new, floa
   lse_out = M + logf(s);
 }
 
+// Max of x over lanes l and l ^ 32 (the two half-waves), without going through LDS: swapping
+// the upper half of one copy with the lower half of another leaves each lane holding both values.
+__device__ inline float max_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+}
+
+// Max of x over lanes l and l ^ 16 (odd and even 16-lane rows), without going through LDS.
+__device__ inline float max_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+}
+
 }  // namespace cpk
