@@ -5,8 +5,8 @@ The computation lives in ``libcpattn.so`` (hand-written HIP kernels behind the C
 """
 from .binding import (CP_BF16, CP_F32, CpError, CpSegment, decode_splitkv, decode_workspace_bytes,
                       last_error, load, merge_lse, partial_attn, ring_pass_kv, ring_pass_q,
-                      segments, shard_map)
+                      segments, select_ring_variant, shard_map)
 
 __all__ = ["CP_BF16", "CP_F32", "CpError", "CpSegment", "decode_splitkv", "decode_workspace_bytes",
            "last_error", "load", "merge_lse", "partial_attn", "ring_pass_kv", "ring_pass_q",
-           "segments", "shard_map"]
+           "segments", "select_ring_variant", "shard_map"]

@@ -21,9 +21,11 @@ CP_F32, CP_BF16 = 0, 1
 CP_MAX_SEGMENTS = 64
 CP_MAX_MERGE_PARTS = 64
 
+CP_PASS_KV, CP_PASS_Q = 0, 1
+
 EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
             "cp_decode_workspace_bytes", "cp_ring_pass_kv", "cp_ring_pass_q",
-            "cp_status_string", "cp_last_error")
+            "cp_select_ring_variant", "cp_status_string", "cp_last_error")
 
 
 class CpSegment(ctypes.Structure):
@@ -85,8 +87,11 @@ def load():
                                    i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
                                    i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), i32, ctypes.POINTER(vp), vp]
+    lib.cp_select_ring_variant.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_double,
+                                           ctypes.c_double, ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]
     for name in ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
-                 "cp_ring_pass_kv", "cp_ring_pass_q"):
+                 "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant"):
         getattr(lib, name).restype = ctypes.c_int
     lib.cp_status_string.argtypes = [ctypes.c_int]
     lib.cp_status_string.restype = ctypes.c_char_p
@@ -241,6 +246,19 @@ def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool
                                _dtype_code(q), int(causal), float(softmax_scale), op, lp,
                                _ptr(o_acc), _ptr(lse_acc), _ptr(o_out), _dtype_code(o_out),
                                _ptr(lse_out), _stream(stream)))
+
+
+def select_ring_variant(new_tokens: int, cached_tokens: int, cp_world: int, n_h: int, n_kv: int,
+                        d_h: int, elem_bytes: int, link_bytes_per_s: float,
+                        attn_flops_per_s: float):
+    """cp_select_ring_variant. Returns ("pass_kv" | "pass_q", reason)."""
+    lib = load()
+    v = ctypes.c_int(-1)
+    r = ctypes.c_int(-1)
+    _check(lib.cp_select_ring_variant(new_tokens, cached_tokens, cp_world, n_h, n_kv, d_h,
+                                      elem_bytes, float(link_bytes_per_s),
+                                      float(attn_flops_per_s), ctypes.byref(v), ctypes.byref(r)))
+    return ("pass_kv" if v.value == CP_PASS_KV else "pass_q"), r.value
 
 
 def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, softmax_scale: float,

@@ -374,4 +374,32 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
   return ok();
 }
 
+// Algorithm 1 of [CPMTI §3 "核心公式"]: Pass-KV if the KV-cache miss rate exceeds 2 N_KV / N_H or
+// if a ring step's KV transfer hides behind its attention compute; Pass-Q otherwise.
+int cp_select_ring_variant(int64_t new_tokens, int64_t cached_tokens, int cp_world, int n_h,
+                           int n_kv, int d_h, int elem_bytes, double link_bytes_per_s,
+                           double attn_flops_per_s, int* variant_out, int* reason_out) {
+  if (!variant_out) return fail(CP_E_ARG, "variant_out is NULL");
+  if (new_tokens < 1 || cached_tokens < 0) return fail(CP_E_ARG, "need T >= 1 and P >= 0");
+  if (cp_world < 1 || n_h < 1 || n_kv < 1 || d_h < 1 || elem_bytes < 1)
+    return fail(CP_E_ARG, "sizes must be positive");
+  if (n_h % n_kv != 0) return fail(CP_E_SHAPE, "n_h=%d is not a multiple of n_kv=%d", n_h, n_kv);
+  if (!(link_bytes_per_s > 0) || !(attn_flops_per_s > 0))
+    return fail(CP_E_ARG, "bandwidth and throughput estimates must be > 0");
+  const double T = (double)new_tokens, P = (double)cached_tokens, N = (double)cp_world;
+  const double miss = T / (T + P);
+  const double threshold = 2.0 * n_kv / n_h;
+  int reason = 0;
+  if (miss > threshold) {
+    reason = 1;
+  } else {
+    const double kv_bytes = 2.0 * (T + P) / N * n_kv * d_h * elem_bytes;
+    const double flops = 4.0 * d_h * n_h * (T / N) * ((T + P) / N - T / (2.0 * N));
+    if (kv_bytes / link_bytes_per_s <= flops / attn_flops_per_s) reason = 2;
+  }
+  *variant_out = reason ? CP_PASS_KV : CP_PASS_Q;
+  if (reason_out) *reason_out = reason;
+  return ok();
+}
+
 }  // extern "C"

@@ -177,6 +177,25 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
                    float* const* o_parts, float* const* lse_parts, void* const* o_out,
                    cp_dtype out_dtype, float* const* lse_out, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * cp_select_ring_variant -- runtime choice between ring Pass-KV and ring Pass-Q ([CPMTI §3
+ * "核心公式", Algorithm 1]): Pass-KV when the KV-cache miss rate T / (T + P) exceeds
+ * 2 * N_KV / N_H (condition 1), or when the SendRecv of one ring step can be hidden behind that
+ * step's attention compute (condition 2); Pass-Q otherwise. Host-only, launches nothing.
+ *   new_tokens T >= 1, cached_tokens P >= 0; elem_bytes: bytes per K/V element.
+ *   link_bytes_per_s, attn_flops_per_s: the caller's estimates of the ring link bandwidth and of
+ *     the attention throughput (> 0). Condition 2 compares, per ring step and rank, the time to
+ *     pass one KV shard, 2 * (T + P) / N * N_KV * D_H * elem_bytes bytes, with the causal
+ *     attention work of one step, 4 * D_H * N_H * (T / N) * ((T + P) / N - T / (2N)) flops (the new
+ *     tokens against one shard of the context, half of the new-token block being masked).
+ *   *variant_out: CP_PASS_KV or CP_PASS_Q. *reason_out (optional): 1 = miss rate above the
+ *     threshold, 2 = transfer hidden by compute, 0 = neither (Pass-Q).
+ * ------------------------------------------------------------------------------------------- */
+typedef enum { CP_PASS_KV = 0, CP_PASS_Q = 1 } cp_ring_variant;
+int cp_select_ring_variant(int64_t new_tokens, int64_t cached_tokens, int cp_world, int n_h,
+                           int n_kv, int d_h, int elem_bytes, double link_bytes_per_s,
+                           double attn_flops_per_s, int* variant_out, int* reason_out);
+
 /* Human-readable name of a cp_status value. */
 const char* cp_status_string(int status);
 /* Message of the last failing call on this thread ("" if none). */
