@@ -1,9 +1,10 @@
 """Algorithm 1 (ring Pass-KV vs Pass-Q selection) of "Context Parallelism for Scalable
-Million-Token Inference" (xllm-io review), section 3: Pass-KV when the KV-cache miss rate exceeds
+Million-Token Inference" (xllm-io review), section "核心公式": Pass-KV when the KV-cache miss rate exceeds
 2 N_KV / N_H or when SendRecv hides behind attention compute, Pass-Q otherwise.
 
 Pinned against the page's own figures: the threshold is 12.5% for 128 query heads and 8 KV heads;
-the measured switch point is T=6400 new tokens on P=121600 cached (5%, section 6 table)."""
+the measured switch point is T=6400 new tokens on P=121600 cached (5%, the Pass-KV vs Pass-Q
+latency table)."""
 import pytest
 
 from context_ring_attention_amd import binding as cp
