@@ -155,18 +155,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   // K/V staging: each thread moves 16-byte chunks; a wave covers whole key rows.
   const int ld_chunk = tid % C::kChunks;
   const int ld_row0 = tid / C::kChunks;
-  const int64_t kv_row_stride = (int64_t)p.n_kv * D;
-  const __bf16* Kg = K + (int64_t)g * D + ld_chunk * 8;
-  const __bf16* Vg = V + (int64_t)g * D + ld_chunk * 8;
+  // Addresses: the tile's first key row is a uniform 64-bit base (scalar arithmetic); a lane
+  // adds a 32-bit offset (its row inside the tile, clamped to the run's last key, and its chunk).
+  const uint32_t row_bytes = (uint32_t)p.n_kv * D * 2;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + (int64_t)g * D);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + (int64_t)g * D);
+  uint32_t row_off[C::kPasses];  // byte offset of this lane's row in pass ps of a tile
+#pragma unroll
+  for (int ps = 0; ps < C::kPasses; ++ps) row_off[ps] = (ld_row0 + ps * C::kRowsPerPass) * row_bytes;
   u32x4 kst[C::kPasses], vst[C::kPasses];  // a tile on its way from HBM to LDS
-#define CP_TILE_LOAD(T)                                                           \
-  {                                                                               \
-    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                   \
-      const int key = min((T).kt + ld_row0 + ps * C::kRowsPerPass, (T).len - 1);  \
-      const int64_t o = (int64_t)((T).loc + key) * kv_row_stride;                 \
-      kst[ps] = *reinterpret_cast<const u32x4*>(Kg + o);                          \
-      vst[ps] = *reinterpret_cast<const u32x4*>(Vg + o);                          \
-    }                                                                             \
+#define CP_TILE_LOAD(T)                                                                   \
+  {                                                                                       \
+    const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                        \
+    const uint32_t last_off = (uint32_t)min((T).len - 1 - (T).kt, C::kBN - 1) * row_bytes; \
+    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                           \
+      const uint32_t o = min(row_off[ps], last_off) + ld_chunk * 16;                      \
+      kst[ps] = *reinterpret_cast<const u32x4*>(Kb + first + o);                          \
+      vst[ps] = *reinterpret_cast<const u32x4*>(Vb + first + o);                          \
+    }                                                                                     \
   }
 #define CP_TILE_STORE(STAGE)                                                      \
   {                                                                               \
