@@ -163,8 +163,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   uint32_t row_off[C::kPasses];  // byte offset of this lane's row in pass ps of a tile
 #pragma unroll
   for (int ps = 0; ps < C::kPasses; ++ps) row_off[ps] = (ld_row0 + ps * C::kRowsPerPass) * row_bytes;
-  u32x4 kst[C::kPasses], vst[C::kPasses];  // a tile on its way from HBM to LDS
-#define CP_TILE_LOAD(T)                                                                   \
+  // Two tiles on their way from HBM to LDS: a tile is loaded two steps before it is stored,
+  // so the load latency hides behind two tiles of work.
+  u32x4 kst0[C::kPasses], vst0[C::kPasses], kst1[C::kPasses], vst1[C::kPasses];
+#define CP_TILE_LOAD(T, kst, vst)                                                         \
   {                                                                                       \
     const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                        \
     const uint32_t last_off = (uint32_t)min((T).len - 1 - (T).kt, C::kBN - 1) * row_bytes; \
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
       vst[ps] = *reinterpret_cast<const u32x4*>(Vb + first + o);                          \
     }                                                                                     \
   }
-#define CP_TILE_STORE(STAGE)                                                      \
+#define CP_TILE_STORE(STAGE, kst, vst)                                            \
   {                                                                               \
     unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                        \
     unsigned char* vt_s = kt_s + C::kBN * C::kStrideK;                            \
@@ -217,32 +219,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   const int tr_key = 4 * half + (j16 >> 2);
   const int tr_dcol = dsub * 16 + 4 * (j16 & 3);
 
-  // ---- prologue: tiles 0 and 1 into stages 0 and 1, tile 2 in flight, QK^T of tile 0 ----
+  // ---- prologue: tiles 0 and 1 into stages 0 and 1, tiles 2 and 3 in flight, QK^T of tile 0
   TilePos cur = first_run_from(0);
   TilePos nxt = next_tile(cur);
   TilePos nn = next_tile(nxt);
-  const bool any = cur.j < p.n_kv_segs;
-  if (any) {
-    CP_TILE_LOAD(cur);
-    CP_TILE_STORE(0);
-  }
-  if (nxt.j < p.n_kv_segs) {
-    CP_TILE_LOAD(nxt);
-    CP_TILE_STORE(1);
-  }
-  if (nn.j < p.n_kv_segs) CP_TILE_LOAD(nn);
-  __syncthreads();
+  TilePos n3 = next_tile(nn);
+  // Loads and stores are issued unconditionally once there is a tile (a position past the last
+  // tile reads key row 0 of the shard into a free stage), so the number of loads in flight is
+  // the same on every path and each store waits only for its own tile.
   int st_cur = 0;  // stage of tile cur; tile nxt is in st_cur+1, tile nn goes to st_cur+2 (mod 3)
-  // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's.
-  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2]) {
+  // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's;
+  // (kst, vst) hold tile nn and receive tile nn+2.
+  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2], u32x4 (&kst)[C::kPasses],
+                  u32x4 (&vst)[C::kPasses]) {
     const int st_nxt = st_cur == 2 ? 0 : st_cur + 1;
     const int st_nn = st_nxt == 2 ? 0 : st_nxt + 1;
     // tile nn: registers -> LDS (its stage was last read by tile cur-1, before the last barrier)
-    const TilePos n3 = next_tile(nn);
-    if (nn.j < p.n_kv_segs) {
-      CP_TILE_STORE(st_nn);
-      if (n3.j < p.n_kv_segs) CP_TILE_LOAD(n3);
-    }
+    const TilePos n4 = next_tile(n3);
+    CP_TILE_STORE(st_nn, kst, vst);
+    CP_TILE_LOAD(n4, kst, vst);
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
     const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
@@ -318,15 +313,33 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     cur = nxt;
     nxt = nn;
     nn = n3;
+    n3 = n4;
     st_cur = st_nxt;
   };
-  // Two steps per trip with the score buffers swapping roles (no register copies).
+  // Two steps per trip with the score buffers and the staging registers swapping roles (no
+  // register copies). A workgroup without visible keys skips the loop (uniform branch).
   f32x16 sa[2], sb[2];
-  if (any) qk(0, sa);
-  while (cur.j < p.n_kv_segs) {
-    step(sa, sb);
-    if (cur.j >= p.n_kv_segs) break;
-    step(sb, sa);
+  int n_tiles = 0;  // tiles of this workgroup: ceil(visible / kBN) over its runs
+  for (int j = 0; j < p.n_kv_segs; ++j) {
+    const Seg ks = p.ks[j];
+    if (ks.seq == qs.seq) n_tiles += (visible_prefix(ks, qpos_hi, p.causal) + C::kBN - 1) / C::kBN;
+  }
+  if (n_tiles > 0) {
+    CP_TILE_LOAD(cur, kst0, vst0);
+    CP_TILE_STORE(0, kst0, vst0);
+    CP_TILE_LOAD(nxt, kst1, vst1);
+    CP_TILE_STORE(1, kst1, vst1);
+    CP_TILE_LOAD(nn, kst0, vst0);
+    CP_TILE_LOAD(n3, kst1, vst1);
+    __syncthreads();
+    qk(0, sa);
+    // a counted loop without exits in its body keeps the two staging sets' loads in a fixed
+    // order, so each store waits only for its own set
+    for (int it = 0; it + 1 < n_tiles; it += 2) {
+      step(sa, sb, kst0, vst0);
+      step(sb, sa, kst1, vst1);
+    }
+    if (n_tiles & 1) step(sa, sb, kst0, vst0);
   }
 #undef CP_TILE_LOAD
 #undef CP_TILE_STORE
