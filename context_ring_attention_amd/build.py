@@ -61,6 +61,14 @@ def build(jobs: int = 8) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    # A kernel whose host pass was rejected silently loses its launch stub; the library would
+    # link but fail to load. Catch that here.
+    nm = shutil.which("nm")
+    if nm:
+        res = subprocess.run([nm, "-u", tmp], capture_output=True, text=True)
+        missing = [l.split()[-1] for l in res.stdout.splitlines() if "__device_stub__" in l]
+        if missing:
+            raise RuntimeError(f"kernel launch stubs missing from the library: {missing}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

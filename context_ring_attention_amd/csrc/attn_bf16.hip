@@ -47,19 +47,27 @@ struct Bf16Cfg {
   static constexpr int kRows = 32 * WAVES;      // query rows per workgroup
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBN = 64;                // keys per LDS tile
-  // Padded LDS rows. K rows are read 16 bytes at a time by 16 lanes on 16 different rows: a
-  // stride of 4 (mod 64) dwords puts those rows on disjoint bank quads. V rows are read by the
-  // transposing loads, 4 lanes x 8 bytes on each of 4 rows per half-wave: a stride of 16
-  // (mod 64) dwords puts those four 64-byte runs on disjoint banks.
-  static constexpr int kStrideK = D * 2 + 16;
-  static constexpr int kStrideV = D * 2 + 64;
-  static constexpr int kStageBytes = kBN * (kStrideK + kStrideV);
-  static constexpr int kStages = 3;
+  static constexpr int kRowBytes = D * 2;       // LDS rows are unpadded (see the swizzles)
   static constexpr int kChunks = D / 8;         // 16-byte chunks per key row
-  static constexpr int kRowsPerPass = kThreads / kChunks;
-  static constexpr int kPasses = kBN / kRowsPerPass;
+  static constexpr int kTileBytes = kBN * kRowBytes;  // one K or one V tile
+  static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kStages = 4;
+  // A direct-to-LDS load writes 64 lanes x 16 bytes = 1 KB contiguously: a block of rows.
+  static constexpr int kRowsPerBlock = 1024 / kRowBytes;
+  static constexpr int kBlocksPerWave = kTileBytes / 1024 / kWaves;
+  static constexpr int kDmaPerTile = 2 * kBlocksPerWave;  // K and V loads per wave per tile
   static constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 32;       // 32-row blocks of O^T
+  // Rows that share a 256-byte bank cycle (1 for D = 128, 2 for D = 64).
+  static constexpr int kRowsPerBankCycle = 256 / kRowBytes;
+  // Chunk c of key row r sits in slot c ^ swz(r). K rows are read 16 bytes at a time by 16
+  // lanes on 16 consecutive rows: swz_k spreads those rows over the 16 bank quads. V rows are
+  // read by the transposing loads, a half-wave covering 4 consecutive rows x 4 aligned chunks:
+  // swz_v moves each of the 4 rows to its own group of 4 slots.
+  static __device__ __host__ constexpr int swz_k(int r) { return (r / kRowsPerBankCycle) & (kChunks - 1); }
+  static __device__ __host__ constexpr int swz_v(int r) {
+    return ((r / kRowsPerBankCycle) & (4 / kRowsPerBankCycle - 1)) << 2;
+  }
 };
 
 // The running max is only moved when a tile raises it by more than this many base-2 units, so
@@ -152,42 +160,51 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     return first_run_from(t.j + 1);
   };
 
-  // K/V staging: each thread moves 16-byte chunks; a wave covers whole key rows.
-  const int ld_chunk = tid % C::kChunks;
-  const int ld_row0 = tid / C::kChunks;
-  // Addresses: the tile's first key row is a uniform 64-bit base (scalar arithmetic); a lane
-  // adds a 32-bit offset (its row inside the tile, clamped to the run's last key, and its chunk).
+  // K/V staging: HBM -> LDS with direct-to-LDS loads (no VGPRs in between). Wave w fills blocks
+  // w * kBlocksPerWave + i of a tile; in a block, lane l fills row l / kChunks, slot l % kChunks,
+  // which holds chunk slot ^ swz(row). The tile's first key row is a uniform 64-bit base; a lane
+  // adds a 32-bit offset (its row, clamped to the run's last key, and its chunk).
   const uint32_t row_bytes = (uint32_t)p.n_kv * D * 2;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + (int64_t)g * D);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + (int64_t)g * D);
-  uint32_t row_off[C::kPasses];  // byte offset of this lane's row in pass ps of a tile
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dma_row_off[C::kBlocksPerWave], dma_k_chunk[C::kBlocksPerWave],
+      dma_v_chunk[C::kBlocksPerWave];
 #pragma unroll
-  for (int ps = 0; ps < C::kPasses; ++ps) row_off[ps] = (ld_row0 + ps * C::kRowsPerPass) * row_bytes;
-  // Two tiles on their way from HBM to LDS: a tile is loaded two steps before it is stored,
-  // so the load latency hides behind two tiles of work.
-  u32x4 kst0[C::kPasses], vst0[C::kPasses], kst1[C::kPasses], vst1[C::kPasses];
-#define CP_TILE_LOAD(T, kst, vst)                                                         \
-  {                                                                                       \
-    const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                        \
-    const uint32_t last_off = (uint32_t)min((T).len - 1 - (T).kt, C::kBN - 1) * row_bytes; \
-    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                           \
-      const uint32_t o = min(row_off[ps], last_off) + ld_chunk * 16;                      \
-      kst[ps] = *reinterpret_cast<const u32x4*>(Kb + first + o);                          \
-      vst[ps] = *reinterpret_cast<const u32x4*>(Vb + first + o);                          \
-    }                                                                                     \
+  for (int i = 0; i < C::kBlocksPerWave; ++i) {
+    const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
+    const int slot = lane % C::kChunks;
+    dma_row_off[i] = row * row_bytes;
+    dma_k_chunk[i] = (slot ^ C::swz_k(row)) * 16;
+    dma_v_chunk[i] = (slot ^ C::swz_v(row)) * 16;
   }
-#define CP_TILE_STORE(STAGE, kst, vst)                                            \
-  {                                                                               \
-    unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                        \
-    unsigned char* vt_s = kt_s + C::kBN * C::kStrideK;                            \
-    _Pragma("unroll") for (int ps = 0; ps < C::kPasses; ++ps) {                   \
-      const int rr = ld_row0 + ps * C::kRowsPerPass;                              \
-      *reinterpret_cast<u32x4*>(kt_s + rr * C::kStrideK + ld_chunk * 16) = kst[ps]; \
-      *reinterpret_cast<u32x4*>(vt_s + rr * C::kStrideV + ld_chunk * 16) = vst[ps]; \
-    }                                                                             \
+#define CP_TILE_DMA(T, STAGE)                                                                 \
+  {                                                                                           \
+    const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                            \
+    const uint32_t last_off = (uint32_t)min((T).len - 1 - (T).kt, C::kBN - 1) * row_bytes;     \
+    unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                                    \
+    _Pragma("unroll") for (int i = 0; i < C::kBlocksPerWave; ++i) {                           \
+      const uint32_t o = min(dma_row_off[i], last_off);                                       \
+      const int blk = (wave_u * C::kBlocksPerWave + i) * 1024;                                \
+      __builtin_amdgcn_global_load_lds(                                                       \
+          (__attribute__((address_space(1))) void*)(Kb + first + o + dma_k_chunk[i]),         \
+          (__attribute__((address_space(3))) void*)(kt_s + blk), 16, 0, 0);                   \
+      __builtin_amdgcn_global_load_lds(                                                       \
+          (__attribute__((address_space(1))) void*)(Vb + first + o + dma_v_chunk[i]),         \
+          (__attribute__((address_space(3))) void*)(kt_s + C::kTileBytes + blk), 16, 0, 0);   \
+    }                                                                                         \
   }
 
+  // s_waitcnt immediate for vmcnt(kDmaPerTile) (at most 15, the low vmcnt field)
+  static_assert(C::kDmaPerTile < 16, "vmcnt immediate");
+  constexpr int kWaitVmcntDmaLgkm0 = 0x0070 | C::kDmaPerTile;  // also lgkmcnt(0)
+
   // S^T = K Q^T of the tile in stage `st`: two 32-key halves against this wave's 32 queries.
+  // K operand addresses: key rows col and 32 + col (same swizzle), chunk half * D/16 + k.
+  uint32_t k_off[C::kKSteps];
+#pragma unroll
+  for (int k = 0; k < C::kKSteps; ++k)
+    k_off[k] = col * C::kRowBytes + 16 * ((half * (D / 16) + k) ^ C::swz_k(col));
   auto qk = [&](int st, f32x16 (&s)[2]) {
     const unsigned char* Kt = smem + st * C::kStageBytes;
 #pragma unroll
@@ -196,9 +213,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
       for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
     for (int k = 0; k < C::kKSteps; ++k) {
-      const int coff = (half * (D / 2) + k * 8) * 2;
-      const bf16x8 a0 = lds_read_b128(Kt, col * C::kStrideK + coff);
-      const bf16x8 a1 = lds_read_b128(Kt, (32 + col) * C::kStrideK + coff);
+      const bf16x8 a0 = lds_read_b128(Kt, k_off[k]);
+      const bf16x8 a1 = lds_read_b128(Kt, k_off[k] + 32 * C::kRowBytes);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[k], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[k], s[1], 0, 0, 0);
     }
@@ -218,26 +234,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   const int j16 = lane & 15;
   const int tr_key = 4 * half + (j16 >> 2);
   const int tr_dcol = dsub * 16 + 4 * (j16 & 3);
+  // key row 16t + tr_key (+8) has the swizzle of row tr_key; columns db*32 + tr_dcol .. +3
+  uint32_t v_off[C::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db)
+    v_off[db] = tr_key * C::kRowBytes + 16 * (((db * 32 + tr_dcol) / 8) ^ C::swz_v(tr_key)) +
+                8 * (j16 & 1);
 
   // ---- prologue: tiles 0 and 1 into stages 0 and 1, tiles 2 and 3 in flight, QK^T of tile 0
   TilePos cur = first_run_from(0);
   TilePos nxt = next_tile(cur);
   TilePos nn = next_tile(nxt);
   TilePos n3 = next_tile(nn);
-  // Loads and stores are issued unconditionally once there is a tile (a position past the last
-  // tile reads key row 0 of the shard into a free stage), so the number of loads in flight is
-  // the same on every path and each store waits only for its own tile.
-  int st_cur = 0;  // stage of tile cur; tile nxt is in st_cur+1, tile nn goes to st_cur+2 (mod 3)
-  // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's;
-  // (kst, vst) hold tile nn and receive tile nn+2.
-  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2], u32x4 (&kst)[C::kPasses],
-                  u32x4 (&vst)[C::kPasses]) {
-    const int st_nxt = st_cur == 2 ? 0 : st_cur + 1;
-    const int st_nn = st_nxt == 2 ? 0 : st_nxt + 1;
-    // tile nn: registers -> LDS (its stage was last read by tile cur-1, before the last barrier)
-    const TilePos n4 = next_tile(n3);
-    CP_TILE_STORE(st_nn, kst, vst);
-    CP_TILE_LOAD(n4, kst, vst);
+  // Tile loads are issued unconditionally (a position past the last tile reads key row 0 of the
+  // shard into a free stage).
+  int st_cur = 0;  // stage of tile cur; tiles nxt, nn, n3 are in the next stages (mod 4)
+  // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's.
+  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2]) {
+    const int st_nxt = (st_cur + 1) & 3;
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
     const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
@@ -294,30 +308,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     l += rs;
 
     // ---- O^T += V^T P^T ----
-    const unsigned char* Vt = smem + st_cur * C::kStageBytes + C::kBN * C::kStrideK;
+    const unsigned char* Vt = smem + st_cur * C::kStageBytes + C::kTileBytes;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int db = 0; db < C::kDBlocks; ++db) {
-        const int off = (16 * t + tr_key) * C::kStrideV + (db * 32 + tr_dcol) * 2;
+        const uint32_t off = v_off[db] + 16 * t * C::kRowBytes;
         const i16x4 lo = lds_read_tr(Vt, off);
-        const i16x4 hi = lds_read_tr(Vt, off + 8 * C::kStrideV);
+        const i16x4 hi = lds_read_tr(Vt, off + 8 * C::kRowBytes);
         const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 va = __builtin_bit_cast(bf16x8, both);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t], oacc[db], 0, 0, 0);
       }
     }
 
-    // every wave is done with stage st_cur, and tile nn is visible in stage st_nn
-    __syncthreads();
+    // Tile n3: HBM -> LDS into the stage of tile cur-1 (read before the last barrier). Issued
+    // after this tile's V reads, so the next tile's V reads are the first LDS reads that have
+    // to wait for it; before the barrier only tile nn's loads (issued one step earlier) must
+    // have landed.
+    CP_TILE_DMA(n3, (st_cur + 3) & 3);
+    // This wave's LDS reads are done and tile nn has landed; then the workgroup barrier. (The
+    // barrier is issued as a bare instruction: the compiler's own barrier would also wait for
+    // tile n3's loads, which have two more tiles of time.)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntDmaLgkm0);
+    asm volatile("s_barrier" ::: "memory");
     cur = nxt;
     nxt = nn;
     nn = n3;
-    n3 = n4;
+    n3 = next_tile(n3);
     st_cur = st_nxt;
   };
-  // Two steps per trip with the score buffers and the staging registers swapping roles (no
-  // register copies). A workgroup without visible keys skips the loop (uniform branch).
+  // Two steps per trip with the score buffers swapping roles (no register copies). A workgroup
+  // without visible keys skips the loop (uniform branch).
   f32x16 sa[2], sb[2];
   int n_tiles = 0;  // tiles of this workgroup: ceil(visible / kBN) over its runs
   for (int j = 0; j < p.n_kv_segs; ++j) {
@@ -325,24 +347,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     if (ks.seq == qs.seq) n_tiles += (visible_prefix(ks, qpos_hi, p.causal) + C::kBN - 1) / C::kBN;
   }
   if (n_tiles > 0) {
-    CP_TILE_LOAD(cur, kst0, vst0);
-    CP_TILE_STORE(0, kst0, vst0);
-    CP_TILE_LOAD(nxt, kst1, vst1);
-    CP_TILE_STORE(1, kst1, vst1);
-    CP_TILE_LOAD(nn, kst0, vst0);
-    CP_TILE_LOAD(n3, kst1, vst1);
+    CP_TILE_DMA(cur, 0);
+    CP_TILE_DMA(nxt, 1);
+    CP_TILE_DMA(nn, 2);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     qk(0, sa);
-    // a counted loop without exits in its body keeps the two staging sets' loads in a fixed
-    // order, so each store waits only for its own set
     for (int it = 0; it + 1 < n_tiles; it += 2) {
-      step(sa, sb, kst0, vst0);
-      step(sb, sa, kst1, vst1);
+      step(sa, sb);
+      step(sb, sa);
     }
-    if (n_tiles & 1) step(sa, sb, kst0, vst0);
+    if (n_tiles & 1) step(sa, sb);
   }
-#undef CP_TILE_LOAD
-#undef CP_TILE_STORE
+#undef CP_TILE_DMA
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2, optional merge into the running result
   const float lt = l + __shfl_xor(l, 32);
