@@ -256,12 +256,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
 // whose partials are one contiguous [S][D] block. 256 / (D/4) groups of D/4 lanes take every
-// kGroups-th split with an online (running-max) combine, so all loads issue without waiting for
-// a global max; the groups are then combined through LDS in a fixed order.
+// kGroups-th split. A lane issues the loads of kBatch splits (their LSEs and 16-byte O slices)
+// before combining any of them, so each lane keeps that many loads in flight; batches are folded
+// into a running max, weight and sum. The groups are then combined through LDS in a fixed order.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
   constexpr int kLanes = D / 4;
   constexpr int kGroups = 256 / kLanes;
+  constexpr int kBatch = 16;
   __shared__ float red_m[kGroups];
   __shared__ float red_w[kGroups];
   __shared__ float4 red_o[kGroups][kLanes];
@@ -273,26 +275,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
 
   float M = -INFINITY, wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int c = grp; c < p.n_splits; c += kGroups) {
-    const float li = lse[c];
-    const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)c * D);
-    if (li == -INFINITY) continue;
-    if (li > M) {  // move the running max; earlier weights shrink by exp(M_old - M_new)
-      const float a = expf(M - li);  // M = -inf -> 0
-      wsum *= a;
-      acc.x *= a;
-      acc.y *= a;
-      acc.z *= a;
-      acc.w *= a;
-      M = li;
+  for (int c0 = grp; c0 < p.n_splits; c0 += kGroups * kBatch) {
+    float li[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = min(c0 + i * kGroups, p.n_splits - 1);  // clamped: in bounds, masked below
+      li[i] = c0 + i * kGroups < p.n_splits ? lse[c] : -INFINITY;
+      v[i] = *reinterpret_cast<const float4*>(o + (int64_t)c * D);
     }
-    const float w = expf(li - M);
-    wsum += w;
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) Mb = fmaxf(Mb, li[i]);
+    if (Mb == -INFINITY) continue;  // nothing seen yet
+    const float a = expf(M - Mb);    // M = -inf -> 0
+    wsum *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
+    M = Mb;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float w = expf(li[i] - M);  // -inf -> 0: the part saw no key
+      if (w == 0.f) continue;           // skip its O, which may be anything
+      wsum += w;
+      acc.x = fmaf(w, v[i].x, acc.x);
+      acc.y = fmaf(w, v[i].y, acc.y);
+      acc.z = fmaf(w, v[i].z, acc.z);
+      acc.w = fmaf(w, v[i].w, acc.w);
+    }
   }
   if (c4 == 0) red_m[grp] = M;
   __syncthreads();
