@@ -266,3 +266,9 @@ def test_decode_gqa_d64_bf16_out():
 
 def test_decode_more_than_16_heads_per_group():
     run_decode([700, 33], 40, 2, 128, 8, seed=2, check_splits=[3])
+
+
+def test_decode_batch_over_64():
+    # more requests than the kernel ranks by length: units are then taken in request order
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 300, size=70)]
+    run_decode(lens, 8, 1, 64, 4, seed=3, check_splits=[0, 3])
