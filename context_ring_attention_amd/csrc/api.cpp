@@ -58,15 +58,16 @@ int pack_segments(const cp_segment* segs, int n, int64_t rows, const char* what,
   return CP_OK;
 }
 
-// Orders the Q runs by the causal work of their heaviest (last) tile, heaviest first, and
-// numbers the workgroup tiles accordingly (see AttnParams).
+// Orders the Q runs (of all problems) by the causal work of their heaviest (last) tile,
+// heaviest first, and numbers the workgroup tiles accordingly (see AttnParams).
 void plan_tiles(cpk::AttnParams& p, int rows_per_tile) {
   std::vector<std::pair<int64_t, int>> work;
   for (int i = 0; i < p.n_q_segs; ++i) {
     const cpk::Seg& q = p.qs[i];
+    const int pr = p.q_prob[i];
     const int64_t last = (int64_t)q.pos + q.len - 1;
     int64_t w = 0;
-    for (int j = 0; j < p.n_kv_segs; ++j) {
+    for (int j = p.kv_lo[pr]; j < p.kv_hi[pr]; ++j) {
       const cpk::Seg& k = p.ks[j];
       if (k.seq != q.seq) continue;
       int64_t n = p.causal ? std::min<int64_t>(k.len, std::max<int64_t>(0, last - k.pos + 1)) : k.len;
@@ -96,6 +97,85 @@ int check_heads(int n_h, int n_kv, int d_h) {
 
 int launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(CP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// One partial attention: a Q shard (with its segment table) against a KV shard.
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t tq, tk;
+  const cp_segment* q_segs;
+  int n_q_segs;
+  const cp_segment* kv_segs;
+  int n_kv_segs;
+  float* o;
+  float* lse;
+};
+
+// Validates and launches independent partial attentions, as few launches as the pooled segment
+// tables allow (problems are packed in order; a problem always fits a launch on its own).
+int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int d_h,
+                          cp_dtype in_dtype, int causal, float softmax_scale, int accumulate,
+                          void* stream, const char* what) {
+  int st = check_heads(n_h, n_kv, d_h);
+  if (st) return st;
+  if (in_dtype != CP_F32 && in_dtype != CP_BF16) return fail(CP_E_ARG, "in_dtype=%d", (int)in_dtype);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CP_E_ARG, "softmax_scale must be finite and > 0");
+  if (accumulate != 0 && accumulate != 1) return fail(CP_E_ARG, "accumulate=%d", accumulate);
+  for (int i = 0; i < n_probs; ++i) {
+    const Problem& pr = probs[i];
+    if (pr.tq < 0 || pr.tk < 0) return fail(CP_E_ARG, "negative token count");
+    if (pr.tq > kI32Max || pr.tk > kI32Max) return fail(CP_E_UNSUPPORTED, "token counts beyond 2^31");
+    cpk::Seg scratch[cpk::kMaxSegs];
+    st = pack_segments(pr.q_segs, pr.n_q_segs, pr.tq, "q_segs", scratch);
+    if (st) return st;
+    st = pack_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs", scratch);
+    if (st) return st;
+    if (pr.n_q_segs > 0 && (!pr.q || !pr.o || !pr.lse)) return fail(CP_E_ARG, "q, o or lse is NULL");
+    if (pr.n_kv_segs > 0 && (!pr.k || !pr.v)) return fail(CP_E_ARG, "k or v is NULL");
+    if (!aligned16(pr.q) || !aligned16(pr.k) || !aligned16(pr.v) || !aligned16(pr.o))
+      return fail(CP_E_ARG, "q, k, v and o must be 16-byte aligned");
+  }
+  const bool bf16 = in_dtype == CP_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int next = 0;
+  while (next < n_probs) {
+    cpk::AttnParams p{};
+    p.n_h = n_h;
+    p.n_kv = n_kv;
+    p.group = n_h / n_kv;
+    p.causal = causal ? 1 : 0;
+    p.accumulate = accumulate;
+    p.scale = softmax_scale;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    int nq = 0, nk = 0, np = 0;
+    while (next < n_probs && np < cpk::kMaxProblems &&
+           nq + probs[next].n_q_segs <= cpk::kMaxSegs && nk + probs[next].n_kv_segs <= cpk::kMaxSegs) {
+      const Problem& pr = probs[next++];
+      pack_segments(pr.q_segs, pr.n_q_segs, pr.tq, "q_segs", p.qs + nq);
+      pack_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs", p.ks + nk);
+      for (int i = 0; i < pr.n_q_segs; ++i) p.q_prob[nq + i] = (int8_t)np;
+      p.kv_lo[np] = (int8_t)nk;
+      p.kv_hi[np] = (int8_t)(nk + pr.n_kv_segs);
+      p.q[np] = pr.q;
+      p.k[np] = pr.k;
+      p.v[np] = pr.v;
+      p.o[np] = pr.o;
+      p.lse[np] = pr.lse;
+      nq += pr.n_q_segs;
+      nk += pr.n_kv_segs;
+      ++np;
+    }
+    p.n_q_segs = nq;
+    plan_tiles(p, bf16 ? cpk::kTileRowsBf16 : cpk::kTileRowsF32);
+    if (p.total_tiles == 0) continue;
+    const hipError_t e = bf16 ? cpk::launch_attn_bf16(p, d_h, s) : cpk::launch_attn_f32(p, d_h, s);
+    st = launch_status(e, what);
+    if (st) return st;
+  }
   return ok();
 }
 
@@ -188,45 +268,9 @@ int cp_partial_attn(const void* q, const void* k, const void* v, int64_t tq, int
                     int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs, int n_q_segs,
                     const cp_segment* kv_segs, int n_kv_segs, int causal, float softmax_scale,
                     float* o, float* lse, int accumulate, void* stream) {
-  int st = check_heads(n_h, n_kv, d_h);
-  if (st) return st;
-  if (in_dtype != CP_F32 && in_dtype != CP_BF16) return fail(CP_E_ARG, "in_dtype=%d", (int)in_dtype);
-  if (tq < 0 || tk < 0) return fail(CP_E_ARG, "negative token count");
-  if (tq > kI32Max || tk > kI32Max) return fail(CP_E_UNSUPPORTED, "token counts beyond 2^31");
-  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-    return fail(CP_E_ARG, "softmax_scale must be finite and > 0");
-  if (accumulate != 0 && accumulate != 1) return fail(CP_E_ARG, "accumulate=%d", accumulate);
-
-  cpk::AttnParams p{};
-  st = pack_segments(q_segs, n_q_segs, tq, "q_segs", p.qs);
-  if (st) return st;
-  st = pack_segments(kv_segs, n_kv_segs, tk, "kv_segs", p.ks);
-  if (st) return st;
-  if (n_q_segs > 0 && (!q || !o || !lse)) return fail(CP_E_ARG, "q, o or lse is NULL");
-  if (n_kv_segs > 0 && (!k || !v)) return fail(CP_E_ARG, "k or v is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(CP_E_ARG, "q, k, v and o must be 16-byte aligned");
-
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.n_h = n_h;
-  p.n_kv = n_kv;
-  p.group = n_h / n_kv;
-  p.causal = causal ? 1 : 0;
-  p.accumulate = accumulate;
-  p.n_q_segs = n_q_segs;
-  p.n_kv_segs = n_kv_segs;
-  p.scale = softmax_scale;
-  p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const bool bf16 = in_dtype == CP_BF16;
-  plan_tiles(p, bf16 ? cpk::kTileRowsBf16 : cpk::kTileRowsF32);
-  if (p.total_tiles == 0) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = bf16 ? cpk::launch_attn_bf16(p, d_h, s) : cpk::launch_attn_f32(p, d_h, s);
-  return launch_status(e, "cp_partial_attn");
+  const Problem pr{q, k, v, tq, tk, q_segs, n_q_segs, kv_segs, n_kv_segs, o, lse};
+  return partial_attn_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale, accumulate,
+                               stream, "cp_partial_attn");
 }
 
 int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* lse_parts,
@@ -356,15 +400,20 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
       !n_kv_segs || !o_parts || !lse_parts || !o_out)
     return fail(CP_E_ARG, "NULL array argument");
   const int N = cp_world;
-  for (int t = 0; t < N; ++t)
+  // Step t: the rank holding KV shard s computes Q shard (s - t) mod N against it. The N partials
+  // of a step are independent and go to the GPU as one launch.
+  std::vector<Problem> step(N);
+  for (int t = 0; t < N; ++t) {
     for (int s = 0; s < N; ++s) {
       const int qi = ((s - t) % N + N) % N;
       const int slot = qi * N + s;
-      const int st = cp_partial_attn(q_shards[qi], k_shards[s], v_shards[s], tq[qi], tk[s], n_h, n_kv,
-                                     d_h, in_dtype, q_segs[qi], n_q_segs[qi], kv_segs[s], n_kv_segs[s],
-                                     causal, softmax_scale, o_parts[slot], lse_parts[slot], 0, stream);
-      if (st) return st;
+      step[s] = Problem{q_shards[qi], k_shards[s], v_shards[s], tq[qi], tk[s], q_segs[qi], n_q_segs[qi],
+                        kv_segs[s], n_kv_segs[s], o_parts[slot], lse_parts[slot]};
     }
+    const int st = partial_attn_problems(step.data(), N, n_h, n_kv, d_h, in_dtype, causal,
+                                         softmax_scale, 0, stream, "cp_ring_pass_q");
+    if (st) return st;
+  }
   for (int qi = 0; qi < N; ++qi) {
     const int st = cp_merge_lse(N, o_parts + (size_t)qi * N, lse_parts + (size_t)qi * N,
                                 tq[qi] * (int64_t)n_h, d_h, o_out[qi], out_dtype,

@@ -88,7 +88,7 @@ __device__ inline i16x4 lds_read_tr(const unsigned char* base, int byte_off) {
       (__attribute__((address_space(3))) i16x4*)(base + byte_off));
 }
 
-// Position of a K/V tile: run j of the KV shard (j == n_kv_segs means "no tile"), key offset kt
+// Position of a K/V tile: run j of the KV shard (j == the problem's kv_hi means "no tile"), key offset kt
 // inside the run, and the run's fields, carried along so that scalar loads of the run table
 // (whose waits would also drain every outstanding LDS read) only happen at run boundaries.
 struct TilePos {
@@ -113,6 +113,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   int seg, tile;
   locate_tile(p, blockIdx.x, seg, tile);
   const Seg qs = p.qs[seg];
+  const int pr = p.q_prob[seg];  // problem of this tile; its KV runs are [kv_lo, kv_hi)
+  const int kv_lo = p.kv_lo[pr], kv_hi = p.kv_hi[pr];
   const int rows = qs.len * p.group;
   const int tile_row0 = tile * C::kRows;
   const int tile_row_last = min(tile_row0 + C::kRows, rows) - 1;
@@ -120,9 +122,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   const int qpos_lo = qs.pos + tile_row0 / p.group;
   const int qpos_hi = qs.pos + tile_row_last / p.group;
 
-  const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q);
-  const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
-  const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
+  const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q[pr]);
+  const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k[pr]);
+  const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v[pr]);
 
   // ---- this lane's query row and its Q^T operand ------------------------------------------
   const int r = tile_row0 + wave * 32 + col;
@@ -143,16 +145,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
 
   // ---- KV tiles: runs of the same sequence, the prefix visible to the last query ----------
   auto first_run_from = [&](int j) -> TilePos {
-    for (; j < p.n_kv_segs; ++j) {
+    for (; j < kv_hi; ++j) {
       const Seg ks = p.ks[j];
       if (ks.seq != qs.seq) continue;
       const int vis = visible_prefix(ks, qpos_hi, p.causal);
       if (vis > 0) return TilePos{j, 0, vis, ks.loc, ks.pos, ks.len};
     }
-    return TilePos{p.n_kv_segs, 0, 0, 0, 0, 1};
+    return TilePos{kv_hi, 0, 0, 0, 0, 1};
   };
   auto next_tile = [&](TilePos t) -> TilePos {
-    if (t.j >= p.n_kv_segs) return t;
+    if (t.j >= kv_hi) return t;
     if (t.kt + C::kBN < t.vis) {
       t.kt += C::kBN;
       return t;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
                 8 * (j16 & 1);
 
   // ---- prologue: tiles 0 and 1 into stages 0 and 1, tiles 2 and 3 in flight, QK^T of tile 0
-  TilePos cur = first_run_from(0);
+  TilePos cur = first_run_from(kv_lo);
   TilePos nxt = next_tile(cur);
   TilePos nn = next_tile(nxt);
   TilePos n3 = next_tile(nn);
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   // without visible keys skips the loop (uniform branch).
   f32x16 sa[2], sb[2];
   int n_tiles = 0;  // tiles of this workgroup: ceil(visible / kBN) over its runs
-  for (int j = 0; j < p.n_kv_segs; ++j) {
+  for (int j = kv_lo; j < kv_hi; ++j) {
     const Seg ks = p.ks[j];
     if (ks.seq == qs.seq) n_tiles += (visible_prefix(ks, qpos_hi, p.causal) + C::kBN - 1) / C::kBN;
   }
@@ -367,10 +369,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse_new = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   float wp = 0.f, wn = 1.f, lse_out = lse_new;
-  float* orow = p.o + qrow * D;
+  float* orow = p.o[pr] + qrow * D;
   float4 prev[C::kDBlocks * 4];
   if (p.accumulate) {
-    running_merge_weights(p.lse[qrow], lse_new, wp, wn, lse_out);
+    running_merge_weights(p.lse[pr][qrow], lse_new, wp, wn, lse_out);
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
       o4.w = fmaf(wp, pv.w, oacc[db][4 * vq + 3] * sc);
       *reinterpret_cast<float4*>(orow + db * 32 + 8 * vq + 4 * half) = o4;
     }
-  if (half == 0) p.lse[qrow] = lse_out;
+  if (half == 0) p.lse[pr][qrow] = lse_out;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream) {

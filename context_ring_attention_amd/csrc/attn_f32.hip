@@ -20,6 +20,7 @@ __global__ __launch_bounds__(kTileRowsF32) void attn_f32_kernel(const AttnParams
   locate_tile(p, blockIdx.x, seg, tile);
   const int g = blockIdx.y;
   const Seg qs = p.qs[seg];
+  const int pr = p.q_prob[seg];  // problem of this tile
   const int rows = qs.len * p.group;
   const int r = tile * kTileRowsF32 + (int)threadIdx.x;
   if (r >= rows) return;
@@ -28,9 +29,9 @@ __global__ __launch_bounds__(kTileRowsF32) void attn_f32_kernel(const AttnParams
   const int head = g * p.group + r % p.group;
   const int64_t qrow = (int64_t)(qs.loc + tok) * p.n_h + head;
   const int qpos = qs.pos + tok;
-  const float* __restrict__ Q = static_cast<const float*>(p.q);
-  const float* __restrict__ K = static_cast<const float*>(p.k);
-  const float* __restrict__ V = static_cast<const float*>(p.v);
+  const float* __restrict__ Q = static_cast<const float*>(p.q[pr]);
+  const float* __restrict__ K = static_cast<const float*>(p.k[pr]);
+  const float* __restrict__ V = static_cast<const float*>(p.v[pr]);
 
   float qv[D];
 #pragma unroll
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(kTileRowsF32) void attn_f32_kernel(const AttnParams
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  for (int j = 0; j < p.n_kv_segs; ++j) {
+  for (int j = p.kv_lo[pr]; j < p.kv_hi[pr]; ++j) {
     const Seg ks = p.ks[j];
     if (ks.seq != qs.seq) continue;
     const int n = visible_prefix(ks, qpos, p.causal);
@@ -83,17 +84,17 @@ __global__ __launch_bounds__(kTileRowsF32) void attn_f32_kernel(const AttnParams
 
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse_new = l > 0.f ? m + logf(l) : -INFINITY;
-  float* orow = p.o + qrow * D;
+  float* orow = p.o[pr] + qrow * D;
   if (p.accumulate) {
     float wp, wn, lse_out;
-    running_merge_weights(p.lse[qrow], lse_new, wp, wn, lse_out);
+    running_merge_weights(p.lse[pr][qrow], lse_new, wp, wn, lse_out);
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = wp * orow[d] + wn * (acc[d] * inv);
-    p.lse[qrow] = lse_out;
+    p.lse[pr][qrow] = lse_out;
   } else {
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
-    p.lse[qrow] = lse_new;
+    p.lse[pr][qrow] = lse_new;
   }
 }
 

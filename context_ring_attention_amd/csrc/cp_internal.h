@@ -22,33 +22,38 @@ struct Seg {
 constexpr int kMaxSegs = CP_MAX_SEGMENTS;
 constexpr int kMaxParts = CP_MAX_MERGE_PARTS;
 
-// Arguments of one partial-attention launch. Rows of the Q shard are handled per KV head group
-// as a flat row space per Q segment: row r of segment i is token loc + r / group, query head
-// g*group + r % group (consecutive heads share KV head g, [CPEP §8.2]). Each workgroup takes one
-// tile of rows; tiles are numbered in processing order: slots 0..n_q_segs-1 visit the Q segments
-// in `order`, and inside a segment tiles go from the last (largest positions, most causal work)
-// to the first, so the heaviest tiles start first.
+// Arguments of one partial-attention launch, covering up to kMaxProblems independent problems
+// (a Q shard against a KV shard each, e.g. the ranks of one ring step) whose segment tables are
+// pooled. Rows of a Q shard are handled per KV head group as a flat row space per Q segment: row r
+// of segment i is token loc + r / group, query head g*group + r % group (consecutive heads share
+// KV head g, [CPEP §8.2]). Each workgroup takes one tile of rows; tiles are numbered in processing
+// order: slots 0..n_q_segs-1 visit the Q segments in `order`, and inside a segment tiles go from
+// the last (largest positions, most causal work) to the first, so the heaviest tiles start first.
+constexpr int kMaxProblems = 8;
 struct AttnParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  float* o;
-  float* lse;
+  const void* q[kMaxProblems];
+  const void* k[kMaxProblems];
+  const void* v[kMaxProblems];
+  float* o[kMaxProblems];
+  float* lse[kMaxProblems];
   int32_t n_h;
   int32_t n_kv;
   int32_t group;       // n_h / n_kv
   int32_t causal;
   int32_t accumulate;
-  int32_t n_q_segs;
-  int32_t n_kv_segs;
+  int32_t n_q_segs;    // Q segments of all problems
   int32_t total_tiles;
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)
   int32_t tile_prefix[kMaxSegs + 1];  // tiles before processing slot i
   int8_t order[kMaxSegs];             // Q segment of processing slot i
+  int8_t q_prob[kMaxSegs];            // problem of Q segment i
+  int8_t kv_lo[kMaxProblems];         // KV segments of problem i: [kv_lo[i], kv_hi[i])
+  int8_t kv_hi[kMaxProblems];
   Seg qs[kMaxSegs];
   Seg ks[kMaxSegs];
 };
+static_assert(sizeof(AttnParams) <= 4096, "kernel arguments are limited to 4 KB");
 
 struct MergeParams {
   const float* o_parts[kMaxParts];
