@@ -136,11 +136,15 @@ def test_bf16_seed1_second_draw():
 
 # --------------------------------------------------------------------------- Pass-Q
 def run_pass_q(P, T, N, n_h, n_kv, d, dtype="bf16", seed=0, n_sample=None, check_partials=True):
+    """Pass-Q over persistent KV: sequence i has P[i] cached and T[i] new tokens (scalars: one
+    sequence)."""
     from context_ring_attention_amd import binding as cp
     std = 1.0
     scale = scale_of(d)
-    q_ranges = [(0, P, P + T)]
-    kv_ranges = [(0, 0, P), (0, P, P + T)]
+    Ps = P if isinstance(P, (list, tuple)) else [P]
+    Ts = T if isinstance(T, (list, tuple)) else [T]
+    q_ranges = [(i, p, p + t) for i, (p, t) in enumerate(zip(Ps, Ts))]
+    kv_ranges = [r for i, (p, t) in enumerate(zip(Ps, Ts)) for r in ((i, 0, p), (i, p, p + t))]
     qsh = product_shards(q_ranges, N)
     ksh = product_shards(kv_ranges, N)
     for s in ksh.values():
@@ -176,6 +180,12 @@ def run_pass_q(P, T, N, n_h, n_kv, d, dtype="bf16", seed=0, n_sample=None, check
 
 def test_pass_q_persistent_kv_small():
     run_pass_q(P=3000, T=520, N=4, n_h=16, n_kv=1, d=128)
+
+
+def test_pass_q_varlen_cp8_split_launches():
+    # 8 ranks, 5 sequences: each KV shard has 20 runs, so a ring step's 8 partials need several
+    # launches (at most 64 pooled runs each)
+    run_pass_q(P=[300, 41, 700, 0, 129], T=[64, 200, 17, 90, 1], N=8, n_h=8, n_kv=2, d=64)
 
 
 # --------------------------------------------------------------------------- merge kernel
