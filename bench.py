@@ -155,6 +155,88 @@ def run_decode(torch, cp, si, seed=0):
             "cached_keys": total, "batch": B, "n_splits": S}
 
 
+def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
+    """One decode step of one request with a 128K-token cache (the per-token latency case),
+    launched eagerly and as a replayed HIP graph (captured through torch)."""
+    cfg = si.CONFIGS["decode_b32_32k_128k"]
+    n_h, n_kv, d, S = cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["n_splits"]
+    toks = np.arange(L)
+    kc = bf16_tokens(torch, si, seed, si.TID_K, toks, (n_kv, d))
+    vc = bf16_tokens(torch, si, seed, si.TID_V, toks, (n_kv, d))
+    q = bf16_tokens(torch, si, seed, si.TID_Q, np.arange(1), (n_h, d))
+    ws = torch.empty(cp.decode_workspace_bytes(1, n_h, d, S) // 4, device="cuda")
+    ws_o, ws_l = ws[: S * n_h * d], ws[S * n_h * d:]
+    o = torch.empty(1, n_h, d, device="cuda")
+    l = torch.empty(1, n_h, device="cuda")
+    offs = torch.zeros(1, dtype=torch.int64, device="cuda")
+    lens = torch.full((1,), L, dtype=torch.int64, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    fn = lambda: cp.decode_splitkv(q, kc, vc, offs, lens, S, scale, ws_o, ws_l, o, l)
+    eager_ms = time_reps(torch, fn, reps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    graph_ms = time_reps(torch, graph.replay, reps)
+
+    def synced(f):  # one step at a time, the host waiting for each (a token-by-token loop)
+        f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            f()
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    eager_sync_ms, graph_sync_ms = synced(fn), synced(graph.replay)
+    alg = L * n_kv * d * 2 * 2 + n_h * d * 2 + n_h * (d * 4 + 4)
+    log(f"decode step B=1 L={L}: back to back eager {eager_ms * 1e3:.1f} us, graph "
+        f"{graph_ms * 1e3:.1f} us; host-synced eager {eager_sync_ms * 1e3:.1f} us, graph "
+        f"{graph_sync_ms * 1e3:.1f} us")
+    return {"metric": "decode step latency", "unit": "us", "higher_is_better": False,
+            "back_to_back": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3, 2)},
+            "host_synced": {"eager_us": round(eager_sync_ms * 1e3, 2),
+                            "graph_us": round(graph_sync_ms * 1e3, 2)},
+            "eager_GBps": round(alg / (eager_ms * 1e-3) / 1e9, 1), "cached_keys": L, "n_splits": S}
+
+
+def device_rooflines(torch):
+    """Peaks derived from the device's reported attributes, next to the published figures, and
+    the achievable device-to-device copy bandwidth (1 GiB read + 1 GiB written)."""
+    import ctypes
+    info = {}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = torch.cuda.current_device()
+
+        def attr(code):  # hipDeviceAttribute values from hip_runtime_api.h
+            v = ctypes.c_int(0)
+            return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev) == 0 else None
+
+        cus, clk_khz, bus_bits, mclk_khz = attr(63), attr(5), attr(59), attr(60)
+        info.update({"cus": cus, "peak_clock_mhz": clk_khz and clk_khz / 1e3,
+                     "memory_clock_mhz": mclk_khz and mclk_khz / 1e3, "memory_bus_bits": bus_bits})
+        if cus and clk_khz:
+            info["bf16_peak_tflops_derived"] = round(cus * clk_khz * 1e3 * 4096 / 1e12, 1)
+        if bus_bits and mclk_khz:  # HBM3E moves 4 bits per pin per reported memory clock
+            info["hbm_peak_gbs_derived_4_per_clock"] = round(4 * mclk_khz * 1e3 * bus_bits / 8 / 1e9, 1)
+    except OSError:
+        pass
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_reps(torch, lambda: dst.copy_(src), 10)
+    info["copy_gbs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
+    info["published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    del src, dst
+    log(f"device: {info}")
+    return info
+
+
 def run_pass_q(torch, cp, si, seed=0):
     cfg = si.CONFIGS["persistent_kv_8k_on_120k"]
     P, T, N, n_h, n_kv, d = cfg["cached"], cfg["new"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
@@ -356,6 +438,7 @@ def main():
         secondary["merge_4parts_128k_cp4"] = run_merge(torch, cp, po, pl, d)
         del po, pl
         secondary["decode_b32_32k_128k"] = run_decode(torch, cp, si)
+        secondary["decode_step_b1_128k_graph"] = run_decode_step_graph(torch, cp, si)
         secondary["persistent_kv_8k_on_120k"] = run_pass_q(torch, cp, si)
         if args.extended:
             secondary["prefill_1m_varlen_cp8"] = run_prefill_1m(torch, cp, si)
@@ -366,6 +449,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log("calibration copy: 1 GiB read, 1 GiB written")
+
+    device_info = device_rooflines(torch) if not args.no_secondary else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +474,7 @@ def main():
                    "causal": True, "ring": "pass_kv", "merge_mode": args.mode,
                    "useful_tflop_per_step": round(flops_step / 1e12, 3)},
         "roofline": roofline,
+        "device": device_info,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
