@@ -5,8 +5,9 @@
 // LSE = -inf ([CPMTI §3 "核心公式": Pass-Q ends with an All2All merge of partial attention
 // results; §5 "关键实现细节" item 3; the ring variants are lossless and exact, §2).
 //
-// HBM-bound: D/4 lanes share a row and move 16 bytes each; parts whose LSE is -inf (they saw no
-// key of this row, which the load-balanced layout produces in every ring step) are not read.
+// HBM-bound: D/4 lanes share a row and move 16 bytes each; a lane issues the loads of eight
+// parts at once. Parts whose LSE is -inf (they saw no key of this row, which the load-balanced
+// layout produces in every ring step) are not read.
 //
 // Pages cited: [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (review).
 #include "device_common.h"
@@ -17,25 +18,45 @@ template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int kLanesPerRow = D / 4;
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  constexpr int kGroup = 8;  // parts whose loads are issued together
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const int c4 = threadIdx.x % kLanesPerRow;
   if (row >= p.rows) return;
+  const int n = p.n_parts;
 
+  // pass 1: M = max_i LSE_i
   float M = -INFINITY;
-  for (int i = 0; i < p.n_parts; ++i) M = fmaxf(M, p.lse_parts[i][row]);
+  for (int i0 = 0; i0 < n; i0 += kGroup) {
+    float li[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) li[k] = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) M = fmaxf(M, li[k]);
+  }
+  // pass 2: weights, then the O slices of a group's parts that saw a key, all loads in flight
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < p.n_parts; ++i) {
-      const float li = p.lse_parts[i][row];
-      if (li == -INFINITY) continue;
-      const float w = expf(li - M);
-      const float4 o = *reinterpret_cast<const float4*>(p.o_parts[i] + row * D + c4 * 4);
-      wsum += w;
-      acc.x = fmaf(w, o.x, acc.x);
-      acc.y = fmaf(w, o.y, acc.y);
-      acc.z = fmaf(w, o.z, acc.z);
-      acc.w = fmaf(w, o.w, acc.w);
+    for (int i0 = 0; i0 < n; i0 += kGroup) {
+      float w[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const float li = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
+        w[k] = li == -INFINITY ? 0.f : expf(li - M);
+      }
+      float4 o[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k)
+        o[k] = w[k] != 0.f ? *reinterpret_cast<const float4*>(p.o_parts[i0 + k] + row * D + c4 * 4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        wsum += w[k];
+        acc.x = fmaf(w[k], o[k].x, acc.x);
+        acc.y = fmaf(w[k], o[k].y, acc.y);
+        acc.z = fmaf(w[k], o[k].z, acc.z);
+        acc.w = fmaf(w[k], o[k].w, acc.w);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
