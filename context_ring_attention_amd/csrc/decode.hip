@@ -243,8 +243,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   lt += __shfl_xor(lt, 32);
   if (!head_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // workspace layout [batch][n_h][n_splits][D]: a head's partials are contiguous
-  const int64_t prow = ((int64_t)b * p.n_h + head) * p.n_splits + c;
+  // workspace layout [batch][n_splits][n_h][D]: a workgroup's heads are one contiguous block
+  const int64_t prow = ((int64_t)b * p.n_splits + c) * p.n_h + head;
   float* wo = p.ws_o + prow * D;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) {
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 }
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
-// whose partials are one contiguous [S][D] block. 256 / (D/4) groups of D/4 lanes take every
+// whose partials are S rows of D floats, n_h rows apart. 256 / (D/4) groups of D/4 lanes take every
 // kGroups-th split. A lane issues the loads of kBatch splits (their LSEs and 16-byte O slices)
 // before combining any of them, so each lane keeps that many loads in flight; batches are folded
 // into a running max, weight and sum. The groups are then combined through LDS in a fixed order.
@@ -270,8 +270,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const int r = blockIdx.x;  // b * n_h + head
   const int grp = threadIdx.x / kLanes;
   const int c4 = threadIdx.x % kLanes;
-  const float* lse = p.ws_lse + (int64_t)r * p.n_splits;
-  const float* o = p.ws_o + (int64_t)r * p.n_splits * D + c4 * 4;
+  const int64_t row0 = (int64_t)(r / p.n_h) * p.n_splits * p.n_h + r % p.n_h;  // split 0's row
+  const float* lse = p.ws_lse + row0;
+  const float* o = p.ws_o + row0 * D + c4 * 4;
+  const int64_t stride = p.n_h;  // rows between consecutive splits
 
   float M = -INFINITY, wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -281,8 +283,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = min(c0 + i * kGroups, p.n_splits - 1);  // clamped: in bounds, masked below
-      li[i] = c0 + i * kGroups < p.n_splits ? lse[c] : -INFINITY;
-      v[i] = *reinterpret_cast<const float4*>(o + (int64_t)c * D);
+      li[i] = c0 + i * kGroups < p.n_splits ? lse[c * stride] : -INFINITY;
+      v[i] = *reinterpret_cast<const float4*>(o + c * stride * D);
     }
     float Mb = M;
 #pragma unroll

@@ -124,9 +124,9 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
  *     [kv_offset[b], kv_offset[b] + kv_len[b]); kv_offset, kv_len: device int64 [batch].
  *   Split c of request b covers cache rows [floor(c*L_b/S), floor((c+1)*L_b/S)); every cached key
  *   is visible (the query comes after the cache).
- *   ws_o: device fp32 [batch, n_h, n_splits, d_h], ws_lse: device fp32 [batch, n_h, n_splits]:
+ *   ws_o: device fp32 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
  *     the per-split partials (caller-owned workspace of cp_decode_workspace_bytes bytes, laid out
- *     ws_o first, then ws_lse at byte offset batch*n_h*n_splits*d_h*4).
+ *     ws_o first, then ws_lse at byte offset batch*n_splits*n_h*d_h*4).
  *   o_out: device [batch, n_h, d_h] in out_dtype; lse_out: device fp32 [batch, n_h] (may be NULL).
  * in_dtype must be CP_BF16. 1 <= n_splits <= 1024.
  * ------------------------------------------------------------------------------------------- */

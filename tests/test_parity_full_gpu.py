@@ -70,8 +70,8 @@ def test_full_decode_b32_256_splits():
                       scale, ws_o, ws_l, o, l)
     torch.cuda.synchronize()
     qf = oracle_view(0, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws_o = ws_o.view(B, n_h, S, d)
-    ws_l = ws_l.view(B, n_h, S)
+    ws_o = ws_o.view(B, S, n_h, d)
+    ws_l = ws_l.view(B, S, n_h)
     rng = np.random.default_rng(0)
     for b in range(B):
         lo, L = int(offs[b]), int(lens[b])
@@ -89,4 +89,4 @@ def test_full_decode_b32_256_splits():
                 a, e = bounds[c]
                 o_p, l_p = oracle.attention(qf[b:b + 1], kf[a:e], vf[a:e], n_h, n_kv, zs, qp,
                                             kseq[a:e], kpos[a:e], False, scale)
-                assert_close(ws_o[b, :, c], ws_l[b, :, c], o_p, l_p, "bf16", f"request {b} split {c}")
+                assert_close(ws_o[b, c], ws_l[b, c], o_p, l_p, "bf16", f"request {b} split {c}")

@@ -246,8 +246,8 @@ def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=
                       n_splits, scale, ws_o, ws_l, o_out, l_out)
     torch.cuda.synchronize()
     qf = oracle_view(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws_o = ws_o.view(B, n_h, n_splits, d)
-    ws_l = ws_l.view(B, n_h, n_splits)
+    ws_o = ws_o.view(B, n_splits, n_h, d)
+    ws_l = ws_l.view(B, n_splits, n_h)
     for b in range(B):
         lo, L = int(offs[b]), int(lengths[b])
         kf = oracle_view(seed, si.TID_K, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
@@ -263,7 +263,7 @@ def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=
             a, e = splits[c]
             o_p, l_p = oracle.attention(qf[b:b + 1], kf[a:e], vf[a:e], n_h, n_kv, qs_, qp_,
                                         np.zeros(e - a, np.int32), np.arange(a, e), False, scale)
-            assert_close(ws_o[b, :, c], ws_l[b, :, c], o_p, l_p, dt, f"request {b} split {c}")
+            assert_close(ws_o[b, c], ws_l[b, c], o_p, l_p, dt, f"request {b} split {c}")
 
 
 def test_decode_small_ragged():
