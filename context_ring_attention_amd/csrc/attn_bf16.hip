@@ -19,8 +19,11 @@
 //    B operand; V^T comes straight from the row-major V tile with ds_read_b64_tr_b16, whose
 //    16-lane transpose turns four key rows into per-lane key vectors.
 //  - Software pipeline: while the VALUs run the softmax of tile n, the MFMA pipe already works
-//    on QK^T of tile n+1; K/V tiles live in three LDS stages (tile n being consumed, tile n+1
-//    ready for QK^T, tile n+2 arriving from registers loaded during the previous tile).
+//    on QK^T of tile n+1. K/V tiles move HBM -> LDS with direct-to-LDS loads (no VGPR staging)
+//    into four stages of unpadded, XOR-swizzled rows; tile n+3's loads are issued right after
+//    tile n's V reads, and the per-tile barrier waits only for tile n+2.
+//  - One launch may carry several independent problems (e.g. the ranks of one ring step), each
+//    with its own pointers and a range of the pooled segment tables.
 //  - Online softmax in base 2 with scale*log2(e) folded into one FMA; the running max only moves
 //    when a tile raises it by more than 2^8, so the O^T accumulators are rarely rescaled; fp32
 //    accumulators, LSE returned in natural log.
