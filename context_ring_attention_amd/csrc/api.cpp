@@ -114,11 +114,9 @@ struct Problem {
   float* lse;
 };
 
-// Validates and launches independent partial attentions, as few launches as the pooled segment
-// tables allow (problems are packed in order; a problem always fits a launch on its own).
-int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int d_h,
-                          cp_dtype in_dtype, int causal, float softmax_scale, int accumulate,
-                          void* stream, const char* what) {
+// Argument checks of a set of partial attentions (nothing is launched).
+int validate_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int d_h,
+                      cp_dtype in_dtype, float softmax_scale, int accumulate) {
   int st = check_heads(n_h, n_kv, d_h);
   if (st) return st;
   if (in_dtype != CP_F32 && in_dtype != CP_BF16) return fail(CP_E_ARG, "in_dtype=%d", (int)in_dtype);
@@ -139,6 +137,37 @@ int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, 
     if (!aligned16(pr.q) || !aligned16(pr.k) || !aligned16(pr.v) || !aligned16(pr.o))
       return fail(CP_E_ARG, "q, k, v and o must be 16-byte aligned");
   }
+  return CP_OK;
+}
+
+// Argument checks of cp_merge_lse (nothing is launched).
+int validate_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                   int64_t rows, int d_h, const void* o_out, cp_dtype out_dtype) {
+  if (n_parts < 1 || n_parts > cpk::kMaxParts)
+    return fail(CP_E_CAPACITY, "n_parts=%d (1..%d supported)", n_parts, cpk::kMaxParts);
+  if (!o_parts || !lse_parts) return fail(CP_E_ARG, "part arrays are NULL");
+  if (rows < 0) return fail(CP_E_ARG, "rows=%lld", (long long)rows);
+  if (d_h != 64 && d_h != 128) return fail(CP_E_UNSUPPORTED, "d_h=%d (64 or 128 supported)", d_h);
+  if (out_dtype != CP_F32 && out_dtype != CP_BF16) return fail(CP_E_ARG, "out_dtype=%d", (int)out_dtype);
+  if (rows > ((int64_t)1 << 40)) return fail(CP_E_UNSUPPORTED, "rows=%lld", (long long)rows);
+  for (int i = 0; i < n_parts; ++i) {
+    if (!o_parts[i] || !lse_parts[i]) return fail(CP_E_ARG, "part %d is NULL", i);
+    if (!aligned16(o_parts[i])) return fail(CP_E_ARG, "o_parts[%d] must be 16-byte aligned", i);
+  }
+  if (!o_out || !aligned16(o_out)) return fail(CP_E_ARG, "o_out is NULL or not 16-byte aligned");
+  if (out_dtype == CP_BF16)
+    for (int i = 0; i < n_parts; ++i)
+      if ((const void*)o_parts[i] == o_out) return fail(CP_E_ARG, "bf16 output cannot alias a part");
+  return CP_OK;
+}
+
+// Validates, then launches independent partial attentions, as few launches as the pooled segment
+// tables allow (problems are packed in order; a problem always fits a launch on its own).
+int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int d_h,
+                          cp_dtype in_dtype, int causal, float softmax_scale, int accumulate,
+                          void* stream, const char* what) {
+  int st = validate_problems(probs, n_probs, n_h, n_kv, d_h, in_dtype, softmax_scale, accumulate);
+  if (st) return st;
   const bool bf16 = in_dtype == CP_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int next = 0;
@@ -276,24 +305,13 @@ int cp_partial_attn(const void* q, const void* k, const void* v, int64_t tq, int
 int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                  int64_t rows, int d_h, void* o_out, cp_dtype out_dtype, float* lse_out,
                  void* stream) {
-  if (n_parts < 1 || n_parts > cpk::kMaxParts)
-    return fail(CP_E_CAPACITY, "n_parts=%d (1..%d supported)", n_parts, cpk::kMaxParts);
-  if (!o_parts || !lse_parts) return fail(CP_E_ARG, "part arrays are NULL");
-  if (rows < 0) return fail(CP_E_ARG, "rows=%lld", (long long)rows);
-  if (d_h != 64 && d_h != 128) return fail(CP_E_UNSUPPORTED, "d_h=%d (64 or 128 supported)", d_h);
-  if (out_dtype != CP_F32 && out_dtype != CP_BF16) return fail(CP_E_ARG, "out_dtype=%d", (int)out_dtype);
-  if (rows > ((int64_t)1 << 40)) return fail(CP_E_UNSUPPORTED, "rows=%lld", (long long)rows);
+  const int st = validate_merge(n_parts, o_parts, lse_parts, rows, d_h, o_out, out_dtype);
+  if (st) return st;
   cpk::MergeParams p{};
   for (int i = 0; i < n_parts; ++i) {
-    if (!o_parts[i] || !lse_parts[i]) return fail(CP_E_ARG, "part %d is NULL", i);
-    if (!aligned16(o_parts[i])) return fail(CP_E_ARG, "o_parts[%d] must be 16-byte aligned", i);
     p.o_parts[i] = o_parts[i];
     p.lse_parts[i] = lse_parts[i];
   }
-  if (!o_out || !aligned16(o_out)) return fail(CP_E_ARG, "o_out is NULL or not 16-byte aligned");
-  if (out_dtype == CP_BF16)
-    for (int i = 0; i < n_parts; ++i)
-      if ((const void*)o_parts[i] == o_out) return fail(CP_E_ARG, "bf16 output cannot alias a part");
   p.o_out = o_out;
   p.lse_out = lse_out;
   p.rows = rows;
@@ -367,22 +385,35 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
   if (partials && !lse_parts) return fail(CP_E_ARG, "lse_parts is NULL");
   if (!partials && (!o_acc || !lse_acc)) return fail(CP_E_ARG, "running mode needs o_acc and lse_acc");
   if (!o_out) return fail(CP_E_ARG, "o_out is NULL");
+  // Step t holds KV shard (rank - t) mod N. Every step and the final merge are validated before
+  // the first launch, so a failing call launches nothing.
+  std::vector<Problem> steps(cp_world);
   for (int t = 0; t < cp_world; ++t) {
     const int s = ((rank - t) % cp_world + cp_world) % cp_world;
-    float* o = partials ? o_parts[t] : o_acc;
-    float* l = partials ? lse_parts[t] : lse_acc;
-    const int acc = (!partials && t > 0) ? 1 : 0;
-    const int st = cp_partial_attn(q, k_shards[s], v_shards[s], tq, tk[s], n_h, n_kv, d_h, in_dtype,
-                                   q_segs, n_q_segs, kv_segs[s], n_kv_segs[s], causal, softmax_scale,
-                                   o, l, acc, stream);
-    if (st) return st;
+    steps[t] = Problem{q, k_shards[s], v_shards[s], tq, tk[s], q_segs, n_q_segs, kv_segs[s],
+                       n_kv_segs[s], partials ? o_parts[t] : o_acc, partials ? lse_parts[t] : lse_acc};
   }
+  int st = validate_problems(steps.data(), cp_world, n_h, n_kv, d_h, in_dtype, softmax_scale, 0);
+  if (st) return st;
   const int64_t rows = tq * (int64_t)n_h;
-  if (partials)
-    return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
-  if (o_out == o_acc && out_dtype == CP_F32 && (lse_out == nullptr || lse_out == lse_acc)) return ok();
+  const bool fold_only = !partials && o_out == o_acc && out_dtype == CP_F32 &&
+                         (lse_out == nullptr || lse_out == lse_acc);
   const float* op[1] = {o_acc};
   const float* lp[1] = {lse_acc};
+  if (partials)
+    st = validate_merge(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype);
+  else if (!fold_only)
+    st = validate_merge(1, op, lp, rows, d_h, o_out, out_dtype);
+  if (st) return st;
+  for (int t = 0; t < cp_world; ++t) {
+    const int acc = (!partials && t > 0) ? 1 : 0;
+    st = partial_attn_problems(&steps[t], 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale, acc,
+                               stream, "cp_ring_pass_kv");
+    if (st) return st;
+  }
+  if (partials)
+    return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
+  if (fold_only) return ok();
   return cp_merge_lse(1, op, lp, rows, d_h, o_out, out_dtype, lse_out, stream);
 }
 
@@ -401,17 +432,27 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
     return fail(CP_E_ARG, "NULL array argument");
   const int N = cp_world;
   // Step t: the rank holding KV shard s computes Q shard (s - t) mod N against it. The N partials
-  // of a step are independent and go to the GPU as one launch.
-  std::vector<Problem> step(N);
-  for (int t = 0; t < N; ++t) {
+  // of a step are independent and go to the GPU as one launch. All N*N partials and the N merges
+  // are validated before the first launch.
+  std::vector<Problem> all((size_t)N * N);
+  for (int t = 0; t < N; ++t)
     for (int s = 0; s < N; ++s) {
       const int qi = ((s - t) % N + N) % N;
       const int slot = qi * N + s;
-      step[s] = Problem{q_shards[qi], k_shards[s], v_shards[s], tq[qi], tk[s], q_segs[qi], n_q_segs[qi],
-                        kv_segs[s], n_kv_segs[s], o_parts[slot], lse_parts[slot]};
+      all[(size_t)t * N + s] = Problem{q_shards[qi], k_shards[s], v_shards[s], tq[qi], tk[s],
+                                       q_segs[qi], n_q_segs[qi], kv_segs[s], n_kv_segs[s],
+                                       o_parts[slot], lse_parts[slot]};
     }
-    const int st = partial_attn_problems(step.data(), N, n_h, n_kv, d_h, in_dtype, causal,
-                                         softmax_scale, 0, stream, "cp_ring_pass_q");
+  int vst = validate_problems(all.data(), N * N, n_h, n_kv, d_h, in_dtype, softmax_scale, 0);
+  if (vst) return vst;
+  for (int qi = 0; qi < N; ++qi) {
+    vst = validate_merge(N, o_parts + (size_t)qi * N, lse_parts + (size_t)qi * N, tq[qi] * (int64_t)n_h,
+                         d_h, o_out[qi], out_dtype);
+    if (vst) return vst;
+  }
+  for (int t = 0; t < N; ++t) {
+    const int st = partial_attn_problems(all.data() + (size_t)t * N, N, n_h, n_kv, d_h, in_dtype,
+                                         causal, softmax_scale, 0, stream, "cp_ring_pass_q");
     if (st) return st;
   }
   for (int qi = 0; qi < N; ++qi) {

@@ -168,6 +168,10 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
  *   o_parts, lse_parts: host arrays [cp_world*cp_world] of device fp32 buffers, slot q*N + s
  *     sized for Q shard q.
  *   o_out, lse_out: host arrays [cp_world] of device outputs (lse_out may be NULL, or hold NULLs).
+ * The cp_world partials of one step are independent (one per rank) and are computed by a single
+ * launch when their segment tables fit it together (at most 8 problems and 64 Q runs and 64 KV
+ * runs in total), otherwise by as few launches as they fit. Every partial is validated as by
+ * cp_partial_attn before anything of its step is launched.
  * ------------------------------------------------------------------------------------------- */
 int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
                    const cp_segment* const* q_segs, const int* n_q_segs,

@@ -141,3 +141,66 @@ def test_merge_and_decode_reject_bad_arguments():
                None) == cp.CP_E_ARG
     assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 + 1) * 4
     assert lib.cp_status_string(cp.CP_E_HIP) == b"CP_E_HIP"
+
+
+def _ring_arrays(N, tq=16, tk=16, bad_kv=None, bad_o_out=False):
+    """ctypes arrays for the ring drivers with fake (never dereferenced) 16-byte aligned device
+    pointers; shard `bad_kv` gets a run that overflows its shard."""
+    vp = ctypes.c_void_p
+    segp = ctypes.POINTER(cp.CpSegment)
+    good, _ = cp.segments([(0, 0, tq, 0)])
+    kv_ok, _ = cp.segments([(0, 0, tk, 0)])
+    kv_bad, _ = cp.segments([(0, 0, tk + 1, 0)])
+    ptr = lambda i: 0x100000 + 0x1000 * i
+    a = {
+        "q": (vp * N)(*[ptr(i) for i in range(N)]),
+        "tq": (ctypes.c_int64 * N)(*[tq] * N),
+        "q_segs": (segp * N)(*[ctypes.cast(good, segp)] * N),
+        "nq": (ctypes.c_int * N)(*[1] * N),
+        "k": (vp * N)(*[ptr(100 + i) for i in range(N)]),
+        "v": (vp * N)(*[ptr(200 + i) for i in range(N)]),
+        "tk": (ctypes.c_int64 * N)(*[tk] * N),
+        "kv_segs": (segp * N)(*[ctypes.cast(kv_bad if i == bad_kv else kv_ok, segp) for i in range(N)]),
+        "nk": (ctypes.c_int * N)(*[1] * N),
+        "o_parts": (vp * (N * N))(*[ptr(300 + i) for i in range(N * N)]),
+        "l_parts": (vp * (N * N))(*[ptr(400 + i) for i in range(N * N)]),
+        "o_out": (vp * N)(*[None if (bad_o_out and i == N - 1) else ptr(500 + i) for i in range(N)]),
+    }
+    return a
+
+
+def test_ring_drivers_validate_every_step_and_merge_before_launching():
+    """A bad shard reached only at a late ring step, or a bad final-merge output, must fail the
+    call before anything is launched (the pointers here are fake; a launch would fault)."""
+    lib = cp.load()
+    N = 4
+    # Pass-KV, rank 0: shard 3 is visited at step 1, shard 1 at the last step
+    for bad in (1, 3):
+        a = _ring_arrays(N, bad_kv=bad)
+        st = lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"], a["kv_segs"],
+                                 a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, None, None, 0x7000000,
+                                 0x7100000, 0x7200000, cp.CP_BF16, None, None)
+        assert st == cp.CP_E_SHAPE and "kv_segs" in cp.last_error()
+    # Pass-KV partials mode with a NULL part: caught by the merge check, before any launch
+    a = _ring_arrays(N)
+    parts = a["o_parts"]
+    parts[2] = None
+    st = lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"], a["kv_segs"],
+                             a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, parts, a["l_parts"], None, None,
+                             0x7200000, cp.CP_F32, None, None)
+    assert st == cp.CP_E_ARG
+    # Pass-Q: a bad KV shard, and a NULL output of the last Q shard's merge
+    for kw, code in (({"bad_kv": 2}, cp.CP_E_SHAPE), ({"bad_o_out": True}, cp.CP_E_ARG)):
+        a = _ring_arrays(N, **kw)
+        st = lib.cp_ring_pass_q(N, a["q"], a["tq"], a["q_segs"], a["nq"], a["k"], a["v"], a["tk"],
+                                a["kv_segs"], a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, a["o_parts"],
+                                a["l_parts"], a["o_out"], cp.CP_F32, None, None)
+        assert st == code, cp.last_error()
+    # argument errors of the drivers themselves
+    a = _ring_arrays(N)
+    assert lib.cp_ring_pass_q(0, a["q"], a["tq"], a["q_segs"], a["nq"], a["k"], a["v"], a["tk"],
+                              a["kv_segs"], a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, a["o_parts"],
+                              a["l_parts"], a["o_out"], cp.CP_F32, None, None) == cp.CP_E_ARG
+    assert lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, N, a["k"], a["v"], a["tk"], a["kv_segs"],
+                               a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, a["o_parts"], a["l_parts"], None,
+                               None, 0x7200000, cp.CP_F32, None, None) == cp.CP_E_ARG
