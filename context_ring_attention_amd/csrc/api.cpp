@@ -123,6 +123,7 @@ int validate_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int 
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(CP_E_ARG, "softmax_scale must be finite and > 0");
   if (accumulate != 0 && accumulate != 1) return fail(CP_E_ARG, "accumulate=%d", accumulate);
+  const int64_t group = n_h / n_kv;
   for (int i = 0; i < n_probs; ++i) {
     const Problem& pr = probs[i];
     if (pr.tq < 0 || pr.tk < 0) return fail(CP_E_ARG, "negative token count");
@@ -132,6 +133,11 @@ int validate_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int 
     if (st) return st;
     st = pack_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs", scratch);
     if (st) return st;
+    // the kernels index a Q run's (token, head-in-group) rows in 32 bits
+    for (int j = 0; j < pr.n_q_segs; ++j)
+      if (pr.q_segs[j].len > 0 && pr.q_segs[j].len * group > kI32Max)
+        return fail(CP_E_UNSUPPORTED, "q_segs[%d]: %lld tokens x %lld heads per KV head exceed 2^31 rows",
+                    j, (long long)pr.q_segs[j].len, (long long)group);
     if (pr.n_q_segs > 0 && (!pr.q || !pr.o || !pr.lse)) return fail(CP_E_ARG, "q, o or lse is NULL");
     if (pr.n_kv_segs > 0 && (!pr.k || !pr.v)) return fail(CP_E_ARG, "k or v is NULL");
     if (!aligned16(pr.q) || !aligned16(pr.k) || !aligned16(pr.v) || !aligned16(pr.o))

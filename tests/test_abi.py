@@ -117,6 +117,8 @@ def test_partial_attn_rejects_bad_arguments_without_launching():
     neg, n = cp.segments([(-1, 0, 1, 0)])
     assert _partial(ks=neg, nk=n) == cp.CP_E_SHAPE
     assert _partial(tq=1 << 31) == cp.CP_E_UNSUPPORTED
+    huge, n = cp.segments([(0, 0, 1 << 27, 0)])       # 2^27 tokens x 16 heads per KV head
+    assert _partial(qs=huge, nq=n, tq=1 << 27, n_h=16, n_kv=1) == cp.CP_E_UNSUPPORTED
     # nothing to do is not an error (no launch either)
     assert _partial(nq=0) == cp.CP_OK
 
