@@ -19,9 +19,12 @@
 //    B operand; V^T comes straight from the row-major V tile with ds_read_b64_tr_b16, whose
 //    16-lane transpose turns four key rows into per-lane key vectors.
 //  - Software pipeline: while the VALUs run the softmax of tile n, the MFMA pipe already works
-//    on QK^T of tile n+1. K/V tiles move HBM -> LDS with direct-to-LDS loads (no VGPR staging)
-//    into four stages of unpadded, XOR-swizzled rows; tile n+3's loads are issued right after
-//    tile n's V reads, and the per-tile barrier waits only for tile n+2.
+//    on QK^T of tile n+1. K/V tiles move HBM -> LDS with direct-to-LDS buffer loads (no VGPR
+//    staging, no per-lane address math: one descriptor per tile bounds the run, rows past its
+//    end arrive as zeros) into four stages of unpadded, XOR-swizzled rows; tile n+3's loads are
+//    issued right after tile n's V reads, and the per-tile barrier waits only for tile n+2.
+//  - The tile loop is unrolled over the four stages, so every LDS operand address is a per-lane
+//    base plus an immediate offset (K tiles of all stages below 64 KB, V tiles above).
 //  - One launch may carry several independent problems (e.g. the ranks of one ring step), each
 //    with its own pointers and a range of the pooled segment tables.
 //  - Online softmax in base 2 with scale*log2(e) folded into one FMA; the running max only moves
@@ -53,8 +56,12 @@ struct Bf16Cfg {
   static constexpr int kRowBytes = D * 2;       // LDS rows are unpadded (see the swizzles)
   static constexpr int kChunks = D / 8;         // 16-byte chunks per key row
   static constexpr int kTileBytes = kBN * kRowBytes;  // one K or one V tile
-  static constexpr int kStageBytes = 2 * kTileBytes;
   static constexpr int kStages = 4;
+  // LDS holds the K tiles of all stages, then the V tiles of all stages: every operand read is a
+  // per-lane base plus an immediate offset below 64 KB.
+  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;
+  static constexpr int k_at(int st) { return st * kTileBytes; }
+  static constexpr int v_at(int st) { return (kStages + st) * kTileBytes; }
   // A direct-to-LDS load writes 64 lanes x 16 bytes = 1 KB contiguously: a block of rows.
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;
   static constexpr int kBlocksPerWave = kTileBytes / 1024 / kWaves;
@@ -82,6 +89,32 @@ constexpr float kRescaleThreshold = 8.0f;
 // s_waitcnt immediate for "vmcnt(0)" on gfx9-family targets (expcnt and lgkmcnt left at max).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Word 3 of a raw buffer descriptor on gfx9-family targets (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
+// Hides x's value from the optimiser (no instruction). Device pass only: the constraint is an
+// AMDGPU one, and a host pass that rejected it would drop the kernel's launch stub.
+__device__ inline void opaque(uint32_t& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+
+// One direct-to-LDS load of 16 bytes per lane through buffer descriptor r: lane l's bytes go to
+// lds + 16 l; a lane whose offset lies outside the descriptor's range writes zeros. (The body is
+// device-pass only: a host pass that saw the builtin would drop the kernel's launch stub.)
+__device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)voff, 0, 0, 0);
+#endif
+}
+
+template <int N>
+struct StageIdx {
+  static constexpr int value = N;
+};
+
 __device__ inline bf16x8 lds_read_b128(const unsigned char* base, int byte_off) {
   return *reinterpret_cast<const bf16x8*>(base + byte_off);
 }
@@ -104,7 +137,7 @@ struct TilePos {
 template <int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStages * C::kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,30 +206,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + (int64_t)g * D);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + (int64_t)g * D);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t dma_row_off[C::kBlocksPerWave], dma_k_chunk[C::kBlocksPerWave],
-      dma_v_chunk[C::kBlocksPerWave];
+  uint32_t dma_k_off[C::kBlocksPerWave], dma_v_off[C::kBlocksPerWave];
 #pragma unroll
   for (int i = 0; i < C::kBlocksPerWave; ++i) {
     const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
     const int slot = lane % C::kChunks;
-    dma_row_off[i] = row * row_bytes;
-    dma_k_chunk[i] = (slot ^ C::swz_k(row)) * 16;
-    dma_v_chunk[i] = (slot ^ C::swz_v(row)) * 16;
+    dma_k_off[i] = row * row_bytes + (slot ^ C::swz_k(row)) * 16;
+    dma_v_off[i] = row * row_bytes + (slot ^ C::swz_v(row)) * 16;
   }
+  // One buffer descriptor per tile and operand covers the tile's rows inside the run; rows past
+  // the run's end fall outside it and arrive in LDS as zeros (no clamp, no per-lane address math).
 #define CP_TILE_DMA(T, STAGE)                                                                 \
   {                                                                                           \
     const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                            \
-    const uint32_t last_off = (uint32_t)min((T).len - 1 - (T).kt, C::kBN - 1) * row_bytes;     \
-    unsigned char* kt_s = smem + (STAGE) * C::kStageBytes;                                    \
+    const int nrec = min((T).len - (T).kt, C::kBN) * (int)row_bytes;                          \
+    const __amdgpu_buffer_rsrc_t kr =                                                         \
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + first), 0, nrec, kBufferWord3);        \
+    const __amdgpu_buffer_rsrc_t vr =                                                         \
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + first), 0, nrec, kBufferWord3);        \
+    unsigned char* kt_s = smem + C::k_at(STAGE);                                              \
+    unsigned char* vt_s = smem + C::v_at(STAGE);                                              \
     _Pragma("unroll") for (int i = 0; i < C::kBlocksPerWave; ++i) {                           \
-      const uint32_t o = min(dma_row_off[i], last_off);                                       \
       const int blk = (wave_u * C::kBlocksPerWave + i) * 1024;                                \
-      __builtin_amdgcn_global_load_lds(                                                       \
-          (__attribute__((address_space(1))) void*)(Kb + first + o + dma_k_chunk[i]),         \
-          (__attribute__((address_space(3))) void*)(kt_s + blk), 16, 0, 0);                   \
-      __builtin_amdgcn_global_load_lds(                                                       \
-          (__attribute__((address_space(1))) void*)(Vb + first + o + dma_v_chunk[i]),         \
-          (__attribute__((address_space(3))) void*)(kt_s + C::kTileBytes + blk), 16, 0, 0);   \
+      buffer_to_lds16(kr, kt_s + blk, dma_k_off[i]);                                          \
+      buffer_to_lds16(vr, vt_s + blk, dma_v_off[i]);                                          \
     }                                                                                         \
   }
 
@@ -210,8 +243,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
 #pragma unroll
   for (int k = 0; k < C::kKSteps; ++k)
     k_off[k] = col * C::kRowBytes + 16 * ((half * (D / 16) + k) ^ C::swz_k(col));
+  // (hide the bases' known bits: stage offsets are then added and folded into the instruction's
+  // offset field instead of being OR-ed in by VALU ops)
+#pragma unroll
+  for (int k = 0; k < C::kKSteps; ++k) opaque(k_off[k]);
   auto qk = [&](int st, f32x16 (&s)[2]) {
-    const unsigned char* Kt = smem + st * C::kStageBytes;
+    const unsigned char* Kt = smem + C::k_at(st);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -244,7 +281,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
     v_off[db] = tr_key * C::kRowBytes + 16 * (((db * 32 + tr_dcol) / 8) ^ C::swz_v(tr_key)) +
-                8 * (j16 & 1);
+                8 * (j16 & 1) + C::v_at(0);
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db) opaque(v_off[db]);
 
   // ---- prologue: tiles 0 and 1 into stages 0 and 1, tiles 2 and 3 in flight, QK^T of tile 0
   TilePos cur = first_run_from(kv_lo);
@@ -252,11 +291,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   TilePos nn = next_tile(nxt);
   TilePos n3 = next_tile(nn);
   // Tile loads are issued unconditionally (a position past the last tile reads key row 0 of the
-  // shard into a free stage).
-  int st_cur = 0;  // stage of tile cur; tiles nxt, nn, n3 are in the next stages (mod 4)
+  // shard, and zeros, into a free stage).
   // One tile: s holds its scores S^T (from the previous step), s_nx receives the next tile's.
-  auto step = [&](f32x16 (&s)[2], f32x16 (&s_nx)[2]) {
-    const int st_nxt = (st_cur + 1) & 3;
+  // The tile's stage is a compile-time constant (the loop is unrolled over the four stages), so
+  // every LDS address is a per-lane base plus an immediate offset.
+  auto step = [&](auto stage, f32x16 (&s)[2], f32x16 (&s_nx)[2]) {
+    constexpr int st_cur = decltype(stage)::value;  // tiles nxt, nn, n3 are in the next stages
+    constexpr int st_nxt = (st_cur + 1) & 3;
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
     const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
@@ -313,7 +354,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     l += rs;
 
     // ---- O^T += V^T P^T ----
-    const unsigned char* Vt = smem + st_cur * C::kStageBytes + C::kTileBytes;
+    const unsigned char* Vt = smem + (C::v_at(st_cur) - C::v_at(0));  // v_off includes v_at(0)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -341,7 +382,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     nxt = nn;
     nn = n3;
     n3 = next_tile(n3);
-    st_cur = st_nxt;
   };
   // Two steps per trip with the score buffers swapping roles (no register copies). A workgroup
   // without visible keys skips the loop (uniform branch).
@@ -358,11 +398,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     qk(0, sa);
-    for (int it = 0; it + 1 < n_tiles; it += 2) {
-      step(sa, sb);
-      step(sb, sa);
+    int left = n_tiles;
+    for (;;) {
+      step(StageIdx<0>{}, sa, sb);
+      if (--left == 0) break;
+      step(StageIdx<1>{}, sb, sa);
+      if (--left == 0) break;
+      step(StageIdx<2>{}, sa, sb);
+      if (--left == 0) break;
+      step(StageIdx<3>{}, sb, sa);
+      if (--left == 0) break;
     }
-    if (n_tiles & 1) step(sa, sb);
   }
 #undef CP_TILE_DMA
 
