@@ -134,8 +134,7 @@ def run_decode(torch, cp, si, seed=0):
     kc = bf16_tokens(torch, si, seed, si.TID_K, toks, (n_kv, d))
     vc = bf16_tokens(torch, si, seed, si.TID_V, toks, (n_kv, d))
     q = bf16_tokens(torch, si, seed, si.TID_Q, np.arange(B), (n_h, d))
-    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, S) // 4, device="cuda")
-    ws_o, ws_l = ws[: B * S * n_h * d], ws[B * S * n_h * d:]
+    ws_o, ws_l = cp.decode_workspace(B, n_h, d, S)
     o = torch.empty(B, n_h, d, device="cuda")
     l = torch.empty(B, n_h, device="cuda")
     offs_d = torch.from_numpy(offs).cuda()
@@ -164,8 +163,7 @@ def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
     kc = bf16_tokens(torch, si, seed, si.TID_K, toks, (n_kv, d))
     vc = bf16_tokens(torch, si, seed, si.TID_V, toks, (n_kv, d))
     q = bf16_tokens(torch, si, seed, si.TID_Q, np.arange(1), (n_h, d))
-    ws = torch.empty(cp.decode_workspace_bytes(1, n_h, d, S) // 4, device="cuda")
-    ws_o, ws_l = ws[: S * n_h * d], ws[S * n_h * d:]
+    ws_o, ws_l = cp.decode_workspace(1, n_h, d, S)
     o = torch.empty(1, n_h, d, device="cuda")
     l = torch.empty(1, n_h, device="cuda")
     offs = torch.zeros(1, dtype=torch.int64, device="cuda")

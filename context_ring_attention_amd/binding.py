@@ -211,6 +211,18 @@ def decode_workspace_bytes(batch: int, n_h: int, d_h: int, n_splits: int) -> int
     return load().cp_decode_workspace_bytes(batch, n_h, d_h, n_splits)
 
 
+def decode_workspace(batch: int, n_h: int, d_h: int, n_splits: int, device="cuda"):
+    """One caller-owned workspace of cp_decode_workspace_bytes bytes, returned as its two views:
+    ws_o bf16 [batch, n_splits, n_h, d_h] and ws_lse fp32 [batch, n_splits, n_h]."""
+    import torch
+    nbytes = decode_workspace_bytes(batch, n_h, d_h, n_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    o_bytes = batch * n_splits * n_h * d_h * 2
+    ws_o = ws[:o_bytes].view(torch.bfloat16).view(batch, n_splits, n_h, d_h)
+    ws_lse = ws[o_bytes:].view(torch.float32).view(batch, n_splits, n_h)
+    return ws_o, ws_lse
+
+
 def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softmax_scale: float,
                    ws_o, ws_lse, o_out, lse_out=None, stream=None):
     """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device."""

@@ -331,13 +331,13 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
 size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits) {
   if (batch < 0 || n_h < 0 || d_h < 0 || n_splits < 0) return 0;
   const size_t parts = (size_t)batch * n_splits * n_h;
-  return parts * d_h * sizeof(float) + parts * sizeof(float);
+  return parts * d_h * 2 + parts * sizeof(float);  // bf16 partial O, then fp32 LSE
 }
 
 int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
                       int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
-                      float* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
+                      void* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
                       void* stream) {
   int st = check_heads(n_h, n_kv, d_h);
   if (st) return st;

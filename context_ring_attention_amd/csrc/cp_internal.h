@@ -72,7 +72,7 @@ struct DecodeParams {
   const void* v;
   const int64_t* kv_offset;
   const int64_t* kv_len;
-  float* ws_o;
+  void* ws_o;  // bf16 [batch, n_splits, n_h, d_h]
   float* ws_lse;
   void* o_out;
   float* lse_out;

@@ -8,15 +8,18 @@
 // The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
 // against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
 // 16-head block) and walks its keys in blocks of 32:
-//  - K and V blocks are loaded with whole-row 16-byte accesses and staged in LDS in their
-//    row-major layout;
+//  - K and V blocks are loaded with whole-row 16-byte non-temporal accesses (the cache is read
+//    once; the loads must not evict the split partials the merge reads back) and staged in LDS
+//    in their row-major layout;
 //  - S^T = K q^T on v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads per MFMA, q^T held in
 //    registers;
 //  - V comes back from LDS as the V^T operand of O^T += V^T P^T via ds_read_b64_tr_b16;
 //  - the next block's K and V loads are issued before the current block's math, and the first
 //    block's loads are in flight together with the query's.
-// The merge kernel then combines the S partials of each (request, head) with the same
-// LSE-weighted rule as cp_merge_lse, reading each head's partials as one contiguous block.
+// Each split's partial O is normalised (a convex combination of V rows) and stored in bf16, the
+// precision of the probabilities its P.V already used; its LSE stays fp32. The merge kernel then
+// combines the S partials of each (request, head) with the same LSE-weighted rule as
+// cp_merge_lse.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
@@ -25,6 +28,7 @@
 namespace cpk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -118,8 +122,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     const int idx = i * 64 + lane;                                                   \
     const int key = min((KB0) + idx / C::kChunks, n - 1);                            \
     const int64_t off = key * row_stride + (idx % C::kChunks) * 8;                   \
-    vr[i] = *reinterpret_cast<const u32x4*>(Vr + off);                               \
-    if constexpr (!C::kKDirect) kr[i] = *reinterpret_cast<const u32x4*>(Kr + off);   \
+    vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vr + off));    \
+    if constexpr (!C::kKDirect)                                                      \
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kr + off));  \
   }
 #define CP_DEC_LOAD_K(KB0, DST)                                                      \
   if constexpr (C::kKDirect) {                                                       \
@@ -245,17 +250,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // workspace layout [batch][n_splits][n_h][D]: a workgroup's heads are one contiguous block
   const int64_t prow = ((int64_t)b * p.n_splits + c) * p.n_h + head;
-  float* wo = p.ws_o + prow * D;
+  __bf16* wo = static_cast<__bf16*>(p.ws_o) + prow * D;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) {
-    const float4 o4 = make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
-    *reinterpret_cast<float4*>(wo + db * 16 + 4 * grp) = o4;
+    const bf16x4 o4 = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
+                       (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
+    *reinterpret_cast<bf16x4*>(wo + db * 16 + 4 * grp) = o4;
   }
   if (grp == 0) p.ws_lse[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
-// whose partials are S rows of D floats, n_h rows apart. 256 / (D/4) groups of D/4 lanes take every
+// whose partials are S rows of D bf16 values (and S fp32 LSEs), n_h rows apart. 256 / (D/4) groups of D/4 lanes take every
 // kGroups-th split. A lane issues the loads of kBatch splits (their LSEs and 16-byte O slices)
 // before combining any of them, so each lane keeps that many loads in flight; batches are folded
 // into a running max, weight and sum. The groups are then combined through LDS in a fixed order.
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const int c4 = threadIdx.x % kLanes;
   const int64_t row0 = (int64_t)(r / p.n_h) * p.n_splits * p.n_h + r % p.n_h;  // split 0's row
   const float* lse = p.ws_lse + row0;
-  const float* o = p.ws_o + row0 * D + c4 * 4;
+  const __bf16* o = static_cast<const __bf16*>(p.ws_o) + row0 * D + c4 * 4;
   const int64_t stride = p.n_h;  // rows between consecutive splits
 
   float M = -INFINITY, wsum = 0.f;
@@ -284,7 +290,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     for (int i = 0; i < kBatch; ++i) {
       const int c = min(c0 + i * kGroups, p.n_splits - 1);  // clamped: in bounds, masked below
       li[i] = c0 + i * kGroups < p.n_splits ? lse[c * stride] : -INFINITY;
-      v[i] = *reinterpret_cast<const float4*>(o + c * stride * D);
+      const bf16x4 h = *reinterpret_cast<const bf16x4*>(o + c * stride * D);
+      v[i] = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
     }
     float Mb = M;
 #pragma unroll
@@ -332,7 +339,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t orow = (int64_t)r * D + c4 * 4;
   if (OUT_BF16) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
     *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o_out) + orow) = v;
   } else {

@@ -124,16 +124,18 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
  *     [kv_offset[b], kv_offset[b] + kv_len[b]); kv_offset, kv_len: device int64 [batch].
  *   Split c of request b covers cache rows [floor(c*L_b/S), floor((c+1)*L_b/S)); every cached key
  *   is visible (the query comes after the cache).
- *   ws_o: device fp32 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
- *     the per-split partials (caller-owned workspace of cp_decode_workspace_bytes bytes, laid out
- *     ws_o first, then ws_lse at byte offset batch*n_splits*n_h*d_h*4).
+ *   ws_o: device bf16 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
+ *     the per-split partials, O normalised over the split's keys and rounded to bf16 (the
+ *     precision of the probabilities its P.V used), LSE in fp32 (caller-owned workspace of
+ *     cp_decode_workspace_bytes bytes, laid out ws_o first, then ws_lse at byte offset
+ *     batch*n_splits*n_h*d_h*2; ws_o 16-byte aligned).
  *   o_out: device [batch, n_h, d_h] in out_dtype; lse_out: device fp32 [batch, n_h] (may be NULL).
  * in_dtype must be CP_BF16. 1 <= n_splits <= 1024.
  * ------------------------------------------------------------------------------------------- */
 int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
                       int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
-                      float* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
+                      void* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
                       void* stream);
 size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits);
 

@@ -141,7 +141,8 @@ def test_merge_and_decode_reject_bad_arguments():
                None) == cp.CP_E_SHAPE
     assert dec(0, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16, cp.CP_F32, None,
                None) == cp.CP_E_ARG
-    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 + 1) * 4
+    # bf16 partial O, then fp32 LSE
+    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 * 2 + 4)
     assert lib.cp_status_string(cp.CP_E_HIP) == b"CP_E_HIP"
 
 

@@ -69,8 +69,7 @@ def test_decode_across_cp_ranks_merged():
             offs_r[b] = first.get(b, 0)
         kc = device_tensor(seed, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
         vc = device_tensor(seed, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
-        ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, S) // 4, device="cuda")
-        ws_o, ws_l = ws[: B * S * n_h * d], ws[B * S * n_h * d:]
+        ws_o, ws_l = cp.decode_workspace(B, n_h, d, S)
         o_r = torch.empty(B, n_h, d, device="cuda")
         l_r = torch.empty(B, n_h, device="cuda")
         cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs_r).cuda(), torch.from_numpy(lens_r).cuda(), S,
@@ -97,8 +96,7 @@ def test_decode_step_graph_replays_match_eager():
     vc = device_tensor(0, si.TID_V, np.arange(total), (n_kv, d), 1.0, "bf16")
     offs_d = torch.from_numpy(offs).cuda()
     lens_d = torch.from_numpy(lengths).cuda()
-    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, S) // 4, device="cuda")
-    ws_o, ws_l = ws[: B * S * n_h * d], ws[B * S * n_h * d:]
+    ws_o, ws_l = cp.decode_workspace(B, n_h, d, S)
     q = torch.empty(B, n_h, d, dtype=torch.bfloat16, device="cuda")
     o_g = torch.empty(B, n_h, d, device="cuda")
     l_g = torch.empty(B, n_h, device="cuda")

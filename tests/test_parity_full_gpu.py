@@ -61,8 +61,7 @@ def test_full_decode_b32_256_splits():
     kc = device_tensor(0, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
     vc = device_tensor(0, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
     q = device_tensor(0, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, S) // 4, device="cuda")
-    ws_o, ws_l = ws[: B * S * n_h * d], ws[B * S * n_h * d:]
+    ws_o, ws_l = cp.decode_workspace(B, n_h, d, S)
     o = torch.empty(B, n_h, d, device="cuda")
     l = torch.empty(B, n_h, device="cuda")
     scale = scale_of(d)
@@ -70,8 +69,6 @@ def test_full_decode_b32_256_splits():
                       scale, ws_o, ws_l, o, l)
     torch.cuda.synchronize()
     qf = oracle_view(0, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws_o = ws_o.view(B, S, n_h, d)
-    ws_l = ws_l.view(B, S, n_h)
     rng = np.random.default_rng(0)
     for b in range(B):
         lo, L = int(offs[b]), int(lens[b])

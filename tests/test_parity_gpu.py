@@ -237,17 +237,13 @@ def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=
     kc = device_tensor(seed, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
     vc = device_tensor(seed, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
     q = device_tensor(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws = torch.empty(cp.decode_workspace_bytes(B, n_h, d, n_splits) // 4, device="cuda")
-    ws_o = ws[: B * n_splits * n_h * d]
-    ws_l = ws[B * n_splits * n_h * d:]
+    ws_o, ws_l = cp.decode_workspace(B, n_h, d, n_splits)
     o_out = torch.empty(B, n_h, d, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
     l_out = torch.empty(B, n_h, device="cuda")
     cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lengths).cuda(),
                       n_splits, scale, ws_o, ws_l, o_out, l_out)
     torch.cuda.synchronize()
     qf = oracle_view(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws_o = ws_o.view(B, n_splits, n_h, d)
-    ws_l = ws_l.view(B, n_splits, n_h)
     for b in range(B):
         lo, L = int(offs[b]), int(lengths[b])
         kf = oracle_view(seed, si.TID_K, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
