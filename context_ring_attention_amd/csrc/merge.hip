@@ -6,13 +6,16 @@
 // results; §5 "关键实现细节" item 3; the ring variants are lossless and exact, §2).
 //
 // HBM-bound: D/4 lanes share a row and move 16 bytes each; a lane issues the loads of eight
-// parts at once. Parts whose LSE is -inf (they saw no key of this row, which the load-balanced
+// parts at once, all partial-O loads and the result stores non-temporal (streamed once). Parts whose LSE is -inf (they saw no key of this row, which the load-balanced
 // layout produces in every ring step) are not read.
 //
 // Pages cited: [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (review).
 #include "device_common.h"
 
 namespace cpk {
+// Native vector for the non-temporal accesses (the partials are read once and the merged result
+// is written once: neither should displace cached data).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
@@ -47,8 +50,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       float4 o[kGroup];
 #pragma unroll
       for (int k = 0; k < kGroup; ++k)
-        o[k] = w[k] != 0.f ? *reinterpret_cast<const float4*>(p.o_parts[i0 + k] + row * D + c4 * 4)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (w[k] != 0.f) {
+          const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p.o_parts[i0 + k] + row * D + c4 * 4));
+          o[k] = make_float4(t[0], t[1], t[2], t[3]);
+        } else {
+          o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
       for (int k = 0; k < kGroup; ++k) {
         wsum += w[k];
@@ -68,9 +75,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     __bf16* out = static_cast<__bf16*>(p.o_out) + row * D + c4 * 4;
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 v = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
-    *reinterpret_cast<bf16x4*>(out) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(out));
   } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(p.o_out) + row * D + c4 * 4) = acc;
+    const f32x4v t = {acc.x, acc.y, acc.z, acc.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4v*>(static_cast<float*>(p.o_out) + row * D + c4 * 4));
   }
   if (c4 == 0 && p.lse_out) p.lse_out[row] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
