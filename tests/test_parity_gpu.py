@@ -130,6 +130,12 @@ def test_bf16_degenerate_shapes():
     run_pass_kv([500], 2, 2, 1, 128, "bf16", seed=5, causal=False)    # no mask
 
 
+def test_bf16_d128_several_kv_heads():
+    # strided K/V rows (n_kv heads per row) through the per-tile load descriptors
+    run_pass_kv([900, 1700], 4, 32, 4, 128, "bf16", seed=6, ranks=[1])   # 8 query heads per KV head
+    run_pass_kv([600], 2, 4, 4, 128, "bf16", seed=7, mode="running")    # MHA: 256 tokens per tile
+
+
 def test_bf16_seed1_second_draw():
     run_pass_kv([2048], 4, 16, 1, 128, "bf16", seed=1, ranks=[2], check_partials=False)
 
