@@ -43,22 +43,29 @@ struct DecCfg {
   // bytes per half-wave (stride 8 mod 64 dwords keeps the eight runs disjoint).
   static constexpr int kStrideK = D * 2 + 16;
   static constexpr int kStrideV = D * 2 + 32;
+  static constexpr int kStageBytes = kBK * (kStrideK + kStrideV);  // one wave's K and V block
   static constexpr int kKSteps = D / 32;         // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
   static constexpr int kChunks = D / 8;          // 16-byte chunks per key row
   static constexpr int kVLoads = kBK * kChunks / 64;
-#ifdef CP_DEC_K_DIRECT
-  static constexpr bool kKDirect = true;
-#else
-  static constexpr bool kKDirect = false;
-#endif
 };
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+// W waves share one (request, split, 16-head block): wave w takes the w-th of W equal parts of
+// the split's keys with LDS of its own, and the W partial results are combined in LDS before
+// the split's partial is written. W = 1 for large batches (enough workgroups to fill the chip);
+// W = 4 for small ones, where one wave per split would leave most of each CU idle.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams p) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char ks[C::kKDirect ? 16 : C::kBK * C::kStrideK];
-  __shared__ __attribute__((aligned(16))) unsigned char vs[C::kBK * C::kStrideV];
+  // combine area: per wave 16 heads x (D values of O + m + l), in fp32
+  constexpr int kCombineBytes = W > 1 ? W * 16 * (D + 2) * 4 : 0;
+  constexpr int kLdsBytes = W * C::kStageBytes > kCombineBytes ? W * C::kStageBytes : kCombineBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+
+  const int wave = W > 1 ? (int)(threadIdx.x / 64) : 0;
+  const int lane = threadIdx.x & 63;
+  unsigned char* ks = smem + wave * C::kStageBytes;
+  unsigned char* vs = ks + C::kBK * C::kStrideK;
 
   const int c = blockIdx.x % p.n_splits;  // split (fastest: neighbours stream adjacent keys)
   // Requests are taken longest first, so the last workgroups to be dispatched are the shortest
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   int b = blockIdx.x / p.n_splits;
   if (p.batch <= 64) {
     const int want = b;
-    const int i = threadIdx.x;
+    const int i = lane;
     const int64_t li = i < p.batch ? p.kv_len[i] : -1;
     int rank = 0;
     for (int j = 0; j < p.batch; ++j) {
@@ -80,14 +87,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int hblocks = (p.group + 15) / 16;
   const int g = blockIdx.y / hblocks;
   const int h0 = (blockIdx.y % hblocks) * 16;
-  const int lane = threadIdx.x;
   const int col = lane & 15;  // head column of the 16x16 blocks
   const int grp = lane >> 4;  // 0..3: k slice of the operands, row group of the accumulator
   const int64_t L = p.kv_len[b];
   const int64_t base = p.kv_offset[b];
   const int64_t lo = ((int64_t)c * L) / p.n_splits;
   const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;
-  const int n = (int)(hi - lo);
+  // this wave's part of the split
+  const int64_t wlo = lo + ((hi - lo) * wave) / W;
+  const int64_t whi = lo + ((hi - lo) * (wave + 1)) / W;
+  const int n = (int)(whi - wlo);
 
   const __bf16* __restrict__ Kc = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ Vc = static_cast<const __bf16*>(p.v);
@@ -107,41 +116,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
   }
 
-  // Loads of one 32-key block. V (and K through LDS): every instruction reads four whole key
-  // rows (16 lanes x 16 bytes per row). K direct: lane (grp, col) reads 16 bytes of key row col
-  // (+16 for the second half) at d offset st*32 + grp*8, as the MFMA A operand, so each load
-  // instruction covers 64 contiguous bytes of 16 rows.
-  const __bf16* Kr = Kc + (base + lo) * p.n_kv * D + (int64_t)g * D;
-  const __bf16* Vr = Vc + (base + lo) * p.n_kv * D + (int64_t)g * D;
+  // Loads of one 32-key block: every instruction reads four whole key rows (16 lanes x 16
+  // bytes per row), non-temporal (the cache is streamed once).
+  const __bf16* Kr = Kc + (base + wlo) * p.n_kv * D + (int64_t)g * D;
+  const __bf16* Vr = Vc + (base + wlo) * p.n_kv * D + (int64_t)g * D;
   const int64_t row_stride = (int64_t)p.n_kv * D;
   u32x4 kr[C::kVLoads], vr[C::kVLoads];
-  bf16x8 kop[2][C::kKSteps];  // K operand of the block being computed (direct mode)
-  bf16x8 knx[2][C::kKSteps];  // K operand of the next block (direct mode)
-#define CP_DEC_LOAD_V(KB0)                                                           \
+#define CP_DEC_LOAD(KB0)                                                             \
   _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
     const int idx = i * 64 + lane;                                                   \
     const int key = min((KB0) + idx / C::kChunks, n - 1);                            \
     const int64_t off = key * row_stride + (idx % C::kChunks) * 8;                   \
     vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vr + off));    \
-    if constexpr (!C::kKDirect)                                                      \
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kr + off));  \
-  }
-#define CP_DEC_LOAD_K(KB0, DST)                                                      \
-  if constexpr (C::kKDirect) {                                                       \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                  \
-      const int key = min((KB0) + 16 * h + col, n - 1);                              \
-      const __bf16* kp = Kr + key * row_stride + grp * 8;                            \
-      _Pragma("unroll") for (int st = 0; st < C::kKSteps; ++st)                      \
-        DST[h][st] = *reinterpret_cast<const bf16x8*>(kp + st * 32);                 \
-    }                                                                                \
+    kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kr + off));    \
   }
 #define CP_DEC_STORE()                                                               \
   _Pragma("unroll") for (int i = 0; i < C::kVLoads; ++i) {                           \
     const int idx = i * 64 + lane;                                                   \
     const int row = idx / C::kChunks, c16 = (idx % C::kChunks) * 16;                 \
     *reinterpret_cast<u32x4*>(vs + row * C::kStrideV + c16) = vr[i];                 \
-    if constexpr (!C::kKDirect)                                                      \
-      *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];               \
+    *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];                 \
   }
 
   float m = -INFINITY, l = 0.f;
@@ -154,21 +148,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int tr_row = 4 * grp + (j16 >> 2);
   const int tr_col = 4 * (j16 & 3);
 
-  if (n > 0) {
-    CP_DEC_LOAD_V(0);
-    CP_DEC_LOAD_K(0, kop);
-  }
+  // The staging LDS is this wave's own: the wave's LDS accesses are ordered among themselves, so
+  // the loop needs no workgroup barrier (and waves with different key counts never meet one).
+  if (n > 0) CP_DEC_LOAD(0);
   // retire the q and first-block loads together before the block loop (keeps the loop's
   // prefetch out of its waits)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   if (n > 0) CP_DEC_STORE();
-  __syncthreads();
   for (int kb0 = 0; kb0 < n; kb0 += C::kBK) {
     const bool has_next = kb0 + C::kBK < n;
-    if (has_next) {
-      CP_DEC_LOAD_V(kb0 + C::kBK);
-      CP_DEC_LOAD_K(kb0 + C::kBK, knx);
-    }
+    if (has_next) CP_DEC_LOAD(kb0 + C::kBK);
 
     // S^T (keys x heads) for the two 16-key halves; K operand: key row col, d slice of grp
     f32x4 s[2];
@@ -177,15 +166,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < C::kKSteps; ++st) {
-        bf16x8 a;
-        if constexpr (C::kKDirect)
-          a = kop[h][st];
-        else
-          a = *reinterpret_cast<const bf16x8*>(ks + (16 * h + col) * C::kStrideK + (st * 32 + grp * 8) * 2);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(ks + (16 * h + col) * C::kStrideK + (st * 32 + grp * 8) * 2);
         s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[st], s[h], 0, 0, 0);
       }
     }
-    // keys past the split are masked
+    // keys past the wave's part are masked
     if (kb0 + C::kBK > n) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -228,24 +214,51 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pt,
                                                           oacc[db], 0, 0, 0);
     }
-    __syncthreads();
-    if (has_next) {
-      CP_DEC_STORE();
-      if constexpr (C::kKDirect) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int st = 0; st < C::kKSteps; ++st) kop[h][st] = knx[h][st];
-      }
-    }
-    __syncthreads();
+    if (has_next) CP_DEC_STORE();  // after this block's LDS reads (same wave: in order)
   }
-#undef CP_DEC_LOAD_V
-#undef CP_DEC_LOAD_K
+#undef CP_DEC_LOAD
 #undef CP_DEC_STORE
 
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
+  if constexpr (W > 1) {
+    // combine the W parts (m in base-2 units, the same in every lane of a head column)
+    float* cm = reinterpret_cast<float*>(smem);  // [W][16] max
+    float* cl = cm + W * 16;                     // [W][16] sum
+    float* co = cl + W * 16;                     // [W][16][D] unnormalised O
+    __syncthreads();                             // every wave is done with its staging LDS
+    if (grp == 0) {
+      cm[wave * 16 + col] = m;
+      cl[wave * 16 + col] = lt;
+    }
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) co[(wave * 16 + col) * D + db * 16 + 4 * grp + v] = oacc[db][v];
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, cm[w * 16 + col]);
+    float wt[W];
+    lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = cm[w * 16 + col];
+      wt[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // a part with no key: 0
+      lt += wt[w] * cl[w * 16 + col];
+    }
+    m = M;
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) o = fmaf(wt[w], co[(w * 16 + col) * D + db * 16 + 4 * grp + v], o);
+        oacc[db][v] = o;
+      }
+  }
   if (!head_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // workspace layout [batch][n_splits][n_h][D]: a workgroup's heads are one contiguous block
@@ -352,14 +365,22 @@ hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
   const int hblocks = (p.group + 15) / 16;
   const dim3 grid(p.n_splits * p.batch, p.n_kv * hblocks);
   const dim3 mgrid(p.batch * p.n_h);
+  // Fewer workgroups than 8 per CU: four waves share each split.
+  const bool wide = (int64_t)grid.x * grid.y < 2048;
   if (d_h == 64) {
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64), 0, stream, p);
+    if (wide)
+      hipLaunchKernelGGL((decode_split_kernel<64, 4>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<64, 1>), grid, dim3(64), 0, stream, p);
     if (p.out_bf16)
       hipLaunchKernelGGL((decode_merge_kernel<64, true>), mgrid, dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((decode_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64), 0, stream, p);
+    if (wide)
+      hipLaunchKernelGGL((decode_split_kernel<128, 4>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<128, 1>), grid, dim3(64), 0, stream, p);
     if (p.out_bf16)
       hipLaunchKernelGGL((decode_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, p);
     else
