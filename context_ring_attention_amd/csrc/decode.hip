@@ -274,37 +274,37 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
 }
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
-// whose partials are S rows of D bf16 values (and S fp32 LSEs), n_h rows apart. 256 / (D/4) groups of D/4 lanes take every
-// kGroups-th split. A lane issues the loads of kBatch splits (their LSEs and 16-byte O slices)
-// before combining any of them, so each lane keeps that many loads in flight; batches are folded
-// into a running max, weight and sum. The groups are then combined through LDS in a fixed order.
+// whose partials are S rows of D bf16 values (and S fp32 LSEs), n_h rows apart. D/8 lanes cover
+// a row, 16 bytes each; the 256 / (D/8) lane groups take every kGroups-th split. A lane issues
+// the loads of up to kBatch splits (their LSEs and O slices) before combining any of them, so
+// one round of loads covers 256 splits at D = 128; batches are folded into a running max,
+// weight and sum. The groups are then combined through LDS in a fixed order.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
-  constexpr int kLanes = D / 4;
+  constexpr int kLanes = D / 8;
   constexpr int kGroups = 256 / kLanes;
   constexpr int kBatch = 16;
   __shared__ float red_m[kGroups];
   __shared__ float red_w[kGroups];
-  __shared__ float4 red_o[kGroups][kLanes];
+  __shared__ float red_o[kGroups][kLanes][8];
   const int r = blockIdx.x;  // b * n_h + head
   const int grp = threadIdx.x / kLanes;
-  const int c4 = threadIdx.x % kLanes;
+  const int c8 = threadIdx.x % kLanes;
   const int64_t row0 = (int64_t)(r / p.n_h) * p.n_splits * p.n_h + r % p.n_h;  // split 0's row
   const float* lse = p.ws_lse + row0;
-  const __bf16* o = static_cast<const __bf16*>(p.ws_o) + row0 * D + c4 * 4;
+  const __bf16* o = static_cast<const __bf16*>(p.ws_o) + row0 * D + c8 * 8;
   const int64_t stride = p.n_h;  // rows between consecutive splits
 
   float M = -INFINITY, wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int c0 = grp; c0 < p.n_splits; c0 += kGroups * kBatch) {
     float li[kBatch];
-    float4 v[kBatch];
+    bf16x8 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = min(c0 + i * kGroups, p.n_splits - 1);  // clamped: in bounds, masked below
       li[i] = c0 + i * kGroups < p.n_splits ? lse[c * stride] : -INFINITY;
-      const bf16x4 h = *reinterpret_cast<const bf16x4*>(o + c * stride * D);
-      v[i] = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+      v[i] = *reinterpret_cast<const bf16x8*>(o + c * stride * D);
     }
     float Mb = M;
 #pragma unroll
@@ -312,53 +312,51 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     if (Mb == -INFINITY) continue;  // nothing seen yet
     const float a = expf(M - Mb);    // M = -inf -> 0
     wsum *= a;
-    acc.x *= a;
-    acc.y *= a;
-    acc.z *= a;
-    acc.w *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= a;
     M = Mb;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const float w = expf(li[i] - M);  // -inf -> 0: the part saw no key
       if (w == 0.f) continue;           // skip its O, which may be anything
       wsum += w;
-      acc.x = fmaf(w, v[i].x, acc.x);
-      acc.y = fmaf(w, v[i].y, acc.y);
-      acc.z = fmaf(w, v[i].z, acc.z);
-      acc.w = fmaf(w, v[i].w, acc.w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)v[i][e], acc[e]);
     }
   }
-  if (c4 == 0) red_m[grp] = M;
+  if (c8 == 0) red_m[grp] = M;
   __syncthreads();
   float Mt = red_m[0];
 #pragma unroll
   for (int i = 1; i < kGroups; ++i) Mt = fmaxf(Mt, red_m[i]);
   const float a = (M == -INFINITY) ? 0.f : expf(M - Mt);
-  red_o[grp][c4] = make_float4(acc.x * a, acc.y * a, acc.z * a, acc.w * a);
-  if (c4 == 0) red_w[grp] = wsum * a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red_o[grp][c8][e] = acc[e] * a;
+  if (c8 == 0) red_w[grp] = wsum * a;
   __syncthreads();
   if (grp != 0) return;
   wsum = 0.f;
-  acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < kGroups; ++i) {  // fixed order: deterministic
     wsum += red_w[i];
-    const float4 v = red_o[i][c4];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += red_o[i][c8][e];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t orow = (int64_t)r * D + c4 * 4;
+  const int64_t orow = (int64_t)r * D + c8 * 8;
   if (OUT_BF16) {
-    bf16x4 v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o_out) + orow) = v;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.o_out) + orow) = out;
   } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(p.o_out) + orow) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    float* out = static_cast<float*>(p.o_out) + orow;
+    *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
-  if (c4 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
+  if (c8 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
