@@ -44,8 +44,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-// Native vector for 16-byte staging (arrays of HIP's uint4 struct are not promoted to registers).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int WAVES>
 struct Bf16Cfg {

@@ -7,7 +7,8 @@
 //
 // The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
 // against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
-// 16-head block) and walks its keys in blocks of 32:
+// 16-head block) and walks its keys in blocks of 32; for small batches four waves share a split,
+// each taking a quarter of its keys, and combine their results in LDS:
 //  - K and V blocks are loaded with whole-row 16-byte non-temporal accesses (the cache is read
 //    once; the loads must not evict the split partials the merge reads back) and staged in LDS
 //    in their row-major layout;
