@@ -272,6 +272,17 @@ def test_decode_small_ragged():
     run_decode([3000, 1, 100, 4097, 257], 16, 1, 128, 256, check_splits=[0, 1, 99, 255])
 
 
+def test_decode_empty_requests_four_waves_per_split():
+    # small grid: four waves share each split; requests with no cached key give O = 0, LSE = -inf
+    run_decode([0, 37, 0, 2000, 5], 16, 1, 128, 256, seed=4, check_splits=[0, 128, 255])
+
+
+def test_decode_one_wave_per_split_with_empty_splits():
+    # 8 requests x 256 splits = 2048 workgroups: one wave per split; short requests leave most
+    # splits empty
+    run_decode([0, 1, 255, 256, 257, 1000, 3, 700], 16, 1, 128, 256, seed=5, check_splits=[0, 1, 200, 255])
+
+
 def test_decode_gqa_d64_bf16_out():
     run_decode([999, 64, 2500], 8, 2, 64, 16, seed=1, out="bf16", check_splits=[0, 15])
 
