@@ -130,6 +130,8 @@ struct TilePos {
   int kt;
   int vis;  // keys of the run visible to the workgroup's last query
   int loc, pos, len;
+  int n_full;    // keys of the run visible to every row of the workgroup
+  int64_t off;   // byte offset of the tile's first key row in the shard
 };
 
 template <int D, int WAVES>
@@ -178,19 +180,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- KV tiles: runs of the same sequence, the prefix visible to the last query ----------
+  const uint32_t row_bytes = (uint32_t)p.n_kv * D * 2;
   auto first_run_from = [&](int j) -> TilePos {
     for (; j < kv_hi; ++j) {
       const Seg ks = p.ks[j];
       if (ks.seq != qs.seq) continue;
       const int vis = visible_prefix(ks, qpos_hi, p.causal);
-      if (vis > 0) return TilePos{j, 0, vis, ks.loc, ks.pos, ks.len};
+      if (vis > 0) {
+        const int n_full = p.causal ? max(0, min(ks.len, qpos_lo - ks.pos + 1)) : ks.len;
+        return TilePos{j, 0, vis, ks.loc, ks.pos, ks.len, n_full, (int64_t)ks.loc * row_bytes};
+      }
     }
-    return TilePos{kv_hi, 0, 0, 0, 0, 1};
+    return TilePos{kv_hi, 0, 0, 0, 0, 1, 1, 0};
   };
   auto next_tile = [&](TilePos t) -> TilePos {
     if (t.j >= kv_hi) return t;
     if (t.kt + C::kBN < t.vis) {
       t.kt += C::kBN;
+      t.off += (int64_t)C::kBN * row_bytes;
       return t;
     }
     return first_run_from(t.j + 1);
@@ -200,7 +207,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   // w * kBlocksPerWave + i of a tile; in a block, lane l fills row l / kChunks, slot l % kChunks,
   // which holds chunk slot ^ swz(row). The tile's first key row is a uniform 64-bit base; a lane
   // adds a 32-bit offset (its row, clamped to the run's last key, and its chunk).
-  const uint32_t row_bytes = (uint32_t)p.n_kv * D * 2;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + (int64_t)g * D);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + (int64_t)g * D);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
   // the run's end fall outside it and arrive in LDS as zeros (no clamp, no per-lane address math).
 #define CP_TILE_DMA(T, STAGE)                                                                 \
   {                                                                                           \
-    const int64_t first = (int64_t)((T).loc + (T).kt) * row_bytes;                            \
+    const int64_t first = (T).off;                                                            \
     const int nrec = min((T).len - (T).kt, C::kBN) * (int)row_bytes;                          \
     const __amdgpu_buffer_rsrc_t kr =                                                         \
         __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + first), 0, nrec, kBufferWord3);        \
@@ -298,8 +304,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
     constexpr int st_nxt = (st_cur + 1) & 3;
 
     // ---- mask (only tiles not fully visible to every row of the workgroup) ----
-    const int n_full = p.causal ? max(0, min(cur.len, qpos_lo - cur.pos + 1)) : cur.len;
-    if (cur.kt + C::kBN > n_full) {
+    if (cur.kt + C::kBN > cur.n_full) {
       // key ko of the run is visible iff ko < len and (not causal or pos + ko <= qpos):
       // ko < lim with lim = min(len, qpos - pos + 1) (or len without the causal mask)
       const int lim = p.causal ? min(cur.len, qpos - cur.pos + 1) : cur.len;
