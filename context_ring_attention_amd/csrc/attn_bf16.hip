@@ -205,8 +205,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
 
   // K/V staging: HBM -> LDS with direct-to-LDS loads (no VGPRs in between). Wave w fills blocks
   // w * kBlocksPerWave + i of a tile; in a block, lane l fills row l / kChunks, slot l % kChunks,
-  // which holds chunk slot ^ swz(row). The tile's first key row is a uniform 64-bit base; a lane
-  // adds a 32-bit offset (its row, clamped to the run's last key, and its chunk).
+  // which holds chunk slot ^ swz(row). A lane's offset (its row and chunk) is fixed; the tile's
+  // position is in the buffer descriptor.
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + (int64_t)g * D);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + (int64_t)g * D);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
