@@ -1,0 +1,51 @@
+"""Seeded random small configurations of the ring paths against the oracle.
+
+Each case draws sequence lengths (ragged, down to one token), a CP world, a head ratio, D_H,
+input dtype, the causal flag and the ring variant (Pass-KV with partials or a running merge, or
+Pass-Q over a cached prefix), then checks one rank's merged result, and its partials where the
+mode keeps them, element by element against the oracle ("Context Parallelism for Scalable
+Million-Token Inference", §3 core formulas; the oracle's readings are the ones the other parity
+tests use).
+"""
+import numpy as np
+import pytest
+
+from test_parity_gpu import run_pass_kv, run_pass_q
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw_cases(n_cases, seed=2026):
+    rng = np.random.default_rng(seed)
+    heads = [(16, 1), (8, 2), (4, 4), (32, 4), (12, 3)]
+    cases = []
+    for i in range(n_cases):
+        n_h, n_kv = heads[rng.integers(len(heads))]
+        d = int(rng.choice([64, 128]))
+        N = int(rng.choice([1, 2, 3, 4, 8]))
+        if rng.random() < 0.3:  # Pass-Q over a cached prefix
+            n_seq = int(rng.integers(1, 4))
+            P = [int(x) for x in rng.integers(0, 1200, size=n_seq)]
+            T = [int(x) for x in rng.integers(1, 400, size=n_seq)]
+            cases.append(("pass_q", dict(P=P, T=T, N=N, n_h=n_h, n_kv=n_kv, d=d, seed=100 + i)))
+        else:
+            n_seq = int(rng.integers(1, 5))
+            seqs = [int(x) for x in rng.integers(1, 1500, size=n_seq)]
+            dtype = "f32" if rng.random() < 0.2 else "bf16"
+            causal = bool(rng.random() < 0.8)
+            mode = str(rng.choice(["partials", "running"]))
+            rank = int(rng.integers(N))
+            cases.append(("pass_kv", dict(seqs=seqs, N=N, n_h=n_h, n_kv=n_kv, d=d, dtype=dtype,
+                                          seed=100 + i, causal=causal, ranks=[rank], mode=mode)))
+    return cases
+
+
+CASES = _draw_cases(20)
+
+
+@pytest.mark.parametrize("kind,kw", CASES, ids=[f"{k}-{i}" for i, (k, _) in enumerate(CASES)])
+def test_random_config(kind, kw):
+    if kind == "pass_q":
+        run_pass_q(**kw)
+    else:
+        run_pass_kv(**kw)
