@@ -10,7 +10,7 @@ tests use).
 import numpy as np
 import pytest
 
-from test_parity_gpu import run_pass_kv, run_pass_q
+from test_parity_gpu import run_decode, run_pass_kv, run_pass_q
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +49,26 @@ def test_random_config(kind, kw):
         run_pass_q(**kw)
     else:
         run_pass_kv(**kw)
+
+
+def _draw_decode_cases(n_cases, seed=2027):
+    rng = np.random.default_rng(seed)
+    heads = [(16, 1), (8, 2), (40, 2), (4, 4)]
+    cases = []
+    for i in range(n_cases):
+        n_h, n_kv = heads[rng.integers(len(heads))]
+        B = int(rng.choice([1, 2, 5, 9, 33]))
+        lengths = [int(x) for x in rng.integers(0, 3000, size=B)]
+        n_splits = int(rng.choice([1, 7, 64, 256]))
+        cases.append(dict(lengths=lengths, n_h=n_h, n_kv=n_kv, d=int(rng.choice([64, 128])),
+                          n_splits=n_splits, seed=200 + i, out=str(rng.choice(["f32", "bf16"])),
+                          check_splits=[0, n_splits - 1]))
+    return cases
+
+
+DECODE_CASES = _draw_decode_cases(10)
+
+
+@pytest.mark.parametrize("kw", DECODE_CASES, ids=[f"decode-{i}" for i in range(len(DECODE_CASES))])
+def test_random_decode_config(kw):
+    run_decode(**kw)
