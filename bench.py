@@ -13,8 +13,9 @@ value = causal-useful TFLOP/s: 4 * D_H flops per visible (query token, query hea
 masked and skipped work is not counted. The same JSON line reports the dominant kernel's
 roofline (cp_partial_attn's MFMA kernel, per-launch time from HIP events on the launch stream),
 secondary measurements (split-KV decode GB/s, persistent-KV Pass-Q TFLOP/s, merge GB/s, and with
---extended the 1M-token varlen rank share), and the fp64 oracle timed on host cores for a
-bounded sample of the same workload.
+--extended the 1M-token varlen rank share), the fp64 oracle timed on host cores for a
+bounded sample of the same workload, and (with the secondary legs) the MFMA clock probe: the bf16
+MFMA rate and shader clock that MFMA-only code sustains on random and on near-constant operands.
 """
 from __future__ import annotations
 
@@ -231,7 +232,30 @@ def device_rooflines(torch):
     info["copy_gbs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
     info["published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     del src, dst
+    info["mfma_probe"] = run_mfma_probe()
     log(f"device: {info}")
+    return info
+
+
+def run_mfma_probe():
+    """The MFMA clock probe (a separate program, run as a child process): the bf16 MFMA rate and
+    shader clock the chip sustains with random and with near-constant operands. None if the probe
+    is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "context_ring_attention_amd", "probe_mfma_clock")
+    if not os.path.exists(exe):
+        log("mfma probe: not built")
+        return None
+    try:
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        log("mfma probe: timed out")
+        return None
+    if res.returncode != 0:
+        log(f"mfma probe failed ({res.returncode}): {res.stderr.strip()[-300:]}")
+        return None
+    info = json.loads(res.stdout.strip().splitlines()[-1])
+    log(f"mfma probe: {info}")
     return info
 
 
@@ -449,6 +473,10 @@ def main():
         log("calibration copy: 1 GiB read, 1 GiB written")
 
     device_info = device_rooflines(torch) if not args.no_secondary else None
+    probe = (device_info or {}).get("mfma_probe")
+    if probe and probe.get("random", {}).get("tflops"):
+        # the same kernel rate against what MFMA-only code sustains on random operands
+        roofline["frac_of_mfma_probe_random"] = round(achieved / probe["random"]["tflops"], 3)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libcpattn.so")
+# stand-alone measurement probe (bench.py runs it for the achievable MFMA rate and clock)
+PROBE_SRC = "probe_mfma_clock.hip"
+PROBE_PATH = os.path.join(PKG, "probe_mfma_clock")
 
 SOURCES = ["api.cpp", "attn_f32.hip", "attn_bf16.hip", "merge.hip", "decode.hip"]
 ARCH = "gfx950"
@@ -51,8 +54,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_probe() -> str:
+    """Compile the MFMA clock probe (a program of its own, not linked into the library)."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [_hipcc(), *COMMON_FLAGS, "-x", "hip", os.path.join(CSRC, PROBE_SRC), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        noise = "not a recognized feature for this target"
+        msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{msgs}")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build(jobs: int = 8) -> str:
-    """Compile every source for gfx950 and link libcpattn.so. Always rebuilds."""
+    """Compile every source for gfx950, link libcpattn.so and build the MFMA clock probe. Always
+    rebuilds."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -70,6 +87,7 @@ def build(jobs: int = 8) -> str:
         if missing:
             raise RuntimeError(f"kernel launch stubs missing from the library: {missing}")
     os.replace(tmp, LIB_PATH)
+    build_probe()
     return LIB_PATH
 
 
