@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <map>
 #include <string>
@@ -48,10 +49,11 @@ int pack_segments(const cp_segment* segs, int n, int64_t rows, const char* what,
     const cp_segment& s = segs[i];
     if (s.seq_id < 0 || s.pos_start < 0 || s.len < 0 || s.local_start < 0)
       return fail(CP_E_SHAPE, "%s[%d]: negative field", what, i);
-    if (s.local_start + s.len > rows)
-      return fail(CP_E_SHAPE, "%s[%d]: rows [%lld, %lld) outside the shard of %lld rows", what, i,
-                  (long long)s.local_start, (long long)(s.local_start + s.len), (long long)rows);
-    if (s.pos_start + s.len > kI32Max)
+    // (written so that no sum of two caller values can overflow)
+    if (s.len > rows || s.local_start > rows - s.len)
+      return fail(CP_E_SHAPE, "%s[%d]: rows [%lld, +%lld) outside the shard of %lld rows", what, i,
+                  (long long)s.local_start, (long long)s.len, (long long)rows);
+    if (s.len > kI32Max || s.pos_start > kI32Max - s.len)
       return fail(CP_E_UNSUPPORTED, "%s[%d]: positions beyond 2^31", what, i);
     out[i] = cpk::Seg{s.seq_id, (int32_t)s.pos_start, (int32_t)s.len, (int32_t)s.local_start};
   }
@@ -264,6 +266,11 @@ int cp_shard_map(int n_ranges, const int32_t* seq_id, const int64_t* range_begin
   // sequences without a range have length 0 and do not shift later bases
 
   const int64_t n_chunks = 2 * (int64_t)cp_world;
+  // chunk edges are computed as c * L / (2N) in 64 bits
+  for (int i = 0; i < n_ranges; ++i)
+    if (range_end[i] - range_begin[i] > INT64_MAX / n_chunks)
+      return fail(CP_E_UNSUPPORTED, "range %d: length %lld too large for %lld chunks", i,
+                  (long long)(range_end[i] - range_begin[i]), (long long)n_chunks);
   int n_segs = 0;
   int64_t n_tok = 0;
   for (int i = 0; i < n_ranges; ++i) {

@@ -75,7 +75,8 @@ typedef struct {
  *               packed global index base[seq] + pos, where base[s] is the sum of the lengths of
  *               sequences 0..s-1 and a sequence's length is the largest range_end given for it.
  *               *n_tokens_out (optional) = local token count.
- * Returns CP_E_CAPACITY (with the counts set) if a buffer is too small, CP_E_ARG on bad ranges.
+ * Returns CP_E_CAPACITY (with the counts set) if a buffer is too small, CP_E_ARG on bad ranges,
+ * CP_E_UNSUPPORTED if a range is so long that its chunk edges (c * L / 2N) overflow 64 bits.
  * ------------------------------------------------------------------------------------------- */
 int cp_shard_map(int n_ranges, const int32_t* seq_id, const int64_t* range_begin,
                  const int64_t* range_end, int cp_world, int rank, cp_segment* segs_out,

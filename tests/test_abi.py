@@ -86,6 +86,11 @@ def test_shard_map_capacity_and_argument_errors():
     st = lib.cp_shard_map(1, None, b.ctypes.data_as(i64p), bad_e.ctypes.data_as(i64p), 4, 0, segs, 1,
                           ctypes.byref(n_segs), None, 0, None)
     assert st == cp.CP_E_ARG
+    # a range whose chunk edges c * L / 2N would overflow 64 bits
+    huge_e = np.array([1 << 62], np.int64)
+    st = lib.cp_shard_map(1, None, b.ctypes.data_as(i64p), huge_e.ctypes.data_as(i64p), 4, 0, segs, 1,
+                          ctypes.byref(n_segs), None, 0, None)
+    assert st == cp.CP_E_UNSUPPORTED and "too large" in cp.last_error()
 
 
 def _partial(**kw):
@@ -119,6 +124,11 @@ def test_partial_attn_rejects_bad_arguments_without_launching():
     assert _partial(tq=1 << 31) == cp.CP_E_UNSUPPORTED
     huge, n = cp.segments([(0, 0, 1 << 27, 0)])       # 2^27 tokens x 16 heads per KV head
     assert _partial(qs=huge, nq=n, tq=1 << 27, n_h=16, n_kv=1) == cp.CP_E_UNSUPPORTED
+    # fields whose sums would overflow 64 bits are rejected, not wrapped
+    wrap, n = cp.segments([(0, 0, 1 << 62, 1 << 62)])
+    assert _partial(qs=wrap, nq=n) == cp.CP_E_SHAPE
+    far, n = cp.segments([(0, (1 << 63) - 1, 1, 0)])
+    assert _partial(ks=far, nk=n) == cp.CP_E_UNSUPPORTED
     # nothing to do is not an error (no launch either)
     assert _partial(nq=0) == cp.CP_OK
 
