@@ -119,6 +119,35 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _req(t, name: str, dtypes=None, shape=None, numel=None):
+    """Checks what the C ABI cannot see behind a raw pointer: a tensor argument must be a
+    contiguous device tensor of the expected dtype and shape. (A host tensor's address handed to a
+    kernel would fault the GPU; a strided view would be read with the wrong layout.) Plain integer
+    addresses are passed through unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _float_types():
+    import torch
+    return (torch.float32,)
+
+
+def _in_types():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -190,6 +219,11 @@ def partial_attn(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: float, o
     ka, nk = _segarg(kv_segs)
     tq, n_h, d = q.shape
     tk, n_kv = k.shape[0], k.shape[1]
+    _req(q, "q", _in_types())
+    _req(k, "k", (q.dtype,), (tk, n_kv, d))
+    _req(v, "v", (q.dtype,), (tk, n_kv, d))
+    _req(o, "o", _float_types(), (tq, n_h, d))
+    _req(lse, "lse", _float_types(), numel=tq * n_h)
     _check(lib.cp_partial_attn(_ptr(q), _ptr(k), _ptr(v), tq, tk, n_h, n_kv, d, _dtype_code(q),
                                qa, nq, ka, nk, int(causal), float(softmax_scale), _ptr(o), _ptr(lse),
                                int(accumulate), _stream(stream)))
@@ -201,6 +235,13 @@ def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None):
     n = len(o_parts)
     d = o_parts[0].shape[-1]
     rows = o_parts[0].numel() // d
+    if len(lse_parts) != n:
+        raise ValueError(f"{n} O parts but {len(lse_parts)} LSE parts")
+    for i in range(n):
+        _req(o_parts[i], f"o_parts[{i}]", _float_types(), numel=rows * d)
+        _req(lse_parts[i], f"lse_parts[{i}]", _float_types(), numel=rows)
+    _req(o_out, "o_out", _in_types(), numel=rows * d)
+    _req(lse_out, "lse_out", _float_types(), numel=rows)
     op = (ctypes.c_void_p * n)(*[_ptr(t) for t in o_parts])
     lp = (ctypes.c_void_p * n)(*[_ptr(t) for t in lse_parts])
     _check(lib.cp_merge_lse(n, op, lp, rows, d, _ptr(o_out), _dtype_code(o_out), _ptr(lse_out),
@@ -227,8 +268,20 @@ def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softma
                    ws_o, ws_lse, o_out, lse_out=None, stream=None):
     """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device."""
     lib = load()
+    import torch
     B, n_h, d = q.shape
     n_kv = k_cache.shape[1]
+    _req(q, "q", (torch.bfloat16,))
+    _req(k_cache, "k_cache", (torch.bfloat16,))
+    _req(v_cache, "v_cache", (torch.bfloat16,), tuple(k_cache.shape))
+    if k_cache.dim() != 3 or k_cache.shape[2] != d:
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected [tokens, n_kv, {d}]")
+    _req(kv_offset, "kv_offset", (torch.int64,), (B,))
+    _req(kv_len, "kv_len", (torch.int64,), (B,))
+    _req(ws_o, "ws_o", (torch.bfloat16,), numel=B * n_splits * n_h * d)
+    _req(ws_lse, "ws_lse", _float_types(), numel=B * n_splits * n_h)
+    _req(o_out, "o_out", _in_types(), (B, n_h, d))
+    _req(lse_out, "lse_out", _float_types(), numel=B * n_h)
     _check(lib.cp_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
                                  _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
                                  float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
@@ -244,6 +297,24 @@ def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool
     qa, nq = _segarg(q_segs)
     tq, n_h, d = q.shape
     n_kv = k_shards[0].shape[1]
+    if len(v_shards) != N or len(kv_segs) != N:
+        raise ValueError("k_shards, v_shards and kv_segs must have one entry per shard")
+    _req(q, "q", _in_types())
+    for i in range(N):
+        _req(k_shards[i], f"k_shards[{i}]", (q.dtype,))
+        _req(v_shards[i], f"v_shards[{i}]", (q.dtype,), tuple(k_shards[i].shape))
+        if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
+            raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
+    for name, parts, shp in (("o_parts", o_parts, (tq, n_h, d)), ("lse_parts", lse_parts, None)):
+        if parts is not None:
+            if len(parts) != N:
+                raise ValueError(f"{name} must have {N} entries")
+            for i, t in enumerate(parts):
+                _req(t, f"{name}[{i}]", _float_types(), shp, None if shp else tq * n_h)
+    _req(o_acc, "o_acc", _float_types(), (tq, n_h, d))
+    _req(lse_acc, "lse_acc", _float_types(), numel=tq * n_h)
+    _req(o_out, "o_out", _in_types(), (tq, n_h, d))
+    _req(lse_out, "lse_out", _float_types(), numel=tq * n_h)
     vp = ctypes.c_void_p
     segp = ctypes.POINTER(CpSegment)
     ks = (vp * N)(*[_ptr(t) for t in k_shards])
@@ -282,6 +353,26 @@ def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, sof
     segp = ctypes.POINTER(CpSegment)
     n_h, d = q_shards[0].shape[1], q_shards[0].shape[2]
     n_kv = k_shards[0].shape[1]
+    if not (len(q_segs) == len(k_shards) == len(v_shards) == len(kv_segs) == len(o_out) == N):
+        raise ValueError("q_shards, q_segs, k_shards, v_shards, kv_segs and o_out need one entry per rank")
+    if len(o_parts) != N * N or len(lse_parts) != N * N:
+        raise ValueError(f"o_parts and lse_parts need {N * N} entries (slot q*N + s)")
+    dt = q_shards[0].dtype
+    for i in range(N):
+        _req(q_shards[i], f"q_shards[{i}]", (dt,))
+        if q_shards[i].dim() != 3 or tuple(q_shards[i].shape[1:]) != (n_h, d):
+            raise ValueError(f"q_shards[{i}] has shape {tuple(q_shards[i].shape)}, expected [tokens, {n_h}, {d}]")
+        _req(k_shards[i], f"k_shards[{i}]", (dt,))
+        _req(v_shards[i], f"v_shards[{i}]", (dt,), tuple(k_shards[i].shape))
+        if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
+            raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
+        tqi = q_shards[i].shape[0]
+        _req(o_out[i], f"o_out[{i}]", _in_types(), (tqi, n_h, d))
+        if lse_out is not None:
+            _req(lse_out[i], f"lse_out[{i}]", _float_types(), numel=tqi * n_h)
+        for s_ in range(N):
+            _req(o_parts[i * N + s_], f"o_parts[{i * N + s_}]", _float_types(), (tqi, n_h, d))
+            _req(lse_parts[i * N + s_], f"lse_parts[{i * N + s_}]", _float_types(), numel=tqi * n_h)
     qs = (vp * N)(*[_ptr(t) for t in q_shards])
     tq = (ctypes.c_int64 * N)(*[t.shape[0] for t in q_shards])
     qseg_objs = [_segarg(s) for s in q_segs]

@@ -217,3 +217,55 @@ def test_ring_drivers_validate_every_step_and_merge_before_launching():
     assert lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, N, a["k"], a["v"], a["tk"], a["kv_segs"],
                                a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, a["o_parts"], a["l_parts"], None,
                                None, 0x7200000, cp.CP_F32, None, None) == cp.CP_E_ARG
+
+
+def test_binding_rejects_host_tensors_before_calling_the_library():
+    """A host tensor's address handed to a kernel would fault the GPU: the binding refuses it (and
+    strided views, wrong dtypes and shapes) before any library call. Needs no GPU."""
+    import torch
+    q = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(16, 1, 64, dtype=torch.bfloat16)
+    o = torch.zeros(16, 4, 64)
+    lse = torch.zeros(16, 4)
+    segs = [(0, 0, 16, 0)]
+    with pytest.raises(ValueError, match="device tensor"):
+        cp.partial_attn(q, k, k, segs, segs, True, 0.125, o, lse)
+    with pytest.raises(ValueError, match="device tensor"):
+        cp.merge_lse([o], [lse], o)
+    with pytest.raises(ValueError, match="device tensor"):
+        cp.decode_splitkv(q[:2], k, k, torch.zeros(2, dtype=torch.int64),
+                          torch.zeros(2, dtype=torch.int64), 4, 0.125,
+                          torch.zeros(2 * 4 * 4 * 64, dtype=torch.bfloat16), torch.zeros(2 * 4 * 4),
+                          torch.zeros(2, 4, 64))
+    with pytest.raises(ValueError, match="device tensor"):
+        cp.ring_pass_kv(q, segs, 0, [k], [k], [segs], True, 0.125, o, o_acc=o, lse_acc=lse)
+
+
+def test_binding_checks_layout_dtype_and_shape():
+    """The same checks on tensors that claim to be on the device: exercised through a stand-in
+    object, so no GPU is needed."""
+    import torch
+
+    class Dev:
+        def __init__(self, t):
+            self.t = t
+            self.is_cuda = True
+            self.dtype, self.shape = t.dtype, t.shape
+
+        def is_contiguous(self):
+            return self.t.is_contiguous()
+
+        def numel(self):
+            return self.t.numel()
+
+    from context_ring_attention_amd.binding import _req
+    _req(Dev(torch.zeros(4, 8)), "x", (torch.float32,), (4, 8))
+    with pytest.raises(ValueError, match="contiguous"):
+        _req(Dev(torch.zeros(8, 4).t()), "x")
+    with pytest.raises(TypeError, match="dtype"):
+        _req(Dev(torch.zeros(4, 8, dtype=torch.float16)), "x", (torch.float32,))
+    with pytest.raises(ValueError, match="shape"):
+        _req(Dev(torch.zeros(4, 8)), "x", None, (8, 4))
+    with pytest.raises(ValueError, match="elements"):
+        _req(Dev(torch.zeros(4, 8)), "x", numel=33)
+    _req(12345, "raw address")   # plain integers are passed through
