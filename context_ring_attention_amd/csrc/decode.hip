@@ -260,18 +260,34 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
         oacc[db][v] = o;
       }
   }
-  if (!head_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // workspace layout [batch][n_splits][n_h][D]: a workgroup's heads are one contiguous block
-  const int64_t prow = ((int64_t)b * p.n_splits + c) * p.n_h + head;
-  __bf16* wo = static_cast<__bf16*>(p.ws_o) + prow * D;
+  // The partial O of this (request, split, head block) is a [heads][D] bf16 tile, and the
+  // workspace layout [batch][n_splits][n_h][D] makes its valid heads one contiguous block. A lane
+  // holds 4-value pieces of one head's row; stored directly, every instruction would write 16
+  // separate 8-byte pieces. The tile goes through this wave's staging LDS instead (no longer
+  // read; the wave's LDS accesses are in order) and leaves as whole rows, 16 bytes per lane,
+  // each instruction covering 1 KB of consecutive bytes.
+  constexpr int kTStride = D * 2 + 32;  // padded rows: the scattered 8-byte writes spread over banks
+  unsigned char* tile = ks;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) {
     const bf16x4 o4 = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
                        (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
-    *reinterpret_cast<bf16x4*>(wo + db * 16 + 4 * grp) = o4;
+    *reinterpret_cast<bf16x4*>(tile + col * kTStride + (db * 16 + 4 * grp) * 2) = o4;
   }
-  if (grp == 0) p.ws_lse[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  const int n_valid = min(16, p.group - h0);  // heads of this block that exist
+  const int64_t prow0 = ((int64_t)b * p.n_splits + c) * p.n_h + g * p.group + h0;
+  unsigned char* wo = reinterpret_cast<unsigned char*>(static_cast<__bf16*>(p.ws_o) + prow0 * D);
+  constexpr int kLanesPerRow = D * 2 / 16;
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += kRowsPerStore) {
+    const int r = r0 + lane / kLanesPerRow;
+    const int c16 = (lane % kLanesPerRow) * 16;
+    if (r < n_valid)
+      *reinterpret_cast<u32x4*>(wo + r * (D * 2) + c16) = *reinterpret_cast<const u32x4*>(tile + r * kTStride + c16);
+  }
+  if (grp == 0 && head_ok) p.ws_lse[prow0 + col] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
