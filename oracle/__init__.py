@@ -32,13 +32,8 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+def _declare(lib):
+    """Argument and result types of the library's entry points."""
     i32p = ctypes.POINTER(ctypes.c_int32)
     i64p = ctypes.POINTER(ctypes.c_int64)
     f32p = ctypes.POINTER(ctypes.c_float)
@@ -56,8 +51,24 @@ def _load():
     lib.orc_merge.restype = None
     lib.orc_split_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, i64p, i64p]
     lib.orc_split_bounds.restype = None
-    _lib = lib
     return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def use_library(path):
+    """Routes every oracle call through the library at ``path`` (None: back to liboracle.so).
+    Used by the test that plants mistakes in a copy of oracle.c to check the pins catch them."""
+    global _lib
+    _lib = None if path is None else _declare(ctypes.CDLL(path))
 
 
 def _ptr(a: np.ndarray, ctype):

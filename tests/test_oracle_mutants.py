@@ -1,0 +1,98 @@
+"""The oracle's pins are not vacuous: plausible mistakes planted in a copy of oracle.c must each
+fail at least one of them (CPU only).
+
+Each mutant is one textual change of oracle.c (a dropped term, a wrong sign or index, a
+transposed operand, a wrong chunk or split rule), compiled with gcc into a temporary library.
+All oracle calls are routed through it, and the pins of test_oracle.py and
+test_oracle_shard_map.py run unchanged. The replaced text must occur in oracle.c, so a later
+edit of the oracle cannot silently turn a mutant into a no-op. Every mutant keeps all memory
+accesses in bounds.
+"""
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as T
+import test_oracle_shard_map as S
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+MUTANTS = [
+    ("causal mask also hides the query's own key", "k_pos[j] > q_pos[t]", "k_pos[j] >= q_pos[t]"),
+    ("causal mask ignored", "if (causal && k_pos[j] > q_pos[t]) continue;", ""),
+    ("sequence boundaries ignored", "if (k_seq[j] != q_seq[t]) continue;", ""),
+    ("GQA heads interleaved instead of consecutive", "int g = h / group;", "int g = h % n_kv;"),
+    ("softmax scale dropped", "s *= scale;", "s *= 1.0;"),
+    ("LSE without the max", "lse[r * n_h + h] = m + log(l);", "lse[r * n_h + h] = log(l);"),
+    ("output not normalised", "out[d] = acc[d] / l;", "out[d] = acc[d];"),
+    ("values read from K", "acc[d] += w * (double)vv[d];", "acc[d] += w * (double)kv[d];"),
+    ("empty visible set gives LSE 0", "lse[r * n_h + h] = -INFINITY;", "lse[r * n_h + h] = 0.0;"),
+    ("query rows read head-major", "const float* qv = q + (t * n_h + h) * (int64_t)d_h;",
+     "const float* qv = q + (h * tq + t) * (int64_t)d_h;"),
+    ("merge weights not shifted by the max", "double w = exp(lse_parts[i][r] - M);",
+     "double w = exp(lse_parts[i][r]);"),
+    ("merged LSE without the max", "lse[r] = M + log(wsum);", "lse[r] = log(wsum);"),
+    ("merged O not normalised", "o[r * d_h + d] /= wsum;", "o[r * d_h + d] /= 1.0;"),
+    ("second chunk not mirrored", "int64_t picks[2] = {rank, n_chunks - 1 - rank};",
+     "int64_t picks[2] = {rank, rank + cp_world};"),
+    ("mirrored chunk off by one", "int64_t picks[2] = {rank, n_chunks - 1 - rank};",
+     "int64_t picks[2] = {rank, (n_chunks - rank) % n_chunks};"),
+    ("global index ignores earlier sequences", "base[s] = base[s - 1] + seq_len[s - 1];", "base[s] = 0;"),
+    ("decode splits drop the remainder", "*hi = ((int64_t)(c + 1) * len) / n_splits;",
+     "*hi = *lo + len / n_splits;"),
+]
+
+PINS = [
+    ("merge of key partitions", lambda: T.test_merge_of_any_key_partition_equals_unsharded(0)),
+    ("uniform values", T.test_uniform_values_give_that_value_for_every_row_and_shard),
+    ("zero query", T.test_zero_query_gives_running_mean_and_log_count),
+    ("one-hot key a=0.7", lambda: T.test_one_hot_key_closed_form(0.7)),
+    ("one-hot key a=5", lambda: T.test_one_hot_key_closed_form(5.0)),
+    ("first token", T.test_first_token_of_each_sequence_sees_only_itself),
+    ("dense brute force, causal", lambda: T.test_dense_brute_force_agrees(True)),
+    ("dense brute force, full", lambda: T.test_dense_brute_force_agrees(False)),
+    ("GQA grouping", T.test_gqa_consecutive_heads_share_kv_head),
+    ("row subset", T.test_partial_over_rows_subset_matches_full),
+    ("empty set and empty merge", T.test_empty_visible_set_and_merge_of_nothing),
+    ("merge identity and ln 2", T.test_merge_single_part_is_identity_and_two_equal_parts_add_ln2),
+    ("decode splits", T.test_decode_splits_cover_keys_and_merge_exactly),
+    ("golden shard map", S.test_golden_t256_cp4_layout_and_pair_counts),
+    ("ranks partition ranges", lambda: S.test_ranks_partition_every_range_with_balanced_counts(257, 4)),
+    ("equal compute per rank", S.test_equal_compute_per_rank_when_divisible),
+    ("persistent-KV layout", S.test_persistent_kv_layout_per_rank),
+    ("varlen global index", S.test_varlen_batch_global_index_and_segments),
+]
+
+
+def _failing_pins():
+    failed = []
+    for name, pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, RuntimeError, IndexError):
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    oracle.use_library(None)
+    assert _failing_pins() == []
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(what, old, new, tmp_path):
+    src = open(oracle._SRC).read()
+    assert old in src, f"mutant '{what}' no longer applies to oracle.c"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-I", oracle._HERE,
+                    "-o", str(lib), str(mutated), "-lm"], check=True)
+    oracle.use_library(str(lib))
+    try:
+        failed = _failing_pins()
+    finally:
+        oracle.use_library(None)
+    print(f"{what}: caught by {failed}")
+    assert failed, f"no pin catches the planted mistake: {what}"
