@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA clock probe (a separate program) in the device figures")
     return ap.parse_args()
 
 
@@ -204,7 +206,7 @@ def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
             "eager_GBps": round(alg / (eager_ms * 1e-3) / 1e9, 1), "cached_keys": L, "n_splits": S}
 
 
-def device_rooflines(torch):
+def device_rooflines(torch, probe=True):
     """Peaks derived from the device's reported attributes, next to the published figures, and
     the achievable device-to-device copy bandwidth (1 GiB read + 1 GiB written)."""
     import ctypes
@@ -232,7 +234,7 @@ def device_rooflines(torch):
     info["copy_gbs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
     info["published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     del src, dst
-    info["mfma_probe"] = run_mfma_probe()
+    info["mfma_probe"] = run_mfma_probe() if probe else None
     log(f"device: {info}")
     return info
 
@@ -472,7 +474,7 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 1 GiB read, 1 GiB written")
 
-    device_info = device_rooflines(torch) if not args.no_secondary else None
+    device_info = device_rooflines(torch, probe=not args.no_mfma_probe) if not args.no_secondary else None
     probe = (device_info or {}).get("mfma_probe")
     if probe and probe.get("random", {}).get("tflops"):
         # the same kernel rate against what MFMA-only code sustains on random operands
