@@ -295,3 +295,18 @@ def test_decode_batch_over_64():
     # more requests than the kernel ranks by length: units are then taken in request order
     lens = [int(x) for x in np.random.default_rng(7).integers(1, 300, size=70)]
     run_decode(lens, 8, 1, 64, 4, seed=3, check_splits=[0, 3])
+
+
+# --------------------------------------------------------------------------- table and split limits
+def test_bf16_full_segment_tables():
+    # 32 ragged sequences at CP = 1: each owns 2 chunks, so the Q and KV tables hold 64 runs each,
+    # the most one call accepts
+    lens = [int(x) for x in np.random.default_rng(12).integers(2, 150, size=32)]
+    run_pass_kv(lens, 1, 16, 1, 128, "bf16", seed=6, mode="partials")
+
+
+def test_decode_most_splits_and_a_single_split():
+    # 1024 splits (the limit): most splits of the short requests are empty; then one split, where
+    # the merge of a single partial must return it unchanged
+    run_decode([5000, 1023, 1, 2048], 16, 1, 128, 1024, seed=8, check_splits=[0, 1, 511, 1023])
+    run_decode([3000, 1, 777], 8, 1, 64, 1, seed=9, check_splits=[0])
