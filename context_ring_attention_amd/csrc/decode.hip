@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
   const int h0 = (blockIdx.y % hblocks) * 16;
   const int col = lane & 15;  // head column of the 16x16 blocks
   const int grp = lane >> 4;  // 0..3: k slice of the operands, row group of the accumulator
-  const int64_t L = p.kv_len[b];
+  const int64_t L = p.kv_len[b] > 0 ? p.kv_len[b] : 0;  // a negative length reads as an empty cache
   const int64_t base = p.kv_offset[b];
   const int64_t lo = ((int64_t)c * L) / p.n_splits;
   const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;

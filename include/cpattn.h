@@ -132,6 +132,10 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
  *     batch*n_splits*n_h*d_h*2; ws_o 16-byte aligned).
  *   o_out: device [batch, n_h, d_h] in out_dtype; lse_out: device fp32 [batch, n_h] (may be NULL).
  * in_dtype must be CP_BF16. 1 <= n_splits <= 1024.
+ * kv_offset and kv_len live in device memory and are read by the kernels, not checked on the host:
+ * the caller guarantees kv_offset[b] >= 0 and kv_offset[b] + kv_len[b] <= the cache's rows. A
+ * negative kv_len[b] is read as an empty cache (O = 0, LSE = -inf). The workspace holds one call's
+ * partials: calls that share it must be ordered (same stream), not overlap.
  * ------------------------------------------------------------------------------------------- */
 int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,

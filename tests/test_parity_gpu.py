@@ -310,3 +310,26 @@ def test_decode_most_splits_and_a_single_split():
     # the merge of a single partial must return it unchanged
     run_decode([5000, 1023, 1, 2048], 16, 1, 128, 1024, seed=8, check_splits=[0, 1, 511, 1023])
     run_decode([3000, 1, 777], 8, 1, 64, 1, seed=9, check_splits=[0])
+
+
+def test_decode_negative_length_reads_as_empty():
+    from context_ring_attention_amd import binding as cp
+    n_h, d, S, L = 16, 128, 256, 300
+    toks = np.arange(L)
+    kc = device_tensor(10, si.TID_K, toks, (1, d), 1.0, "bf16")
+    vc = device_tensor(10, si.TID_V, toks, (1, d), 1.0, "bf16")
+    q = device_tensor(10, si.TID_Q, np.arange(2), (n_h, d), 1.0, "bf16")
+    offs = torch.tensor([0, 0], dtype=torch.int64, device="cuda")
+    lens = torch.tensor([-7, L], dtype=torch.int64, device="cuda")
+    ws_o, ws_l = cp.decode_workspace(2, n_h, d, S)
+    o = torch.full((2, n_h, d), float("nan"), device="cuda")
+    lse = torch.empty(2, n_h, device="cuda")
+    cp.decode_splitkv(q, kc, vc, offs, lens, S, scale_of(d), ws_o, ws_l, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    qf = oracle_view(10, si.TID_Q, np.arange(2), (n_h, d), 1.0, "bf16")
+    kf = oracle_view(10, si.TID_K, toks, (1, d), 1.0, "bf16")
+    vf = oracle_view(10, si.TID_V, toks, (1, d), 1.0, "bf16")
+    o_ref, l_ref = oracle.attention(qf[1:2], kf, vf, n_h, 1, np.zeros(1, np.int32), np.array([L]),
+                                    np.zeros(L, np.int32), np.arange(L), False, scale_of(d))
+    assert_close(o[1:2], lse[1:2], o_ref, l_ref, "bf16", "request after an empty one")
