@@ -356,7 +356,20 @@ def run_cpu_baseline(si, ranges, N, n_h, n_kv, d, seed, budget_s):
     log(f"oracle: {done} query tokens in {spent:.1f}s on {oracle.num_threads()} threads, {tf * 1e3:.2f} GFLOP/s")
     return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} random query tokens (x{n_h} heads) of rank 0's 32K-token Q shard of "
-                      f"prefill_128k_cp4, each against its full visible key set; {spent:.1f} s of fp64 work"}
+                      f"prefill_128k_cp4, each against its full visible key set; {spent:.1f} s of fp64 work",
+            "host": {"cpu_model": host_cpu_model(), "logical_cpus": os.cpu_count()}}
+
+
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not available)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # --------------------------------------------------------------------------- main
