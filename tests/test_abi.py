@@ -269,3 +269,22 @@ def test_binding_checks_layout_dtype_and_shape():
     with pytest.raises(ValueError, match="elements"):
         _req(Dev(torch.zeros(4, 8)), "x", numel=33)
     _req(12345, "raw address")   # plain integers are passed through
+
+
+def test_c_program_uses_the_abi_without_python(tmp_path):
+    """include/cpattn.h is valid standalone C11, and a plain C program linked against
+    libcpattn.so gets the documented host-side behaviour (tests/c_abi_check.c). No GPU needed."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(cp.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), src, "-o", exe, "-L", lib_dir, "-lcpattn",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "ok"
