@@ -123,8 +123,8 @@ def _req(t, name: str, dtypes=None, shape=None, numel=None):
     """Checks what the C ABI cannot see behind a raw pointer: a tensor argument must be a
     contiguous device tensor of the expected dtype and shape. (A host tensor's address handed to a
     kernel would fault the GPU; a strided view would be read with the wrong layout.) Plain integer
-    addresses are passed through unchecked."""
-    if t is None or isinstance(t, int):
+    addresses are passed through unchecked. Kept to a few attribute reads: it runs on every call."""
+    if t is None or type(t) is int:
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (got {t.device})")
@@ -132,20 +132,30 @@ def _req(t, name: str, dtypes=None, shape=None, numel=None):
         raise ValueError(f"{name} must be contiguous")
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
+_DT = {}
+
+
+def _types(key):
+    """dtype tuples used by the checks (built once; torch is imported lazily)."""
+    if not _DT:
+        import torch
+        _DT.update(f32=(torch.float32,), bf16=(torch.bfloat16,), i64=(torch.int64,),
+                   inp=(torch.float32, torch.bfloat16))
+    return _DT[key]
+
+
 def _float_types():
-    import torch
-    return (torch.float32,)
+    return _types("f32")
 
 
 def _in_types():
-    import torch
-    return (torch.float32, torch.bfloat16)
+    return _types("inp")
 
 
 def _stream(stream) -> Optional[int]:
@@ -212,24 +222,25 @@ def shard_map(ranges, cp_world: int, rank: int, with_tokens: bool = True):
 
 
 def partial_attn(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: float, o, lse,
-                 accumulate: bool = False, stream=None):
+                 accumulate: bool = False, stream=None, check: bool = True):
     """cp_partial_attn. q: [tq, n_h, d], k/v: [tk, n_kv, d] (same dtype), o fp32, lse fp32."""
     lib = load()
     qa, nq = _segarg(q_segs)
     ka, nk = _segarg(kv_segs)
     tq, n_h, d = q.shape
     tk, n_kv = k.shape[0], k.shape[1]
-    _req(q, "q", _in_types())
-    _req(k, "k", (q.dtype,), (tk, n_kv, d))
-    _req(v, "v", (q.dtype,), (tk, n_kv, d))
-    _req(o, "o", _float_types(), (tq, n_h, d))
-    _req(lse, "lse", _float_types(), numel=tq * n_h)
+    if check:
+        _req(q, "q", _in_types())
+        _req(k, "k", (q.dtype,), (tk, n_kv, d))
+        _req(v, "v", (q.dtype,), (tk, n_kv, d))
+        _req(o, "o", _float_types(), (tq, n_h, d))
+        _req(lse, "lse", _float_types(), numel=tq * n_h)
     _check(lib.cp_partial_attn(_ptr(q), _ptr(k), _ptr(v), tq, tk, n_h, n_kv, d, _dtype_code(q),
                                qa, nq, ka, nk, int(causal), float(softmax_scale), _ptr(o), _ptr(lse),
                                int(accumulate), _stream(stream)))
 
 
-def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None):
+def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None, check: bool = True):
     """cp_merge_lse over fp32 parts [rows, d] (any shape whose last dim is d)."""
     lib = load()
     n = len(o_parts)
@@ -237,11 +248,12 @@ def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None):
     rows = o_parts[0].numel() // d
     if len(lse_parts) != n:
         raise ValueError(f"{n} O parts but {len(lse_parts)} LSE parts")
-    for i in range(n):
-        _req(o_parts[i], f"o_parts[{i}]", _float_types(), numel=rows * d)
-        _req(lse_parts[i], f"lse_parts[{i}]", _float_types(), numel=rows)
-    _req(o_out, "o_out", _in_types(), numel=rows * d)
-    _req(lse_out, "lse_out", _float_types(), numel=rows)
+    if check:
+        for i in range(n):
+            _req(o_parts[i], f"o_parts[{i}]", _float_types(), numel=rows * d)
+            _req(lse_parts[i], f"lse_parts[{i}]", _float_types(), numel=rows)
+        _req(o_out, "o_out", _in_types(), numel=rows * d)
+        _req(lse_out, "lse_out", _float_types(), numel=rows)
     op = (ctypes.c_void_p * n)(*[_ptr(t) for t in o_parts])
     lp = (ctypes.c_void_p * n)(*[_ptr(t) for t in lse_parts])
     _check(lib.cp_merge_lse(n, op, lp, rows, d, _ptr(o_out), _dtype_code(o_out), _ptr(lse_out),
@@ -265,23 +277,27 @@ def decode_workspace(batch: int, n_h: int, d_h: int, n_splits: int, device="cuda
 
 
 def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softmax_scale: float,
-                   ws_o, ws_lse, o_out, lse_out=None, stream=None):
-    """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device."""
+                   ws_o, ws_lse, o_out, lse_out=None, stream=None, check: bool = True):
+    """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device.
+
+    check=False skips the tensor checks (about 3 us of host time per call): for loops whose
+    tensors were validated on an earlier call."""
     lib = load()
-    import torch
     B, n_h, d = q.shape
     n_kv = k_cache.shape[1]
-    _req(q, "q", (torch.bfloat16,))
-    _req(k_cache, "k_cache", (torch.bfloat16,))
-    _req(v_cache, "v_cache", (torch.bfloat16,), tuple(k_cache.shape))
-    if k_cache.dim() != 3 or k_cache.shape[2] != d:
-        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected [tokens, n_kv, {d}]")
-    _req(kv_offset, "kv_offset", (torch.int64,), (B,))
-    _req(kv_len, "kv_len", (torch.int64,), (B,))
-    _req(ws_o, "ws_o", (torch.bfloat16,), numel=B * n_splits * n_h * d)
-    _req(ws_lse, "ws_lse", _float_types(), numel=B * n_splits * n_h)
-    _req(o_out, "o_out", _in_types(), (B, n_h, d))
-    _req(lse_out, "lse_out", _float_types(), numel=B * n_h)
+    if check:
+        bf16, i64, f32 = _types("bf16"), _types("i64"), _types("f32")
+        _req(q, "q", bf16)
+        _req(k_cache, "k_cache", bf16)
+        _req(v_cache, "v_cache", bf16, k_cache.shape)
+        if k_cache.dim() != 3 or k_cache.shape[2] != d:
+            raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected [tokens, n_kv, {d}]")
+        _req(kv_offset, "kv_offset", i64, (B,))
+        _req(kv_len, "kv_len", i64, (B,))
+        _req(ws_o, "ws_o", bf16, numel=B * n_splits * n_h * d)
+        _req(ws_lse, "ws_lse", f32, numel=B * n_splits * n_h)
+        _req(o_out, "o_out", _types("inp"), (B, n_h, d))
+        _req(lse_out, "lse_out", f32, numel=B * n_h)
     _check(lib.cp_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
                                  _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
                                  float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
@@ -290,7 +306,7 @@ def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softma
 
 def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,
                  softmax_scale: float, o_out, lse_out=None, o_parts=None, lse_parts=None,
-                 o_acc=None, lse_acc=None, stream=None):
+                 o_acc=None, lse_acc=None, stream=None, check: bool = True):
     """cp_ring_pass_kv for one rank. k_shards/v_shards/kv_segs: per shard id."""
     lib = load()
     N = len(k_shards)
@@ -299,22 +315,23 @@ def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool
     n_kv = k_shards[0].shape[1]
     if len(v_shards) != N or len(kv_segs) != N:
         raise ValueError("k_shards, v_shards and kv_segs must have one entry per shard")
-    _req(q, "q", _in_types())
-    for i in range(N):
-        _req(k_shards[i], f"k_shards[{i}]", (q.dtype,))
-        _req(v_shards[i], f"v_shards[{i}]", (q.dtype,), tuple(k_shards[i].shape))
-        if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
-            raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
-    for name, parts, shp in (("o_parts", o_parts, (tq, n_h, d)), ("lse_parts", lse_parts, None)):
-        if parts is not None:
-            if len(parts) != N:
-                raise ValueError(f"{name} must have {N} entries")
-            for i, t in enumerate(parts):
-                _req(t, f"{name}[{i}]", _float_types(), shp, None if shp else tq * n_h)
-    _req(o_acc, "o_acc", _float_types(), (tq, n_h, d))
-    _req(lse_acc, "lse_acc", _float_types(), numel=tq * n_h)
-    _req(o_out, "o_out", _in_types(), (tq, n_h, d))
-    _req(lse_out, "lse_out", _float_types(), numel=tq * n_h)
+    if check:
+        _req(q, "q", _in_types())
+        for i in range(N):
+            _req(k_shards[i], f"k_shards[{i}]", (q.dtype,))
+            _req(v_shards[i], f"v_shards[{i}]", (q.dtype,), tuple(k_shards[i].shape))
+            if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
+                raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
+        for name, parts, shp in (("o_parts", o_parts, (tq, n_h, d)), ("lse_parts", lse_parts, None)):
+            if parts is not None:
+                if len(parts) != N:
+                    raise ValueError(f"{name} must have {N} entries")
+                for i, t in enumerate(parts):
+                    _req(t, f"{name}[{i}]", _float_types(), shp, None if shp else tq * n_h)
+        _req(o_acc, "o_acc", _float_types(), (tq, n_h, d))
+        _req(lse_acc, "lse_acc", _float_types(), numel=tq * n_h)
+        _req(o_out, "o_out", _in_types(), (tq, n_h, d))
+        _req(lse_out, "lse_out", _float_types(), numel=tq * n_h)
     vp = ctypes.c_void_p
     segp = ctypes.POINTER(CpSegment)
     ks = (vp * N)(*[_ptr(t) for t in k_shards])
@@ -345,7 +362,7 @@ def select_ring_variant(new_tokens: int, cached_tokens: int, cp_world: int, n_h:
 
 
 def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, softmax_scale: float,
-                o_parts, lse_parts, o_out, lse_out=None, stream=None):
+                o_parts, lse_parts, o_out, lse_out=None, stream=None, check: bool = True):
     """cp_ring_pass_q over all ranks. o_parts/lse_parts: N*N buffers, slot q*N + s."""
     lib = load()
     N = len(q_shards)
@@ -357,22 +374,23 @@ def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, sof
         raise ValueError("q_shards, q_segs, k_shards, v_shards, kv_segs and o_out need one entry per rank")
     if len(o_parts) != N * N or len(lse_parts) != N * N:
         raise ValueError(f"o_parts and lse_parts need {N * N} entries (slot q*N + s)")
-    dt = q_shards[0].dtype
-    for i in range(N):
-        _req(q_shards[i], f"q_shards[{i}]", (dt,))
-        if q_shards[i].dim() != 3 or tuple(q_shards[i].shape[1:]) != (n_h, d):
-            raise ValueError(f"q_shards[{i}] has shape {tuple(q_shards[i].shape)}, expected [tokens, {n_h}, {d}]")
-        _req(k_shards[i], f"k_shards[{i}]", (dt,))
-        _req(v_shards[i], f"v_shards[{i}]", (dt,), tuple(k_shards[i].shape))
-        if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
-            raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
-        tqi = q_shards[i].shape[0]
-        _req(o_out[i], f"o_out[{i}]", _in_types(), (tqi, n_h, d))
-        if lse_out is not None:
-            _req(lse_out[i], f"lse_out[{i}]", _float_types(), numel=tqi * n_h)
-        for s_ in range(N):
-            _req(o_parts[i * N + s_], f"o_parts[{i * N + s_}]", _float_types(), (tqi, n_h, d))
-            _req(lse_parts[i * N + s_], f"lse_parts[{i * N + s_}]", _float_types(), numel=tqi * n_h)
+    if check:
+        dt = q_shards[0].dtype
+        for i in range(N):
+            _req(q_shards[i], f"q_shards[{i}]", (dt,))
+            if q_shards[i].dim() != 3 or tuple(q_shards[i].shape[1:]) != (n_h, d):
+                raise ValueError(f"q_shards[{i}] has shape {tuple(q_shards[i].shape)}, expected [tokens, {n_h}, {d}]")
+            _req(k_shards[i], f"k_shards[{i}]", (dt,))
+            _req(v_shards[i], f"v_shards[{i}]", (dt,), tuple(k_shards[i].shape))
+            if k_shards[i].dim() != 3 or tuple(k_shards[i].shape[1:]) != (n_kv, d):
+                raise ValueError(f"k_shards[{i}] has shape {tuple(k_shards[i].shape)}, expected [tokens, {n_kv}, {d}]")
+            tqi = q_shards[i].shape[0]
+            _req(o_out[i], f"o_out[{i}]", _in_types(), (tqi, n_h, d))
+            if lse_out is not None:
+                _req(lse_out[i], f"lse_out[{i}]", _float_types(), numel=tqi * n_h)
+            for s_ in range(N):
+                _req(o_parts[i * N + s_], f"o_parts[{i * N + s_}]", _float_types(), (tqi, n_h, d))
+                _req(lse_parts[i * N + s_], f"lse_parts[{i * N + s_}]", _float_types(), numel=tqi * n_h)
     qs = (vp * N)(*[_ptr(t) for t in q_shards])
     tq = (ctypes.c_int64 * N)(*[t.shape[0] for t in q_shards])
     qseg_objs = [_segarg(s) for s in q_segs]

@@ -288,3 +288,18 @@ def test_c_program_uses_the_abi_without_python(tmp_path):
     res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip() == "ok"
+
+
+def test_binding_check_false_skips_only_the_tensor_checks():
+    """check=False passes tensors straight to the library (for loops that validated them once);
+    the library's own validation still runs and reports through CpError."""
+    import torch
+    q = torch.zeros(16, 6, 64, dtype=torch.bfloat16)   # 6 heads over 4 KV heads: invalid shape
+    k = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
+    o = torch.zeros(16, 6, 64)
+    lse = torch.zeros(16, 6)
+    segs = [(0, 0, 16, 0)]
+    with pytest.raises(ValueError, match="device tensor"):
+        cp.partial_attn(q, k, k, segs, segs, True, 0.125, o, lse)
+    with pytest.raises(cp.CpError, match="CP_E_SHAPE"):
+        cp.partial_attn(q, k, k, segs, segs, True, 0.125, o, lse, stream=0, check=False)
