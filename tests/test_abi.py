@@ -303,3 +303,38 @@ def test_binding_check_false_skips_only_the_tensor_checks():
         cp.partial_attn(q, k, k, segs, segs, True, 0.125, o, lse)
     with pytest.raises(cp.CpError, match="CP_E_SHAPE"):
         cp.partial_attn(q, k, k, segs, segs, True, 0.125, o, lse, stream=0, check=False)
+
+
+def test_product_and_oracle_share_no_code():
+    """The HIP path never imports, includes or loads the oracle, and the oracle never refers to
+    the HIP path except in its header comments (which say it does not)."""
+    import glob
+    prod = [f for ext in ("py", "hip", "cpp", "h") for f in
+            glob.glob(os.path.join(ROOT, "context_ring_attention_amd", "**", f"*.{ext}"), recursive=True)]
+    prod += glob.glob(os.path.join(ROOT, "include", "*.h"))
+    assert prod
+    for f in prod:
+        text = open(f).read()
+        assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b|#include\s*[<\"][^>\"]*oracle|liboracle",
+                             text), f
+    for f in glob.glob(os.path.join(ROOT, "oracle", "*.[ch]")) + glob.glob(os.path.join(ROOT, "oracle", "*.py")):
+        code = re.sub(r"/\*.*?\*/", "", open(f).read(), flags=re.S)       # C comments
+        code = re.sub(r'""".*?"""', "", code, flags=re.S)                   # Python docstrings
+        code = "\n".join(l.split("#", 1)[0] if f.endswith(".py") else l for l in code.splitlines())
+        assert "context_ring_attention_amd" not in code and "cpattn" not in code, f
+
+
+def test_bench_uses_the_oracle_only_for_its_cpu_baseline():
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    users = set()
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            for node in ast.walk(fn):
+                if isinstance(node, ast.Import) and any(a.name == "oracle" for a in node.names):
+                    users.add(fn.name)
+                if isinstance(node, ast.ImportFrom) and node.module == "oracle":
+                    users.add(fn.name)
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))
+           and ("oracle" in [a.name for a in n.names] or getattr(n, "module", None) == "oracle")]
+    assert not top and users == {"run_cpu_baseline"}, (top, users)
