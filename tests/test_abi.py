@@ -338,3 +338,16 @@ def test_bench_uses_the_oracle_only_for_its_cpu_baseline():
     top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))
            and ("oracle" in [a.name for a in n.names] or getattr(n, "module", None) == "oracle")]
     assert not top and users == {"run_cpu_baseline"}, (top, users)
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No silent fallback: with libcpattn.so absent, loading (and so every entry point) raises."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("cpattn_binding_copy", cp.__file__)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.LIB_PATH = os.path.join(ROOT, "no_such_dir", "libcpattn.so")
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        mod.load()
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        mod.shard_map([(0, 0, 16)], 2, 0)
