@@ -333,3 +333,16 @@ def test_decode_negative_length_reads_as_empty():
     o_ref, l_ref = oracle.attention(qf[1:2], kf, vf, n_h, 1, np.zeros(1, np.int32), np.array([L]),
                                     np.zeros(L, np.int32), np.arange(L), False, scale_of(d))
     assert_close(o[1:2], lse[1:2], o_ref, l_ref, "bf16", "request after an empty one")
+
+
+def test_bf16_group_sizes_that_straddle_tiles():
+    # row = token * G + head: with G = 3 or 5 a 256-row workgroup tile starts and ends inside a
+    # token's heads; G = 32 puts 8 tokens in a tile
+    run_pass_kv([700, 333], 2, 21, 7, 128, "bf16", seed=11, mode="partials")
+    run_pass_kv([900], 3, 10, 2, 64, "bf16", seed=12, mode="running", ranks=[1])
+    run_pass_kv([513, 64], 2, 64, 2, 128, "bf16", seed=13, mode="partials", ranks=[0])
+
+
+def test_decode_group_sizes_that_straddle_head_blocks():
+    run_decode([1500, 37, 0], 21, 7, 128, 256, seed=14, check_splits=[0, 255])
+    run_decode([800, 2049], 10, 2, 64, 32, seed=15, out="bf16", check_splits=[5])
