@@ -412,6 +412,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(const AttnParams 
       step(StageIdx<3>{}, sb, sa);
       if (--left == 0) break;
     }
+    // The last step issued loads of a tile past the end (unused). Retire them here rather than
+    // leave them to the end of the program, so no LDS write is pending once the waves finish.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 #undef CP_TILE_DMA
 
