@@ -111,7 +111,9 @@ int cp_partial_attn(const void* q, const void* k, const void* v, int64_t tq, int
  *   o_parts, lse_parts: host arrays of n_parts (1..CP_MAX_MERGE_PARTS) device pointers to fp32
  *     [rows, d_h] and [rows]. rows = T_q * N_H.
  *   o_out: device [rows, d_h] in out_dtype (fp32 or bf16, round to nearest even);
- *   lse_out: device fp32 [rows] (may be NULL). o_out may alias o_parts[0] when out_dtype is fp32.
+ *   lse_out: device fp32 [rows] (may be NULL). Merging in place is allowed: o_out may alias a part's
+ *     O when out_dtype is fp32, and lse_out may alias a part's LSE (each row is read before it is
+ *     written, by the same wave).
  * ------------------------------------------------------------------------------------------- */
 int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                  int64_t rows, int d_h, void* o_out, cp_dtype out_dtype, float* lse_out,
