@@ -224,10 +224,14 @@ def test_merge_in_place_fp32():
     o, lse = si.random_partials(3, 4, 300, 128)
     o_dev = [o[i].contiguous().cuda() for i in range(4)]
     l_dev = [lse[i].contiguous().cuda() for i in range(4)]
-    cp.merge_lse(o_dev, l_dev, o_dev[0], None)
+    cp.merge_lse(o_dev, l_dev, o_dev[0], l_dev[0])   # O and LSE both merged in place
     torch.cuda.synchronize()
-    o_ref, _ = oracle.merge([o[i].double().numpy() for i in range(4)], [lse[i].double().numpy() for i in range(4)])
+    o_ref, l_ref = oracle.merge([o[i].double().numpy() for i in range(4)], [lse[i].double().numpy() for i in range(4)])
     assert np.max(np.abs(o_dev[0].cpu().numpy() - o_ref)) <= 1e-5
+    l_g = l_dev[0].cpu().numpy()
+    assert np.array_equal(np.isneginf(l_g), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(l_g[fin] - l_ref[fin])) <= 1e-5
 
 
 # --------------------------------------------------------------------------- decode
