@@ -351,3 +351,34 @@ def test_binding_fails_loudly_without_the_library():
         mod.load()
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         mod.shard_map([(0, 0, 16)], 2, 0)
+
+
+def test_c_abi_host_code_under_address_sanitizer(tmp_path):
+    """The C ABI's host code (api.cpp) built with AddressSanitizer, the kernel launchers replaced
+    by stubs that abort, driven by tests/c_abi_check.c: shard map, validation and selector paths
+    must run without any ASan report. Host code only; no device code is built."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    csrc = os.path.join(ROOT, "context_ring_attention_amd", "csrc")
+    lib = str(tmp_path / "libcpattn.so")
+    san = ["-Xarch_host", "-fsanitize=address", "-fno-omit-frame-pointer", "-g"]
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    subprocess.run([hipcc, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+                    "-std=c++17", "-O1", "-fPIC", "-shared", *san,
+                    "-I", os.path.join(ROOT, "include"), "-I", csrc,
+                    os.path.join(csrc, "api.cpp"), os.path.join(ROOT, "tests", "host_launch_stubs.cpp"),
+                    "-o", lib], check=True, capture_output=True)
+    exe = str(tmp_path / "c_abi_check_asan")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")   # the same sanitizer runtime as the library
+    if not os.path.exists(clang):
+        pytest.skip("ROCm clang not available")
+    subprocess.run([clang, "-std=c11", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_check.c"),
+                    "-o", exe, "-L", str(tmp_path), "-lcpattn", f"-Wl,-rpath,{tmp_path}"], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert res.returncode == 0 and "ERROR: AddressSanitizer" not in res.stderr, res.stderr[-2000:]
+    assert res.stdout.strip() == "ok"
