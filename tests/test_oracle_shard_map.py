@@ -107,3 +107,40 @@ def test_varlen_batch_global_index_and_segments():
             expect = np.r_[np.arange(r * C, (r + 1) * C), np.arange((2 * N - 1 - r) * C, (2 * N - r) * C)]
             assert np.array_equal(pos[seq == i], expect)
     assert sizes == [131072] * 3
+
+
+# ------------------------------------------------------------------------ property-based, vs the library
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def _batches(draw):
+    n_seq = draw(st.integers(1, 5))
+    ids = draw(st.permutations(list(range(n_seq + draw(st.integers(0, 2))))))[:n_seq]
+    ranges = []
+    for sid in ids:
+        L = draw(st.integers(0, 3000))
+        if draw(st.booleans()) and L > 1:          # a cached prefix and new tokens, as two ranges
+            P = draw(st.integers(1, L - 1))
+            ranges += [(sid, 0, P), (sid, P, L)]
+        else:
+            ranges.append((sid, 0, L))
+    return ranges, draw(st.integers(1, 8))
+
+
+@settings(max_examples=150, deadline=None)
+@given(_batches())
+def test_library_shard_map_matches_oracle_for_random_batches(batch):
+    from context_ring_attention_amd import binding as cp
+    ranges, N = batch
+    seen = []
+    for r in range(N):
+        segs, toks = cp.shard_map(ranges, N, r)
+        seq, pos, glob = oracle.shard_tokens(ranges, N, r)
+        lib_seq = np.concatenate([np.full(n, s, np.int64) for s, _, n, _ in segs]) if segs else np.zeros(0, np.int64)
+        lib_pos = np.concatenate([np.arange(p, p + n) for _, p, n, _ in segs]) if segs else np.zeros(0, np.int64)
+        assert np.array_equal(lib_seq, seq) and np.array_equal(lib_pos, pos)
+        assert np.array_equal(toks, glob)
+        seen.append(glob)
+    allg = np.concatenate(seen) if seen else np.zeros(0, np.int64)
+    assert len(np.unique(allg)) == len(allg)      # no token owned twice
