@@ -51,6 +51,9 @@ def _declare(lib):
     lib.orc_merge.restype = None
     lib.orc_split_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, i64p, i64p]
     lib.orc_split_bounds.restype = None
+    for name in ("orc_pass_kv_shard", "orc_pass_q_query", "orc_pass_q_slot"):
+        getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        getattr(lib, name).restype = ctypes.c_int
     return lib
 
 
@@ -179,3 +182,25 @@ def split_bounds(length: int, n_splits: int):
         lib.orc_split_bounds(length, n_splits, c, ctypes.byref(lo), ctypes.byref(hi))
         out.append((lo.value, hi.value))
     return out
+
+
+def _ring(name, *args) -> int:
+    v = getattr(_load(), name)(*[int(a) for a in args])
+    if v < 0:
+        raise ValueError(f"{name}{args}: bad arguments")
+    return v
+
+
+def pass_kv_shard(cp_world: int, rank: int, step: int) -> int:
+    """KV shard held by ``rank`` at ring Pass-KV step ``step``."""
+    return _ring("orc_pass_kv_shard", cp_world, rank, step)
+
+
+def pass_q_query(cp_world: int, kv_shard: int, step: int) -> int:
+    """Q shard hosted by the owner of ``kv_shard`` at ring Pass-Q step ``step``."""
+    return _ring("orc_pass_q_query", cp_world, kv_shard, step)
+
+
+def pass_q_slot(cp_world: int, q_shard: int, kv_shard: int) -> int:
+    """Storage slot of the Pass-Q partial of ``q_shard`` against ``kv_shard``."""
+    return _ring("orc_pass_q_slot", cp_world, q_shard, kv_shard)

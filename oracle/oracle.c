@@ -214,3 +214,32 @@ void orc_split_bounds(int64_t len, int n_splits, int c, int64_t* lo, int64_t* hi
   *lo = ((int64_t)c * len) / n_splits;
   *hi = ((int64_t)(c + 1) * len) / n_splits;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Ring schedules.  [CPMTI §3 "核心公式", Fig. 3]: in ring Pass-KV each rank keeps its Q shard while
+ * the KV shards travel around the ring of N ranks for N-1 rounds; in ring Pass-Q the KV shards
+ * stay on their ranks, the Q shards travel, and an All2All then returns every partial result to
+ * the rank that owns its Q shard, where the partials are merged.
+ * Readings (the page fixes neither the direction nor the storage order; O and LSE do not depend
+ * on them): a shard moves from rank r to rank r+1 at every step, so at step t
+ *   - Pass-KV: rank r holds the KV shard that started on rank (r - t) mod N;
+ *   - Pass-Q: the rank that owns KV shard s hosts the Q shard that started on rank (s - t) mod N;
+ * and the partial of Q shard q against KV shard s is stored in slot q*N + s.
+ * ------------------------------------------------------------------------------------------ */
+static int ring_mod(int a, int n) { return ((a % n) + n) % n; }
+
+int orc_pass_kv_shard(int cp_world, int rank, int step) {
+  if (cp_world < 1 || rank < 0 || rank >= cp_world || step < 0) return -1;
+  return ring_mod(rank - step, cp_world);
+}
+
+int orc_pass_q_query(int cp_world, int kv_shard, int step) {
+  if (cp_world < 1 || kv_shard < 0 || kv_shard >= cp_world || step < 0) return -1;
+  return ring_mod(kv_shard - step, cp_world);
+}
+
+int orc_pass_q_slot(int cp_world, int q_shard, int kv_shard) {
+  if (cp_world < 1 || q_shard < 0 || q_shard >= cp_world || kv_shard < 0 || kv_shard >= cp_world)
+    return -1;
+  return q_shard * cp_world + kv_shard;
+}

@@ -35,6 +35,13 @@ void orc_merge(int n_parts, const double* const* o_parts, const double* const* l
 /* Key range [lo, hi) of decode split c out of n_splits for a request with len cached keys. */
 void orc_split_bounds(int64_t len, int n_splits, int c, int64_t* lo, int64_t* hi);
 
+/* Ring schedules: KV shard rank `rank` holds at Pass-KV step `step`; Q shard hosted by the owner of
+   KV shard `kv_shard` at Pass-Q step `step`; storage slot of the partial (q_shard, kv_shard).
+   Each returns -1 on bad arguments. */
+int orc_pass_kv_shard(int cp_world, int rank, int step);
+int orc_pass_q_query(int cp_world, int kv_shard, int step);
+int orc_pass_q_slot(int cp_world, int q_shard, int kv_shard);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,14 @@ def test_decode_splits_cover_keys_and_merge_exactly():
     # a split with fewer keys than splits: empty splits merge away
     b2 = oracle.split_bounds(5, 8)
     assert sum(hi - lo for lo, hi in b2) == 5 and sum(hi == lo for lo, hi in b2) == 3
+
+
+def test_decode_split_table_golden_l300_s32():
+    """Hand-worked split table of a length the split count does not divide (L=300, S=32):
+    tests/golden/decode_splits_l300_s32.txt."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "decode_splits_l300_s32.txt")
+    rows = [tuple(int(x) for x in line.split()) for line in open(path)
+            if line.strip() and not line.startswith("#")]
+    assert [c for c, _, _ in rows] == list(range(32))
+    assert oracle.split_bounds(300, 32) == [(lo, hi) for _, lo, hi in rows]

@@ -41,6 +41,20 @@ MUTANTS = [
     ("global index ignores earlier sequences", "base[s] = base[s - 1] + seq_len[s - 1];", "base[s] = 0;"),
     ("decode splits drop the remainder", "*hi = ((int64_t)(c + 1) * len) / n_splits;",
      "*hi = *lo + len / n_splits;"),
+    ("decode split edges rounded up",
+     "*lo = ((int64_t)c * len) / n_splits;\n  *hi = ((int64_t)(c + 1) * len) / n_splits;",
+     "*lo = ((int64_t)c * len + n_splits - 1) / n_splits;\n"
+     "  *hi = ((int64_t)(c + 1) * len + n_splits - 1) / n_splits;"),
+    ("chunk edges rounded up",
+     "int64_t lo = a + (c * len) / n_chunks;\n      int64_t hi = a + ((c + 1) * len) / n_chunks;",
+     "int64_t lo = a + (c * len + n_chunks - 1) / n_chunks;\n"
+     "      int64_t hi = a + ((c + 1) * len + n_chunks - 1) / n_chunks;"),
+    ("Pass-KV ring runs backwards", "return ring_mod(rank - step, cp_world);",
+     "return ring_mod(rank + step, cp_world);"),
+    ("Pass-Q hosts the KV shard's own Q at every step", "return ring_mod(kv_shard - step, cp_world);",
+     "return kv_shard;"),
+    ("Pass-Q slots transposed", "return q_shard * cp_world + kv_shard;",
+     "return kv_shard * cp_world + q_shard;"),
 ]
 
 PINS = [
@@ -57,7 +71,11 @@ PINS = [
     ("empty set and empty merge", T.test_empty_visible_set_and_merge_of_nothing),
     ("merge identity and ln 2", T.test_merge_single_part_is_identity_and_two_equal_parts_add_ln2),
     ("decode splits", T.test_decode_splits_cover_keys_and_merge_exactly),
+    ("golden decode split table", T.test_decode_split_table_golden_l300_s32),
     ("golden shard map", S.test_golden_t256_cp4_layout_and_pair_counts),
+    ("golden shard map, T=257", S.test_golden_t257_cp4_floor_edges_and_pair_counts),
+    ("golden ring schedules", S.test_golden_ring_schedules_cp4),
+    ("rings, N=5", lambda: S.test_ring_schedules_are_rings(5)),
     ("ranks partition ranges", lambda: S.test_ranks_partition_every_range_with_balanced_counts(257, 4)),
     ("equal compute per rank", S.test_equal_compute_per_rank_when_divisible),
     ("persistent-KV layout", S.test_persistent_kv_layout_per_rank),

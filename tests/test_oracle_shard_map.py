@@ -12,15 +12,16 @@ import pytest
 
 import oracle
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shard_map_t256_cp4.txt")
+GOLDEN_DIR = os.path.join(os.path.dirname(__file__), "golden")
+GOLDEN = os.path.join(GOLDEN_DIR, "shard_map_t256_cp4.txt")
 
 
-def _golden():
+def _golden(path=GOLDEN):
     rows = []
-    with open(GOLDEN) as f:
+    with open(path) as f:
         for line in f:
             if line.strip() and not line.startswith("#"):
-                rows.append([int(x) for x in line.split()])
+                rows.append([int(x) if x.lstrip("-").isdigit() else x for x in line.split()])
     return rows
 
 
@@ -34,10 +35,10 @@ def _visible_pairs(q_seq, q_pos, k_seq, k_pos):
     return total
 
 
-def test_golden_t256_cp4_layout_and_pair_counts():
-    gold = _golden()
-    N = 4
-    shards = [oracle.shard_tokens([(0, 0, 256)], N, r) for r in range(N)]
+def _check_golden_layout(path, T, N):
+    gold = _golden(path)
+    shards = [oracle.shard_tokens([(0, 0, T)], N, r) for r in range(N)]
+    assert sorted(row[0] for row in gold) == list(range(N))
     for row in gold:
         r = row[0]
         seq, pos, glob = shards[r]
@@ -47,11 +48,55 @@ def test_golden_t256_cp4_layout_and_pair_counts():
         assert np.all(seq == 0)
         counts = []
         for t in range(N):
-            s = (r - t) % N
+            s = oracle.pass_kv_shard(N, r, t)
             ks, kp, _ = shards[s]
             counts.append(_visible_pairs(seq, pos, ks, kp))
         assert counts == row[5:9]
         assert sum(counts) == row[9]
+
+
+def test_golden_t256_cp4_layout_and_pair_counts():
+    _check_golden_layout(GOLDEN, 256, 4)
+
+
+def test_golden_t257_cp4_floor_edges_and_pair_counts():
+    """A length 2N does not divide: the hand-worked floor edges put the odd token in chunk 7."""
+    _check_golden_layout(os.path.join(GOLDEN_DIR, "shard_map_t257_cp4.txt"), 257, 4)
+
+
+def test_golden_ring_schedules_cp4():
+    """Pass-KV and Pass-Q step tables and Pass-Q slots against the hand-written golden table."""
+    N = 4
+    for row in _golden(os.path.join(GOLDEN_DIR, "ring_schedule_cp4.txt")):
+        kind, who, steps = row[0], row[1], row[2:2 + N]
+        if kind == "pass_kv":
+            assert [oracle.pass_kv_shard(N, who, t) for t in range(N)] == steps
+        else:
+            assert [oracle.pass_q_query(N, who, t) for t in range(N)] == steps
+            assert [oracle.pass_q_slot(N, q, who) for q in steps] == row[2 + N:]
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 16])
+def test_ring_schedules_are_rings(N):
+    """What the ring itself fixes, for any world size: every rank starts on its own shard, a shard
+    held by rank r at step t is held by rank r+1 at step t+1 (it travels one hop per step), and over
+    N steps every rank meets every shard once. Pass-Q slots are a bijection onto [0, N^2)."""
+    for r in range(N):
+        held = [oracle.pass_kv_shard(N, r, t) for t in range(N)]
+        assert held[0] == r and sorted(held) == list(range(N))
+        for t in range(N - 1):
+            assert oracle.pass_kv_shard(N, (r + 1) % N, t + 1) == held[t]
+    slots = set()
+    for s in range(N):
+        hosted = [oracle.pass_q_query(N, s, t) for t in range(N)]
+        assert hosted[0] == s and sorted(hosted) == list(range(N))
+        for t in range(N - 1):
+            assert oracle.pass_q_query(N, (s + 1) % N, t + 1) == hosted[t]
+        slots.update(oracle.pass_q_slot(N, q, s) for q in hosted)
+    assert slots == set(range(N * N))
+    for bad in ((N, 0), (-1, 0), (0, -1)):
+        with pytest.raises(ValueError):
+            oracle.pass_kv_shard(N, *bad)
 
 
 @pytest.mark.parametrize("L,N", [(256, 4), (257, 4), (7, 4), (3, 2), (1000, 8), (1, 1), (0, 3)])

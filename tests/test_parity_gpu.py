@@ -93,7 +93,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         assert_close(o_out[sel], lse_out[sel], o_ref, l_ref, dtype, f"rank {r} merged")
         if mode == "partials" and check_partials:
             for t in range(N):
-                s = (r - t) % N
+                s = oracle.pass_kv_shard(N, r, t)
                 kf, vf, kseq, kpos = _oracle_keys(ranges, N, [s], seed, n_kv, d, std, dtype)
                 o_p, l_p = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
                                             scale, rows=rows)
@@ -175,13 +175,15 @@ def run_pass_q(P, T, N, n_h, n_kv, d, dtype="bf16", seed=0, n_sample=None, check
         o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, True, scale,
                                         rows=rows)
         assert_close(o_out[qi][sel], lse_out[qi][sel], o_ref, l_ref, dtype, f"q shard {qi} merged")
-        if check_partials and qi == N - 1:
+        if check_partials:
+            # every slot: the partial of Q shard qi against KV shard s, wherever the ring put it
             for s in range(N):
                 kf1, vf1, ks1, kp1 = _oracle_keys(kv_ranges, N, [s], seed, n_kv, d, std, dtype)
                 o_p, l_p = oracle.attention(qf, kf1, vf1, n_h, n_kv, q_seq, q_pos, ks1, kp1, True,
                                             scale, rows=rows)
-                assert_close(o_parts[qi * N + s][sel], lse_parts[qi * N + s][sel], o_p, l_p, dtype,
-                             f"slot [{qi}][{s}]")
+                slot = oracle.pass_q_slot(N, qi, s)
+                assert_close(o_parts[slot][sel], lse_parts[slot][sel], o_p, l_p, dtype,
+                             f"slot {slot} = (q shard {qi}, kv shard {s})")
 
 
 def test_pass_q_persistent_kv_small():
