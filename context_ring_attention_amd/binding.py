@@ -24,8 +24,9 @@ CP_MAX_MERGE_PARTS = 64
 CP_PASS_KV, CP_PASS_Q = 0, 1
 
 EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
-            "cp_decode_workspace_bytes", "cp_ring_pass_kv", "cp_ring_pass_q",
-            "cp_select_ring_variant", "cp_status_string", "cp_last_error")
+            "cp_decode_workspace_bytes", "cp_decode_splitkv_ex", "cp_decode_workspace_bytes_ex",
+            "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant", "cp_status_string",
+            "cp_last_error")
 
 
 class CpSegment(ctypes.Structure):
@@ -78,6 +79,10 @@ def load():
                                       i32, vp, vp]
     lib.cp_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.cp_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.cp_decode_splitkv_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f, i32, vp,
+                                         vp, vp, i32, vp, vp]
+    lib.cp_decode_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32]
+    lib.cp_decode_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.cp_ring_pass_kv.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
                                     i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
@@ -91,7 +96,8 @@ def load():
                                            ctypes.c_double, ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]
     for name in ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
-                 "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant"):
+                 "cp_decode_splitkv_ex", "cp_ring_pass_kv", "cp_ring_pass_q",
+                 "cp_select_ring_variant"):
         getattr(lib, name).restype = ctypes.c_int
     lib.cp_status_string.argtypes = [ctypes.c_int]
     lib.cp_status_string.restype = ctypes.c_char_p
@@ -260,31 +266,47 @@ def merge_lse(o_parts, lse_parts, o_out, lse_out=None, stream=None, check: bool 
                             _stream(stream)))
 
 
-def decode_workspace_bytes(batch: int, n_h: int, d_h: int, n_splits: int) -> int:
-    return load().cp_decode_workspace_bytes(batch, n_h, d_h, n_splits)
+def _ws_code(ws_dtype) -> int:
+    if ws_dtype in ("f32", CP_F32):
+        return CP_F32
+    if ws_dtype in ("bf16", CP_BF16):
+        return CP_BF16
+    raise ValueError(f"ws_dtype must be 'f32' or 'bf16', got {ws_dtype!r}")
 
 
-def decode_workspace(batch: int, n_h: int, d_h: int, n_splits: int, device="cuda"):
-    """One caller-owned workspace of cp_decode_workspace_bytes bytes, returned as its two views:
-    ws_o bf16 [batch, n_splits, n_h, d_h] and ws_lse fp32 [batch, n_splits, n_h]."""
+def decode_workspace_bytes(batch: int, n_h: int, d_h: int, n_splits: int, ws_dtype="f32") -> int:
+    """cp_decode_workspace_bytes_ex: bytes of one split workspace (partial O in ws_dtype, then
+    fp32 LSEs)."""
+    return load().cp_decode_workspace_bytes_ex(batch, n_h, d_h, n_splits, _ws_code(ws_dtype))
+
+
+def decode_workspace(batch: int, n_h: int, d_h: int, n_splits: int, device="cuda", ws_dtype="f32"):
+    """One caller-owned workspace of cp_decode_workspace_bytes_ex bytes, returned as its two views:
+    ws_o [batch, n_splits, n_h, d_h] (fp32 by default, bf16 for the half-size workspace) and
+    ws_lse fp32 [batch, n_splits, n_h]."""
     import torch
-    nbytes = decode_workspace_bytes(batch, n_h, d_h, n_splits)
+    code = _ws_code(ws_dtype)
+    nbytes = decode_workspace_bytes(batch, n_h, d_h, n_splits, code)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    o_bytes = batch * n_splits * n_h * d_h * 2
-    ws_o = ws[:o_bytes].view(torch.bfloat16).view(batch, n_splits, n_h, d_h)
+    elt, tdt = (2, torch.bfloat16) if code == CP_BF16 else (4, torch.float32)
+    o_bytes = batch * n_splits * n_h * d_h * elt
+    ws_o = ws[:o_bytes].view(tdt).view(batch, n_splits, n_h, d_h)
     ws_lse = ws[o_bytes:].view(torch.float32).view(batch, n_splits, n_h)
     return ws_o, ws_lse
 
 
 def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softmax_scale: float,
                    ws_o, ws_lse, o_out, lse_out=None, stream=None, check: bool = True):
-    """cp_decode_splitkv. q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device.
+    """cp_decode_splitkv (fp32 ws_o) or cp_decode_splitkv_ex (bf16 ws_o: the half-size workspace).
+    q [B, n_h, d] bf16; caches [sum L, n_kv, d]; offsets/lens int64 device.
 
     check=False skips the tensor checks (about 3 us of host time per call): for loops whose
     tensors were validated on an earlier call."""
+    import torch
     lib = load()
     B, n_h, d = q.shape
     n_kv = k_cache.shape[1]
+    ws_bf16 = getattr(ws_o, "dtype", None) == torch.bfloat16
     if check:
         bf16, i64, f32 = _types("bf16"), _types("i64"), _types("f32")
         _req(q, "q", bf16)
@@ -294,14 +316,21 @@ def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softma
             raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected [tokens, n_kv, {d}]")
         _req(kv_offset, "kv_offset", i64, (B,))
         _req(kv_len, "kv_len", i64, (B,))
-        _req(ws_o, "ws_o", bf16, numel=B * n_splits * n_h * d)
+        _req(ws_o, "ws_o", _types("inp"), numel=B * n_splits * n_h * d)
         _req(ws_lse, "ws_lse", f32, numel=B * n_splits * n_h)
         _req(o_out, "o_out", _types("inp"), (B, n_h, d))
         _req(lse_out, "lse_out", f32, numel=B * n_h)
-    _check(lib.cp_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
-                                 _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
-                                 float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
-                                 _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
+    if ws_bf16:
+        _check(lib.cp_decode_splitkv_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
+                                        _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
+                                        float(softmax_scale), CP_BF16, _ptr(ws_o), _ptr(ws_lse),
+                                        _ptr(o_out), _dtype_code(o_out), _ptr(lse_out),
+                                        _stream(stream)))
+    else:
+        _check(lib.cp_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
+                                     _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
+                                     float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
+                                     _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,

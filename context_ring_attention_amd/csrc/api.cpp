@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -335,27 +336,37 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
   return launch_status(cpk::launch_merge(p, static_cast<hipStream_t>(stream)), "cp_merge_lse");
 }
 
-size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits) {
+size_t cp_decode_workspace_bytes_ex(int batch, int n_h, int d_h, int n_splits, cp_dtype ws_dtype) {
   if (batch < 0 || n_h < 0 || d_h < 0 || n_splits < 0) return 0;
+  if (ws_dtype != CP_F32 && ws_dtype != CP_BF16) return 0;
   const size_t parts = (size_t)batch * n_splits * n_h;
-  return parts * d_h * 2 + parts * sizeof(float);  // bf16 partial O, then fp32 LSE
+  const size_t elt = ws_dtype == CP_BF16 ? 2 : 4;
+  return parts * d_h * elt + parts * sizeof(float);  // partial O, then fp32 LSE
 }
 
-int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                      const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
-                      int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
-                      void* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
-                      void* stream) {
+size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits) {
+  return cp_decode_workspace_bytes_ex(batch, n_h, d_h, n_splits, CP_F32);
+}
+
+int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                         int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
+                         cp_dtype ws_dtype, void* ws_o, float* ws_lse, void* o_out,
+                         cp_dtype out_dtype, float* lse_out, void* stream) {
   int st = check_heads(n_h, n_kv, d_h);
   if (st) return st;
   if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "decode supports bf16 inputs only");
   if (out_dtype != CP_F32 && out_dtype != CP_BF16) return fail(CP_E_ARG, "out_dtype=%d", (int)out_dtype);
+  if (ws_dtype != CP_F32 && ws_dtype != CP_BF16) return fail(CP_E_ARG, "ws_dtype=%d", (int)ws_dtype);
   if (batch < 0 || batch > 65535) return fail(CP_E_UNSUPPORTED, "batch=%d (0..65535)", batch);
   if (n_splits < 1 || n_splits > 1024) return fail(CP_E_UNSUPPORTED, "n_splits=%d (1..1024)", n_splits);
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(CP_E_ARG, "softmax_scale must be finite and > 0");
   const int group = n_h / n_kv;
   if ((int64_t)n_kv * ((group + 15) / 16) > 65535) return fail(CP_E_UNSUPPORTED, "too many head blocks");
+  // the merge grid has one workgroup per (request, head) in one 32-bit dimension, 256 threads each
+  if ((int64_t)batch * n_h * 256 > (int64_t)UINT32_MAX)
+    return fail(CP_E_UNSUPPORTED, "batch * n_h = %lld too large", (long long)batch * n_h);
   if (batch == 0) return ok();
   if (!q || !k_cache || !v_cache || !kv_offset || !kv_len || !ws_o || !ws_lse || !o_out)
     return fail(CP_E_ARG, "NULL pointer argument");
@@ -377,9 +388,20 @@ int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   p.group = group;
   p.n_splits = n_splits;
   p.out_bf16 = out_dtype == CP_BF16;
+  p.ws_bf16 = ws_dtype == CP_BF16;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_status(cpk::launch_decode(p, d_h, static_cast<hipStream_t>(stream)), "cp_decode_splitkv");
+}
+
+int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                      int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
+                      float* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
+                      void* stream) {
+  return cp_decode_splitkv_ex(q, k_cache, v_cache, kv_offset, kv_len, batch, n_h, n_kv, d_h,
+                              in_dtype, n_splits, softmax_scale, CP_F32, ws_o, ws_lse, o_out,
+                              out_dtype, lse_out, stream);
 }
 
 // Ring Pass-KV ([CPMTI §3 "核心公式"; Fig. 3]): the rank keeps its Q shard; at step t it holds the

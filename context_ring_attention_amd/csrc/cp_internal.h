@@ -72,7 +72,7 @@ struct DecodeParams {
   const void* v;
   const int64_t* kv_offset;
   const int64_t* kv_len;
-  void* ws_o;  // bf16 [batch, n_splits, n_h, d_h]
+  void* ws_o;  // [batch, n_splits, n_h, d_h], fp32 (or bf16 if ws_bf16)
   float* ws_lse;
   void* o_out;
   float* lse_out;
@@ -82,6 +82,7 @@ struct DecodeParams {
   int32_t group;
   int32_t n_splits;
   int32_t out_bf16;
+  int32_t ws_bf16;
   float scale;
   float scale_log2;
 };

@@ -17,10 +17,10 @@
 //  - V comes back from LDS as the V^T operand of O^T += V^T P^T via ds_read_b64_tr_b16;
 //  - the next block's K and V loads are issued before the current block's math, and the first
 //    block's loads are in flight together with the query's.
-// Each split's partial O is normalised (a convex combination of V rows) and stored in bf16, the
-// precision of the probabilities its P.V already used; its LSE stays fp32. The merge kernel then
-// combines the S partials of each (request, head) with the same LSE-weighted rule as
-// cp_merge_lse.
+// Each split's partial O is normalised (a convex combination of V rows) and stored in the
+// workspace in fp32 (the default: the merge then rounds nothing), or in bf16 when the caller asks
+// for the half-size workspace; its LSE is always fp32. The merge kernel then combines the S
+// partials of each (request, head) with the same LSE-weighted rule as cp_merge_lse.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
@@ -55,7 +55,7 @@ struct DecCfg {
 // the split's keys with LDS of its own, and the W partial results are combined in LDS before
 // the split's partial is written. W = 1 for large batches (enough workgroups to fill the chip);
 // W = 4 for small ones, where one wave per split would leave most of each CU idle.
-template <int D, int W>
+template <int D, int W, bool WS_BF16>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams p) {
   using C = DecCfg<D>;
   // combine area: per wave 16 heads x (D values of O + m + l), in fp32
@@ -261,67 +261,80 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
       }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // The partial O of this (request, split, head block) is a [heads][D] bf16 tile, and the
-  // workspace layout [batch][n_splits][n_h][D] makes its valid heads one contiguous block. A lane
-  // holds 4-value pieces of one head's row; stored directly, every instruction would write 16
-  // separate 8-byte pieces. The tile goes through this wave's staging LDS instead (no longer
-  // read; the wave's LDS accesses are in order) and leaves as whole rows, 16 bytes per lane,
-  // each instruction covering 1 KB of consecutive bytes.
-  constexpr int kTStride = D * 2 + 32;  // padded rows: the scattered 8-byte writes spread over banks
+  // The partial O of this (request, split, head block) is a [heads][D] tile, and the workspace
+  // layout [batch][n_splits][n_h][D] makes its valid heads one contiguous block. A lane holds
+  // 4-value pieces of one head's row; stored directly, every instruction would write 16 separate
+  // pieces. The tile goes through this wave's staging LDS instead (no longer read; the wave's LDS
+  // accesses are in order) and leaves as whole rows, 16 bytes per lane, each instruction covering
+  // 1 KB of consecutive bytes.
+  constexpr int kElt = WS_BF16 ? 2 : 4;        // bytes per stored value
+  constexpr int kRowBytes = D * kElt;
+  // padded LDS rows: the 16 head rows written by one instruction land on distinct banks
+  constexpr int kTStride = kRowBytes + (WS_BF16 ? 32 : 16);
+  static_assert(16 * kTStride <= C::kStageBytes, "the tile fits the wave's staging LDS");
   unsigned char* tile = ks;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) {
-    const bf16x4 o4 = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
-                       (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
-    *reinterpret_cast<bf16x4*>(tile + col * kTStride + (db * 16 + 4 * grp) * 2) = o4;
+    unsigned char* dst = tile + col * kTStride + (db * 16 + 4 * grp) * kElt;
+    if constexpr (WS_BF16) {
+      const bf16x4 o4 = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
+                         (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
+      *reinterpret_cast<bf16x4*>(dst) = o4;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = oacc[db] * inv;
+    }
   }
   const int n_valid = min(16, p.group - h0);  // heads of this block that exist
   const int64_t prow0 = ((int64_t)b * p.n_splits + c) * p.n_h + g * p.group + h0;
-  unsigned char* wo = reinterpret_cast<unsigned char*>(static_cast<__bf16*>(p.ws_o) + prow0 * D);
-  constexpr int kLanesPerRow = D * 2 / 16;
+  unsigned char* wo = static_cast<unsigned char*>(p.ws_o) + prow0 * kRowBytes;
+  constexpr int kLanesPerRow = kRowBytes / 16;
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
 #pragma unroll
   for (int r0 = 0; r0 < 16; r0 += kRowsPerStore) {
     const int r = r0 + lane / kLanesPerRow;
     const int c16 = (lane % kLanesPerRow) * 16;
     if (r < n_valid)
-      *reinterpret_cast<u32x4*>(wo + r * (D * 2) + c16) = *reinterpret_cast<const u32x4*>(tile + r * kTStride + c16);
+      *reinterpret_cast<u32x4*>(wo + r * kRowBytes + c16) = *reinterpret_cast<const u32x4*>(tile + r * kTStride + c16);
   }
   if (grp == 0 && head_ok) p.ws_lse[prow0 + col] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // Merge of the S split partials of each (request, head): one workgroup per (request, head),
-// whose partials are S rows of D bf16 values (and S fp32 LSEs), n_h rows apart. D/8 lanes cover
-// a row, 16 bytes each; the 256 / (D/8) lane groups take every kGroups-th split. A lane issues
-// the loads of up to kBatch splits (their LSEs and O slices) before combining any of them, so
-// one round of loads covers 256 splits at D = 128; batches are folded into a running max,
-// weight and sum. The groups are then combined through LDS in a fixed order.
-template <int D, bool OUT_BF16>
+// whose partials are S rows of D values (fp32, or bf16 for the half-size workspace) and S fp32
+// LSEs, n_h rows apart. A lane loads 16 bytes of a row (4 fp32 or 8 bf16 values); D / (values per
+// lane) lanes cover a row and the 256 threads form kGroups lane groups that take every
+// kGroups-th split. A lane issues the loads of up to kBatch splits (their LSEs and O slices)
+// before combining any of them; batches are folded into a running max, weight and sum. The groups
+// are then combined through LDS in a fixed order (deterministic).
+template <int D, bool OUT_BF16, bool WS_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
-  constexpr int kLanes = D / 8;
+  constexpr int kVals = WS_BF16 ? 8 : 4;  // values per 16-byte load
+  constexpr int kLanes = D / kVals;
   constexpr int kGroups = 256 / kLanes;
   constexpr int kBatch = 16;
   __shared__ float red_m[kGroups];
   __shared__ float red_w[kGroups];
-  __shared__ float red_o[kGroups][kLanes][8];
+  __shared__ float red_o[kGroups][kLanes][kVals];
   const int r = blockIdx.x;  // b * n_h + head
   const int grp = threadIdx.x / kLanes;
-  const int c8 = threadIdx.x % kLanes;
+  const int cv = threadIdx.x % kLanes;
   const int64_t row0 = (int64_t)(r / p.n_h) * p.n_splits * p.n_h + r % p.n_h;  // split 0's row
   const float* lse = p.ws_lse + row0;
-  const __bf16* o = static_cast<const __bf16*>(p.ws_o) + row0 * D + c8 * 8;
-  const int64_t stride = p.n_h;  // rows between consecutive splits
+  const unsigned char* o = static_cast<const unsigned char*>(p.ws_o) + (row0 * D + cv * kVals) * (WS_BF16 ? 2 : 4);
+  const int64_t stride_b = (int64_t)p.n_h * D * (WS_BF16 ? 2 : 4);  // bytes between splits
 
   float M = -INFINITY, wsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[kVals];
+#pragma unroll
+  for (int e = 0; e < kVals; ++e) acc[e] = 0.f;
   for (int c0 = grp; c0 < p.n_splits; c0 += kGroups * kBatch) {
     float li[kBatch];
-    bf16x8 v[kBatch];
+    u32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = min(c0 + i * kGroups, p.n_splits - 1);  // clamped: in bounds, masked below
-      li[i] = c0 + i * kGroups < p.n_splits ? lse[c * stride] : -INFINITY;
-      v[i] = *reinterpret_cast<const bf16x8*>(o + c * stride * D);
+      li[i] = c0 + i * kGroups < p.n_splits ? lse[(int64_t)c * p.n_h] : -INFINITY;
+      v[i] = *reinterpret_cast<const u32x4*>(o + c * stride_b);
     }
     float Mb = M;
 #pragma unroll
@@ -330,76 +343,89 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     const float a = expf(M - Mb);    // M = -inf -> 0
     wsum *= a;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= a;
+    for (int e = 0; e < kVals; ++e) acc[e] *= a;
     M = Mb;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const float w = expf(li[i] - M);  // -inf -> 0: the part saw no key
       if (w == 0.f) continue;           // skip its O, which may be anything
       wsum += w;
+      if constexpr (WS_BF16) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, v[i]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)v[i][e], acc[e]);
+        for (int e = 0; e < kVals; ++e) acc[e] = fmaf(w, (float)x[e], acc[e]);
+      } else {
+        const f32x4 x = __builtin_bit_cast(f32x4, v[i]);
+#pragma unroll
+        for (int e = 0; e < kVals; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+      }
     }
   }
-  if (c8 == 0) red_m[grp] = M;
+  if (cv == 0) red_m[grp] = M;
   __syncthreads();
   float Mt = red_m[0];
 #pragma unroll
   for (int i = 1; i < kGroups; ++i) Mt = fmaxf(Mt, red_m[i]);
   const float a = (M == -INFINITY) ? 0.f : expf(M - Mt);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red_o[grp][c8][e] = acc[e] * a;
-  if (c8 == 0) red_w[grp] = wsum * a;
+  for (int e = 0; e < kVals; ++e) red_o[grp][cv][e] = acc[e] * a;
+  if (cv == 0) red_w[grp] = wsum * a;
   __syncthreads();
   if (grp != 0) return;
   wsum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int e = 0; e < kVals; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < kGroups; ++i) {  // fixed order: deterministic
     wsum += red_w[i];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += red_o[i][c8][e];
+    for (int e = 0; e < kVals; ++e) acc[e] += red_o[i][cv][e];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t orow = (int64_t)r * D + c8 * 8;
-  if (OUT_BF16) {
-    bf16x8 out;
+  const int64_t orow = (int64_t)r * D + cv * kVals;
+  if constexpr (OUT_BF16) {
+    __bf16* out = static_cast<__bf16*>(p.o_out) + orow;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.o_out) + orow) = out;
+    for (int e0 = 0; e0 < kVals; e0 += 4) {
+      const bf16x4 o4 = {(__bf16)(acc[e0] * inv), (__bf16)(acc[e0 + 1] * inv),
+                         (__bf16)(acc[e0 + 2] * inv), (__bf16)(acc[e0 + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(out + e0) = o4;
+    }
   } else {
     float* out = static_cast<float*>(p.o_out) + orow;
-    *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+#pragma unroll
+    for (int e0 = 0; e0 < kVals; e0 += 4)
+      *reinterpret_cast<float4*>(out + e0) =
+          make_float4(acc[e0] * inv, acc[e0 + 1] * inv, acc[e0 + 2] * inv, acc[e0 + 3] * inv);
   }
-  if (c8 == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
+  if (cv == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
+}
+
+template <int D, bool WS_BF16>
+void launch_decode_d(const DecodeParams& p, dim3 grid, dim3 mgrid, bool wide, hipStream_t stream) {
+  if (wide)
+    hipLaunchKernelGGL((decode_split_kernel<D, 4, WS_BF16>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, 1, WS_BF16>), grid, dim3(64), 0, stream, p);
+  if (p.out_bf16)
+    hipLaunchKernelGGL((decode_merge_kernel<D, true, WS_BF16>), mgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, false, WS_BF16>), mgrid, dim3(256), 0, stream, p);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
+  // grid sizes are checked on the host (api.cpp) to fit these 32-bit dimensions
   const int hblocks = (p.group + 15) / 16;
   const dim3 grid(p.n_splits * p.batch, p.n_kv * hblocks);
   const dim3 mgrid(p.batch * p.n_h);
   // Fewer workgroups than 8 per CU: four waves share each split.
   const bool wide = (int64_t)grid.x * grid.y < 2048;
   if (d_h == 64) {
-    if (wide)
-      hipLaunchKernelGGL((decode_split_kernel<64, 4>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<64, 1>), grid, dim3(64), 0, stream, p);
-    if (p.out_bf16)
-      hipLaunchKernelGGL((decode_merge_kernel<64, true>), mgrid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<64, false>), mgrid, dim3(256), 0, stream, p);
+    if (p.ws_bf16) launch_decode_d<64, true>(p, grid, mgrid, wide, stream);
+    else launch_decode_d<64, false>(p, grid, mgrid, wide, stream);
   } else {
-    if (wide)
-      hipLaunchKernelGGL((decode_split_kernel<128, 4>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<128, 1>), grid, dim3(64), 0, stream, p);
-    if (p.out_bf16)
-      hipLaunchKernelGGL((decode_merge_kernel<128, true>), mgrid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<128, false>), mgrid, dim3(256), 0, stream, p);
+    if (p.ws_bf16) launch_decode_d<128, true>(p, grid, mgrid, wide, stream);
+    else launch_decode_d<128, false>(p, grid, mgrid, wide, stream);
   }
   return hipGetLastError();
 }

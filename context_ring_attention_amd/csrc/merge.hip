@@ -10,6 +10,8 @@
 // layout produces in every ring step) are not read.
 //
 // Pages cited: [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (review).
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace cpk {
@@ -22,70 +24,72 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int kLanesPerRow = D / 4;
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
   constexpr int kGroup = 8;  // parts whose loads are issued together
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const int c4 = threadIdx.x % kLanesPerRow;
-  if (row >= p.rows) return;
   const int n = p.n_parts;
-
-  // pass 1: M = max_i LSE_i
-  float M = -INFINITY;
-  for (int i0 = 0; i0 < n; i0 += kGroup) {
-    float li[kGroup];
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) li[k] = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) M = fmaxf(M, li[k]);
-  }
-  // pass 2: weights, then the O slices of a group's parts that saw a key, all loads in flight
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  if (M != -INFINITY) {
+  // grid-stride over rows: the grid is capped on the host, so any row count fits one launch
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow; row < p.rows;
+       row += (int64_t)gridDim.x * kRowsPerBlock) {
+    // pass 1: M = max_i LSE_i
+    float M = -INFINITY;
     for (int i0 = 0; i0 < n; i0 += kGroup) {
-      float w[kGroup];
+      float li[kGroup];
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        const float li = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
-        w[k] = li == -INFINITY ? 0.f : expf(li - M);
-      }
-      float4 o[kGroup];
+      for (int k = 0; k < kGroup; ++k) li[k] = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k)
-        if (w[k] != 0.f) {
-          const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p.o_parts[i0 + k] + row * D + c4 * 4));
-          o[k] = make_float4(t[0], t[1], t[2], t[3]);
-        } else {
-          o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < kGroup; ++k) M = fmaxf(M, li[k]);
+    }
+    // pass 2: weights, then the O slices of a group's parts that saw a key, all loads in flight
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+      for (int i0 = 0; i0 < n; i0 += kGroup) {
+        float w[kGroup];
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          const float li = i0 + k < n ? p.lse_parts[i0 + k][row] : -INFINITY;
+          w[k] = li == -INFINITY ? 0.f : expf(li - M);
         }
+        float4 o[kGroup];
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k) {
-        wsum += w[k];
-        acc.x = fmaf(w[k], o[k].x, acc.x);
-        acc.y = fmaf(w[k], o[k].y, acc.y);
-        acc.z = fmaf(w[k], o[k].z, acc.z);
-        acc.w = fmaf(w[k], o[k].w, acc.w);
+        for (int k = 0; k < kGroup; ++k)
+          if (w[k] != 0.f) {
+            const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p.o_parts[i0 + k] + row * D + c4 * 4));
+            o[k] = make_float4(t[0], t[1], t[2], t[3]);
+          } else {
+            o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          wsum += w[k];
+          acc.x = fmaf(w[k], o[k].x, acc.x);
+          acc.y = fmaf(w[k], o[k].y, acc.y);
+          acc.z = fmaf(w[k], o[k].z, acc.z);
+          acc.w = fmaf(w[k], o[k].w, acc.w);
+        }
       }
     }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+    if (OUT_BF16) {
+      __bf16* out = static_cast<__bf16*>(p.o_out) + row * D + c4 * 4;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 v = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
+      __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(out));
+    } else {
+      const f32x4v t = {acc.x, acc.y, acc.z, acc.w};
+      __builtin_nontemporal_store(t, reinterpret_cast<f32x4v*>(static_cast<float*>(p.o_out) + row * D + c4 * 4));
+    }
+    if (c4 == 0 && p.lse_out) p.lse_out[row] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  acc.x *= inv;
-  acc.y *= inv;
-  acc.z *= inv;
-  acc.w *= inv;
-  if (OUT_BF16) {
-    __bf16* out = static_cast<__bf16*>(p.o_out) + row * D + c4 * 4;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 v = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
-    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(out));
-  } else {
-    const f32x4v t = {acc.x, acc.y, acc.z, acc.w};
-    __builtin_nontemporal_store(t, reinterpret_cast<f32x4v*>(static_cast<float*>(p.o_out) + row * D + c4 * 4));
-  }
-  if (c4 == 0 && p.lse_out) p.lse_out[row] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int rows_per_block = 256 / (p.d_h / 4);
-  const int64_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
+  // at most 64K workgroups (256 per CU); larger merges loop inside the kernel
+  const int64_t blocks = std::min<int64_t>((p.rows + rows_per_block - 1) / rows_per_block, 65536);
   const dim3 grid((unsigned)blocks), block(256);
   if (p.d_h == 64) {
     if (p.out_bf16)

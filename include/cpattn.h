@@ -127,11 +127,11 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
  *     [kv_offset[b], kv_offset[b] + kv_len[b]); kv_offset, kv_len: device int64 [batch].
  *   Split c of request b covers cache rows [floor(c*L_b/S), floor((c+1)*L_b/S)); every cached key
  *   is visible (the query comes after the cache).
- *   ws_o: device bf16 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
- *     the per-split partials, O normalised over the split's keys and rounded to bf16 (the
- *     precision of the probabilities its P.V used), LSE in fp32 (caller-owned workspace of
- *     cp_decode_workspace_bytes bytes, laid out ws_o first, then ws_lse at byte offset
- *     batch*n_splits*n_h*d_h*2; ws_o 16-byte aligned).
+ *   ws_o: device fp32 [batch, n_splits, n_h, d_h], ws_lse: device fp32 [batch, n_splits, n_h]:
+ *     the per-split partials (O normalised over the split's keys, and its LSE). They are merged
+ *     in fp32, so the result is the exact combine of the splits ([CPMTI §2]: the ring variants
+ *     are lossless). Caller-owned; cp_decode_workspace_bytes gives the size of one buffer holding
+ *     ws_o then ws_lse (at byte offset batch*n_splits*n_h*d_h*4). ws_o is 16-byte aligned.
  *   o_out: device [batch, n_h, d_h] in out_dtype; lse_out: device fp32 [batch, n_h] (may be NULL).
  * in_dtype must be CP_BF16. 1 <= n_splits <= 1024.
  * kv_offset and kv_len live in device memory and are read by the kernels, not checked on the host:
@@ -142,9 +142,23 @@ int cp_merge_lse(int n_parts, const float* const* o_parts, const float* const* l
 int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
                       int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
-                      void* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
+                      float* ws_o, float* ws_lse, void* o_out, cp_dtype out_dtype, float* lse_out,
                       void* stream);
 size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits);
+
+/* cp_decode_splitkv_ex -- cp_decode_splitkv with the precision of the split workspace's partial O
+ * chosen by the caller: ws_dtype CP_F32 (exactly cp_decode_splitkv) or CP_BF16, which halves the
+ * partials' HBM traffic at the price of rounding each split's O to bf16 before the merge (a
+ * relative 2^-9 of |V|, the precision the split's bf16 probabilities already carry). The LSEs stay
+ * fp32. ws_o: device [batch, n_splits, n_h, d_h] in ws_dtype; cp_decode_workspace_bytes_ex sizes
+ * the buffer (ws_lse at byte offset batch*n_splits*n_h*d_h*sizeof(ws_dtype)); returns 0 for a bad
+ * ws_dtype. Other arguments and errors as cp_decode_splitkv (CP_E_ARG for a bad ws_dtype). */
+int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                         int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
+                         cp_dtype ws_dtype, void* ws_o, float* ws_lse, void* o_out,
+                         cp_dtype out_dtype, float* lse_out, void* stream);
+size_t cp_decode_workspace_bytes_ex(int batch, int n_h, int d_h, int n_splits, cp_dtype ws_dtype);
 
 /* ---------------------------------------------------------------------------------------------
  * cp_ring_pass_kv -- one rank's ring Pass-KV on one device ([CPMTI §3 "核心公式": each rank keeps

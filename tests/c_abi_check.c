@@ -96,7 +96,8 @@ static void check_validation(void) {
 }
 
 static void check_sizes_and_selector(void) {
-  CHECK(cp_decode_workspace_bytes(32, 16, 128, 256) == (size_t)32 * 256 * 16 * (128 * 2 + 4));
+  CHECK(cp_decode_workspace_bytes(32, 16, 128, 256) == (size_t)32 * 256 * 16 * (128 * 4 + 4));
+  CHECK(cp_decode_workspace_bytes_ex(32, 16, 128, 256, CP_BF16) == (size_t)32 * 256 * 16 * (128 * 2 + 4));
   CHECK(cp_decode_workspace_bytes(-1, 16, 128, 256) == 0);
 
   int variant = -1, reason = -1;

@@ -151,8 +151,19 @@ def test_merge_and_decode_reject_bad_arguments():
                None) == cp.CP_E_SHAPE
     assert dec(0, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16, cp.CP_F32, None,
                None) == cp.CP_E_ARG
-    # bf16 partial O, then fp32 LSE
-    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 * 2 + 4)
+    # fp32 partial O, then fp32 LSE; the _ex sizes follow the chosen workspace dtype
+    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) == 32 * 256 * 16 * (128 * 4 + 4)
+    assert lib.cp_decode_workspace_bytes_ex(32, 16, 128, 256, cp.CP_F32) == 32 * 256 * 16 * (128 * 4 + 4)
+    assert lib.cp_decode_workspace_bytes_ex(32, 16, 128, 256, cp.CP_BF16) == 32 * 256 * 16 * (128 * 2 + 4)
+    assert lib.cp_decode_workspace_bytes_ex(32, 16, 128, 256, 7) == 0
+    dex = lib.cp_decode_splitkv_ex
+    assert dex(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 256, 0.1, 7, 16, 16, 16, cp.CP_F32, None,
+               None) == cp.CP_E_ARG                                    # bad workspace dtype
+    assert dex(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 2000, 0.1, cp.CP_BF16, 16, 16, 16,
+               cp.CP_F32, None, None) == cp.CP_E_UNSUPPORTED
+    # grid limits are checked on the host: one merge workgroup of 256 threads per (request, head)
+    assert dec(16, 16, 16, 16, 16, 65535, 4096, 4096, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16,
+               cp.CP_F32, None, None) == cp.CP_E_UNSUPPORTED
     assert lib.cp_status_string(cp.CP_E_HIP) == b"CP_E_HIP"
 
 
