@@ -39,17 +39,54 @@ def product_shards(ranges, N, ranks=None):
     return {r: Shard(*cp.shard_map(ranges, N, r)) for r in ranks}
 
 
-def device_tensor(seed, tid, tokens, shape, std, dtype, device="cuda"):
-    x = si.normal_tokens(seed, tid, tokens, shape, std)
+def device_tensor(seed, tid, tokens, shape, std, dtype, device="cuda", gen=None):
+    x = (gen or si.normal_tokens)(seed, tid, tokens, shape, std)
     xd, _ = si.to_dtype(x, dtype)
     return xd.contiguous().to(device)
 
 
-def oracle_view(seed, tid, tokens, shape, std, dtype):
+def oracle_view(seed, tid, tokens, shape, std, dtype, gen=None):
     """The exact fp32 values the device holds for these tokens (bf16-rounded when bf16)."""
-    x = si.normal_tokens(seed, tid, tokens, shape, std)
+    x = (gen or si.normal_tokens)(seed, tid, tokens, shape, std)
     _, xf = si.to_dtype(x, dtype)
     return xf.numpy()
+
+
+class Planted:
+    """Seeded inputs with planted structure, for driving the online softmax's rarely taken paths
+    (a row max that jumps late, scores spread over tens of nats). Input construction only: it
+    draws the same seeded N(0, std^2) tokens as synth_inputs.normal_tokens and then, per global
+    token index g,
+      - Q and K may take their own std (q_std, k_std: wide score ranges); V keeps `std`;
+      - Q: adds q_bias * u to every query head (u = the all-ones direction / sqrt(D));
+      - K: adds ramp * (g / total) * u (keys score higher the later they sit), and overwrites the
+        keys at `spikes` {g: a} with a * u, so a query scores them about scale * a * (q.u + q_bias).
+    V is plain. The device and the oracle both take their values from here, so they see identical
+    (bf16-rounded) inputs."""
+
+    def __init__(self, q_bias=0.0, ramp=0.0, spikes=None, total=1, q_std=None, k_std=None):
+        self.q_bias, self.ramp, self.spikes, self.total = q_bias, ramp, dict(spikes or {}), max(1, total)
+        self.q_std, self.k_std = q_std, k_std
+
+    def __call__(self, seed, tid, tokens, shape, std):
+        tokens = np.asarray(tokens, np.int64)
+        if tid == si.TID_Q and self.q_std is not None:
+            std = self.q_std
+        if tid == si.TID_K and self.k_std is not None:
+            std = self.k_std
+        x = si.normal_tokens(seed, tid, tokens, shape, std)
+        d = shape[-1]
+        u = torch.full((d,), 1.0 / math.sqrt(d))
+        if tid == si.TID_Q and self.q_bias:
+            x += self.q_bias * u
+        if tid == si.TID_K:
+            if self.ramp:
+                x += (self.ramp * torch.from_numpy(tokens / self.total).float()).view(-1, *([1] * len(shape))) * u
+            for g, a in self.spikes.items():
+                hit = np.flatnonzero(tokens == g)
+                if hit.size:
+                    x[torch.from_numpy(hit)] = (a * u).expand(shape)
+        return x
 
 
 def seq_pos_of(ranges, tokens):

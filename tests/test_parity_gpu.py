@@ -26,8 +26,8 @@ def _gpu():
     binding.load()
 
 
-def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
-    tol_o, tol_l = TOL[dtype]
+def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, tol=None):
+    tol_o, tol_l = tol or TOL[dtype]
     o_g = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
     l_g = lse_gpu.float().cpu().numpy().astype(np.float64).reshape(lse_ref.shape)
     inf_g, inf_r = np.isneginf(l_g), np.isneginf(lse_ref)
@@ -41,19 +41,19 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
     assert err_o <= tol_o and err_l <= tol_l, what
 
 
-def _oracle_keys(ranges, N, shard_ids, seed, n_kv, d, std, dtype):
+def _oracle_keys(ranges, N, shard_ids, seed, n_kv, d, std, dtype, gen=None):
     ks, vs, sq, ps = [], [], [], []
     for s in shard_ids:
         seq, pos, glob = oracle.shard_tokens(ranges, N, s)
-        ks.append(oracle_view(seed, si.TID_K, glob, (n_kv, d), std, dtype))
-        vs.append(oracle_view(seed, si.TID_V, glob, (n_kv, d), std, dtype))
+        ks.append(oracle_view(seed, si.TID_K, glob, (n_kv, d), std, dtype, gen))
+        vs.append(oracle_view(seed, si.TID_V, glob, (n_kv, d), std, dtype, gen))
         sq.append(seq)
         ps.append(pos)
     return np.concatenate(ks), np.concatenate(vs), np.concatenate(sq), np.concatenate(ps)
 
 
 def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, mode="partials",
-                check_partials=True, n_sample=None, std=None):
+                check_partials=True, n_sample=None, std=None, gen=None):
     from context_ring_attention_amd import binding as cp
     ranges = [(i, 0, L) for i, L in enumerate(seqs)]
     std = std if std is not None else (1.0 / np.sqrt(d) if dtype == "f32" else 1.0)
@@ -61,12 +61,12 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
     ranks = list(range(N)) if ranks is None else ranks
     sh = product_shards(ranges, N)
     for s in sh.values():
-        s.k = device_tensor(seed, si.TID_K, s.tokens, (n_kv, d), std, dtype)
-        s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype)
-    all_keys = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype)
+        s.k = device_tensor(seed, si.TID_K, s.tokens, (n_kv, d), std, dtype, gen=gen)
+        s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype, gen=gen)
+    all_keys = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype, gen)
     for r in ranks:
         log(f"pass-kv seqs={seqs} N={N} rank={r} n_h={n_h} n_kv={n_kv} d={d} {dtype} mode={mode} causal={causal}")
-        q = device_tensor(seed, si.TID_Q, sh[r].tokens, (n_h, d), std, dtype)
+        q = device_tensor(seed, si.TID_Q, sh[r].tokens, (n_h, d), std, dtype, gen=gen)
         tq = q.shape[0]
         o_out = torch.empty(tq, n_h, d, dtype=torch.float32, device="cuda")
         lse_out = torch.empty(tq, n_h, dtype=torch.float32, device="cuda")
@@ -84,7 +84,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         torch.cuda.synchronize()
 
         q_seq, q_pos, q_glob = oracle.shard_tokens(ranges, N, r)
-        qf = oracle_view(seed, si.TID_Q, q_glob, (n_h, d), std, dtype)
+        qf = oracle_view(seed, si.TID_Q, q_glob, (n_h, d), std, dtype, gen)
         rows = sample_rows(sh[r].segs, n_sample, seed + r) if n_sample else None
         kf, vf, kseq, kpos = all_keys
         o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
@@ -94,7 +94,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         if mode == "partials" and check_partials:
             for t in range(N):
                 s = oracle.pass_kv_shard(N, r, t)
-                kf, vf, kseq, kpos = _oracle_keys(ranges, N, [s], seed, n_kv, d, std, dtype)
+                kf, vf, kseq, kpos = _oracle_keys(ranges, N, [s], seed, n_kv, d, std, dtype, gen)
                 o_p, l_p = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, causal,
                                             scale, rows=rows)
                 assert_close(kw["o_parts"][t][sel], kw["lse_parts"][t][sel], o_p, l_p, dtype,
@@ -237,50 +237,57 @@ def test_merge_in_place_fp32():
 
 
 # --------------------------------------------------------------------------- decode
-def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=None):
+def run_decode(lengths, n_h, n_kv, d, n_splits, seed=0, out="f32", check_splits=None, ws="f32",
+               std=1.0, gen=None, tol_scale=1.0):
+    """Split-KV decode through the C ABI against the oracle: every request's merged (O, LSE), and
+    the split partials listed in check_splits. ws: workspace precision of the partial O ("f32",
+    cp_decode_splitkv; "bf16", cp_decode_splitkv_ex). tol_scale widens the O bound for inputs
+    whose values are tol_scale times larger than N(0,1) (the bound is relative to |V|)."""
     from context_ring_attention_amd import binding as cp
     lengths = np.asarray(lengths, np.int64)
     B = len(lengths)
     offs = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
     total = int(lengths.sum())
-    log(f"decode B={B} n_splits={n_splits} total_keys={total} n_h={n_h} n_kv={n_kv} d={d}")
+    log(f"decode B={B} n_splits={n_splits} total_keys={total} n_h={n_h} n_kv={n_kv} d={d} ws={ws}")
     scale = scale_of(d)
     toks = np.arange(total)
-    kc = device_tensor(seed, si.TID_K, toks, (n_kv, d), 1.0, "bf16")
-    vc = device_tensor(seed, si.TID_V, toks, (n_kv, d), 1.0, "bf16")
-    q = device_tensor(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
-    ws_o, ws_l = cp.decode_workspace(B, n_h, d, n_splits)
+    kc = device_tensor(seed, si.TID_K, toks, (n_kv, d), std, "bf16", gen=gen)
+    vc = device_tensor(seed, si.TID_V, toks, (n_kv, d), std, "bf16", gen=gen)
+    q = device_tensor(seed, si.TID_Q, np.arange(B), (n_h, d), std, "bf16", gen=gen)
+    ws_o, ws_l = cp.decode_workspace(B, n_h, d, n_splits, ws_dtype=ws)
     o_out = torch.empty(B, n_h, d, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
     l_out = torch.empty(B, n_h, device="cuda")
     cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lengths).cuda(),
                       n_splits, scale, ws_o, ws_l, o_out, l_out)
     torch.cuda.synchronize()
-    qf = oracle_view(seed, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+    qf = oracle_view(seed, si.TID_Q, np.arange(B), (n_h, d), std, "bf16", gen)
+    tol = (TOL["bf16"][0] * tol_scale, TOL["bf16"][1])
     for b in range(B):
         lo, L = int(offs[b]), int(lengths[b])
-        kf = oracle_view(seed, si.TID_K, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
-        vf = oracle_view(seed, si.TID_V, np.arange(lo, lo + L), (n_kv, d), 1.0, "bf16")
+        kf = oracle_view(seed, si.TID_K, np.arange(lo, lo + L), (n_kv, d), std, "bf16", gen)
+        vf = oracle_view(seed, si.TID_V, np.arange(lo, lo + L), (n_kv, d), std, "bf16", gen)
         qs_ = np.zeros(1, np.int32)
         qp_ = np.array([L], np.int64)
         o_ref, l_ref = oracle.attention(qf[b:b + 1], kf, vf, n_h, n_kv, qs_, qp_, np.zeros(L, np.int32),
                                         np.arange(L), False, scale)
-        dt = "bf16"
-        assert_close(o_out[b:b + 1], l_out[b:b + 1], o_ref, l_ref, dt, f"request {b} (L={L})")
+        assert_close(o_out[b:b + 1], l_out[b:b + 1], o_ref, l_ref, "bf16", f"request {b} (L={L})", tol)
         splits = oracle.split_bounds(L, n_splits)
         for c in (check_splits or []):
             a, e = splits[c]
             o_p, l_p = oracle.attention(qf[b:b + 1], kf[a:e], vf[a:e], n_h, n_kv, qs_, qp_,
                                         np.zeros(e - a, np.int32), np.arange(a, e), False, scale)
-            assert_close(ws_o[b, c], ws_l[b, c], o_p, l_p, dt, f"request {b} split {c}")
+            assert_close(ws_o[b, c], ws_l[b, c], o_p, l_p, "bf16", f"request {b} split {c}", tol)
 
 
-def test_decode_small_ragged():
-    run_decode([3000, 1, 100, 4097, 257], 16, 1, 128, 256, check_splits=[0, 1, 99, 255])
+@pytest.mark.parametrize("ws", ["f32", "bf16"])
+def test_decode_small_ragged(ws):
+    run_decode([3000, 1, 100, 4097, 257], 16, 1, 128, 256, check_splits=[0, 1, 99, 255], ws=ws)
 
 
 def test_decode_empty_requests_four_waves_per_split():
     # small grid: four waves share each split; requests with no cached key give O = 0, LSE = -inf
     run_decode([0, 37, 0, 2000, 5], 16, 1, 128, 256, seed=4, check_splits=[0, 128, 255])
+    run_decode([0, 37, 0, 2000, 5], 16, 1, 128, 256, seed=4, check_splits=[0, 128, 255], ws="bf16")
 
 
 def test_decode_one_wave_per_split_with_empty_splits():
@@ -291,6 +298,7 @@ def test_decode_one_wave_per_split_with_empty_splits():
 
 def test_decode_gqa_d64_bf16_out():
     run_decode([999, 64, 2500], 8, 2, 64, 16, seed=1, out="bf16", check_splits=[0, 15])
+    run_decode([999, 64, 2500], 8, 2, 64, 16, seed=1, out="bf16", check_splits=[0, 15], ws="bf16")
 
 
 def test_decode_more_than_16_heads_per_group():
