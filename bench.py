@@ -1,21 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of one context-parallel rank's exact GQA attention on one MI355X.
 
-Workload timed per step (``prefill_128k_cp4``): one attention layer of a 128K-token causal
-prefill with the per-GPU head share of a 128-query-head / 8-KV-head model under TP8 (16 query
-heads, 1 KV head, D_H = 128, bf16), sharded over a CP ring of 4 ranks with load-balanced
-chunking. A step plays every rank's ring Pass-KV on this one GPU: the rank's 32K-token Q shard
-attends to the 4 KV shards of 32K tokens in ring order (by default each ring step folds its
-partial into the running (O, LSE); ``--mode partials`` keeps the 4 partials and merges them).
-Inputs are seeded synthetic N(0,1) values rounded to bf16, resident in HBM before timing starts.
+Workload timed per step (``prefill_1m_varlen_cp8``, the largest single-GPU configuration): one
+attention layer of a causal prefill over a 1M-token batch of four requests (64K, 192K, 256K and
+512K tokens) at CP = 8, with the per-GPU head share of a 128-query-head / 8-KV-head model under
+TP8 (16 query heads, 1 KV head, D_H = 128, bf16). Every request is sharded with load-balanced
+chunking; a step plays rank 0's ring Pass-KV on this one GPU: its 128K-token Q shard (8 runs)
+attends to the 8 KV shards of 128K tokens in ring order, each ring step folding its partial into
+the running (O, LSE) (``--mode partials`` keeps the 8 partials and merges them). Inputs are
+seeded synthetic N(0,1) values rounded to bf16, resident in HBM before timing starts.
 
 value = causal-useful TFLOP/s: 4 * D_H flops per visible (query token, query head, key) triple;
-masked and skipped work is not counted. The same JSON line reports the dominant kernel's
-roofline (cp_partial_attn's MFMA kernel, per-launch time from HIP events on the launch stream),
-secondary measurements (split-KV decode GB/s, persistent-KV Pass-Q TFLOP/s, merge GB/s, and with
---extended the 1M-token varlen rank share), the fp64 oracle timed on host cores for a
-bounded sample of the same workload, and (with the secondary legs) the MFMA clock probe: the bf16
-MFMA rate and shader clock that MFMA-only code sustains on random and on near-constant operands.
+masked and skipped work is not counted. The same JSON line reports the dominant kernel's roofline
+(cp_partial_attn's MFMA kernel, per-launch time from HIP events on the launch stream), secondary
+measurements (the 128K CP4 prefill, the persistent-KV workload as Pass-Q and as Pass-KV with the
+ring-variant selector's choice, the merge, split-KV decode with both workspace precisions, the
+one-request decode step eager and graph-replayed), and the fp64 oracle timed on the host cores:
+measured on a bounded sample of each large workload (and checked against the GPU output of the
+same run), in full on the small ones.
 """
 from __future__ import annotations
 
@@ -33,7 +35,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_prefill_128k_cp4_counters.md")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_prefill_1m_varlen_cp8_counters.md")
+HEADLINE = "prefill_1m_varlen_cp8"
+# Condition 2 of the ring-variant selector needs a link rate; the pages run CP across nodes over
+# RDMA at 400 Gb/s per GPU. It is a stated assumption here (one GPU has no link to measure).
+LINK_BYTES_PER_S = 400e9 / 8
 
 
 def parse():
@@ -45,12 +51,10 @@ def parse():
                     help="fold each ring step into a running (O, LSE) or keep N partials + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--extended", action="store_true", help="also time the 1M-token varlen rank share")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device-to-device copy (calibrates HBM byte counters)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-mfma-probe", action="store_true",
-                    help="skip the MFMA clock probe (a separate program) in the device figures")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time on the headline workload's sample")
     return ap.parse_args()
 
 
@@ -71,9 +75,9 @@ def visible_pairs(q_segs, kv_segs, causal=True):
 
 
 def recorded_traffic():
-    """HBM bytes per launch of the partial-attention kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if the kernel sources changed
-    since the counters were taken."""
+    """HBM bytes per launch of the partial-attention kernel at the headline workload from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if
+    the kernel sources changed since the counters were taken."""
     import hashlib
     try:
         text = open(COUNTERS_MD).read()
@@ -111,8 +115,11 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def bf16_tokens(torch, si, seed, tid, tokens, shape):
-    return si.to_dtype(si.normal_tokens(seed, tid, tokens, shape), "bf16")[0].cuda()
+def tokens_bf16(torch, si, seed, tid, tokens, shape, keep_host=False):
+    """Seeded bf16 values on the device (and, with keep_host, the same values widened to fp32 on
+    the host, for the oracle leg)."""
+    xb, xf = si.to_dtype(si.normal_tokens(seed, tid, tokens, shape), "bf16")
+    return xb.cuda(), (xf.numpy() if keep_host else None)
 
 
 def time_reps(torch, fn, reps, warm=2):
@@ -126,35 +133,229 @@ def time_reps(torch, fn, reps, warm=2):
     return t.ms() / reps
 
 
+def sample_tokens(segs, n_random, seed):
+    """Local rows of a Q shard to check against the oracle: the first and last token of every
+    run (chunk) plus n_random random tokens."""
+    rows = set()
+    for _, _, n, loc in segs:
+        rows.update((loc, loc + n - 1))
+    total = sum(n for _, _, n, _ in segs)
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.integers(0, total, n_random))
+    return np.array(sorted(rows), np.int64)
+
+
+# --------------------------------------------------------------------------- ring Pass-KV workload
+class PassKV:
+    """One Pass-KV workload on the device: the shard map of every rank (from the library), the KV
+    shards of all ranks and the Q shards of `ranks`, plus their running outputs."""
+
+    def __init__(self, torch, cp, si, name, ranks, seed=0, mode="running", keep_host=False):
+        cfg = si.CONFIGS[name]
+        self.name, self.cfg, self.mode = name, cfg, mode
+        self.N, self.n_h, self.n_kv, self.d = cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
+        self.scale = 1.0 / math.sqrt(self.d)
+        self.ranges = [(i, 0, L) for i, L in enumerate(cfg["seqs"])]
+        self.shards = [cp.shard_map(self.ranges, self.N, r) for r in range(self.N)]
+        self.kv_segs = [s for s, _ in self.shards]
+        t0 = time.time()
+        self.ks = [tokens_bf16(torch, si, seed, si.TID_K, t, (self.n_kv, self.d))[0] for _, t in self.shards]
+        self.vs = [tokens_bf16(torch, si, seed, si.TID_V, t, (self.n_kv, self.d))[0] for _, t in self.shards]
+        self.ranks = list(ranks)
+        self.qs = {r: tokens_bf16(torch, si, seed, si.TID_Q, self.shards[r][1], (self.n_h, self.d))[0]
+                   for r in self.ranks}
+        log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
+        self.o = {r: torch.empty(q.shape[0], self.n_h, self.d, device="cuda") for r, q in self.qs.items()}
+        self.lse = {r: torch.empty(q.shape[0], self.n_h, device="cuda") for r, q in self.qs.items()}
+        self.parts = None
+        if mode == "partials":
+            self.parts = {r: ([torch.empty_like(self.o[r]) for _ in range(self.N)],
+                              [torch.empty_like(self.lse[r]) for _ in range(self.N)]) for r in self.ranks}
+        self.pairs = {r: [visible_pairs(self.shards[r][0], self.shards[s][0]) for s in range(self.N)]
+                      for r in self.ranks}
+        self.flops = sum(4 * self.d * self.n_h * sum(p) for p in self.pairs.values())
+
+    def ring(self, cp, r):
+        if self.parts is None:
+            cp.ring_pass_kv(self.qs[r], self.shards[r][0], r, self.ks, self.vs, self.kv_segs, True,
+                            self.scale, self.o[r], self.lse[r], o_acc=self.o[r], lse_acc=self.lse[r],
+                            check=False)
+        else:
+            cp.ring_pass_kv(self.qs[r], self.shards[r][0], r, self.ks, self.vs, self.kv_segs, True,
+                            self.scale, self.o[r], self.lse[r], o_parts=self.parts[r][0],
+                            lse_parts=self.parts[r][1], check=False)
+
+    def step(self, cp):
+        for r in self.ranks:
+            self.ring(cp, r)
+
+    def per_launch(self, torch, cp, passes=2):
+        """Average duration and useful flops of one cp_partial_attn launch (one ring step of one
+        rank), HIP events around each launch on the launch stream."""
+        ms, fl = [], []
+        tmr = Timer(torch)
+        for _ in range(passes):
+            for r in self.ranks:
+                for t in range(self.N):
+                    s = (r - t) % self.N
+                    with tmr:
+                        cp.partial_attn(self.qs[r], self.ks[s], self.vs[s], self.shards[r][0],
+                                        self.shards[s][0], True, self.scale, self.o[r], self.lse[r],
+                                        accumulate=t > 0, check=False)
+                    ms.append(tmr.ms())
+                    fl.append(4 * self.d * self.n_h * self.pairs[r][s])
+        return float(np.mean(ms)), float(np.mean(fl)), len(ms)
+
+    def sample_outputs(self, r, rows):
+        """The device's (O, LSE) of rank r at the given local rows, on the host."""
+        import torch
+        idx = torch.from_numpy(rows).cuda()
+        return self.o[r][idx].cpu().numpy(), self.lse[r][idx].cpu().numpy()
+
+
+def run_timed_steps(torch, wl, cp, steps, warmup):
+    for _ in range(warmup):
+        wl.step(cp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step(cp)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 # --------------------------------------------------------------------------- secondary workloads
+def run_prefill_128k(torch, cp, si, steps):
+    wl = PassKV(torch, cp, si, "prefill_128k_cp4", ranks=range(4))
+    ms = run_timed_steps(torch, wl, cp, steps, 1)
+    tf = wl.flops / (ms * 1e-3) / 1e12
+    avg_ms, avg_fl, n = wl.per_launch(torch, cp, passes=1)
+    ach = avg_fl / (avg_ms * 1e-3) / 1e12
+    log(f"prefill_128k_cp4: {ms:.2f} ms/step (4 ranks), {tf:.1f} useful TFLOP/s; per launch "
+        f"{avg_ms:.3f} ms, {ach:.1f} TFLOP/s")
+    r0 = {"rows": sample_tokens(wl.shards[0][0], 8, 5)}
+    r0["o"], r0["lse"] = wl.sample_outputs(0, r0["rows"])
+    out = {"metric": "causal-useful TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
+           "ms_per_step_all_4_ranks": round(ms, 3), "ms_per_rank": round(ms / 4, 3),
+           "useful_tflop_per_step": round(wl.flops / 1e12, 3),
+           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "per_launch": {"avg_ms": round(avg_ms, 4), "tflops": round(ach, 1), "launches": n,
+                          "frac_of_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}}
+    return out, wl, r0
+
+
+def run_persistent_kv(torch, cp, si, seed=0):
+    """The persistent-KV workload (8K new tokens on 120K cached, CP 4) as ring Pass-Q and as ring
+    Pass-KV over all four ranks, and the ring-variant selector fed with the measured rate."""
+    cfg = si.CONFIGS["persistent_kv_8k_on_120k"]
+    P, T, N, n_h, n_kv, d = cfg["cached"], cfg["new"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
+    q_ranges = [(0, P, P + T)]
+    kv_ranges = [(0, 0, P), (0, P, P + T)]
+    qsh = [cp.shard_map(q_ranges, N, r) for r in range(N)]
+    ksh = [cp.shard_map(kv_ranges, N, r) for r in range(N)]
+    qs = [tokens_bf16(torch, si, seed, si.TID_Q, t, (n_h, d))[0] for _, t in qsh]
+    ks = [tokens_bf16(torch, si, seed, si.TID_K, t, (n_kv, d))[0] for _, t in ksh]
+    vs = [tokens_bf16(torch, si, seed, si.TID_V, t, (n_kv, d))[0] for _, t in ksh]
+    parts_o = [torch.empty(qs[i // N].shape[0], n_h, d, device="cuda") for i in range(N * N)]
+    parts_l = [torch.empty(qs[i // N].shape[0], n_h, device="cuda") for i in range(N * N)]
+    o = [torch.empty(x.shape[0], n_h, d, device="cuda") for x in qs]
+    l = [torch.empty(x.shape[0], n_h, device="cuda") for x in qs]
+    scale = 1.0 / math.sqrt(d)
+    kv_segs, q_segs = [s for s, _ in ksh], [s for s, _ in qsh]
+    pass_q = lambda: cp.ring_pass_q(qs, q_segs, ks, vs, kv_segs, True, scale, parts_o, parts_l, o, l,
+                                    check=False)
+    ms_q = time_reps(torch, pass_q, 5)
+    r0 = {"rows": sample_tokens(q_segs[0], 8, 6)}
+    idx = torch.from_numpy(r0["rows"]).cuda()
+    r0["o"], r0["lse"] = o[0][idx].cpu().numpy(), l[0][idx].cpu().numpy()
+    o_kv = [torch.empty_like(x) for x in o]
+    l_kv = [torch.empty_like(x) for x in l]
+
+    def pass_kv():
+        for r in range(N):
+            cp.ring_pass_kv(qs[r], q_segs[r], r, ks, vs, kv_segs, True, scale, o_kv[r], l_kv[r],
+                            o_acc=o_kv[r], lse_acc=l_kv[r], check=False)
+    ms_kv = time_reps(torch, pass_kv, 5)
+    pairs = sum(visible_pairs(q_segs[a], kv_segs[b]) for a in range(N) for b in range(N))
+    flops = 4 * d * n_h * pairs
+    tf_q, tf_kv = flops / (ms_q * 1e-3) / 1e12, flops / (ms_kv * 1e-3) / 1e12
+    # Algorithm 1: condition 2 with the attention rate measured just now (the Pass-KV rate)
+    choice, reason = cp.select_ring_variant(T, P, N, n_h, n_kv, d, 2, LINK_BYTES_PER_S, tf_kv * 1e12)
+    log(f"persistent KV: pass-q {ms_q:.2f} ms ({tf_q:.1f} TFLOP/s), pass-kv {ms_kv:.2f} ms "
+        f"({tf_kv:.1f} TFLOP/s); selector: {choice} (reason {reason})")
+    out = {"metric": "causal-useful TFLOP/s", "value": round(tf_q, 1), "unit": "TFLOP/s",
+           "ms_per_call": round(ms_q, 3), "useful_tflop": round(flops / 1e12, 3),
+           "frac_of_bf16_peak": round(tf_q / PEAK_BF16_TFLOPS, 4),
+           "pass_kv_same_workload": {"ms": round(ms_kv, 3), "tflops": round(tf_kv, 1)},
+           "selector": {"choice": choice, "reason": reason,
+                        "miss_rate": round(T / (T + P), 5), "threshold_2nkv_over_nh": 2 * n_kv / n_h,
+                        "attn_flops_per_s_measured": round(tf_kv * 1e12),
+                        "link_bytes_per_s_assumed": LINK_BYTES_PER_S,
+                        "faster_measured_here": "pass_q" if ms_q < ms_kv else "pass_kv"}}
+    return out, r0
+
+
+def run_merge(torch, cp, wl):
+    """Merge of rank 0's N ring partials of a Pass-KV workload."""
+    r, N, n_h, d = 0, wl.N, wl.n_h, wl.d
+    tq = wl.qs[r].shape[0]
+    po = [torch.empty(tq, n_h, d, device="cuda") for _ in range(N)]
+    pl = [torch.empty(tq, n_h, device="cuda") for _ in range(N)]
+    for t in range(N):
+        s = (r - t) % N
+        cp.partial_attn(wl.qs[r], wl.ks[s], wl.vs[s], wl.shards[r][0], wl.shards[s][0], True,
+                        wl.scale, po[t], pl[t])
+    rows = tq * n_h
+    out = torch.empty(rows, d, device="cuda")
+    lse = torch.empty(rows, device="cuda")
+    fn = lambda: cp.merge_lse(po, pl, out, lse, check=False)
+    ms = time_reps(torch, fn, 10)
+    seen = sum(int(torch.isfinite(x).sum()) for x in pl)
+    alg = seen * d * 4 + len(pl) * rows * 4 + rows * (d * 4 + 4)
+    gbs = alg / (ms * 1e-3) / 1e9
+    log(f"merge: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"metric": "merge GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": alg, "parts": len(pl),
+            "rows": rows, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def run_decode(torch, cp, si, seed=0):
+    """Split-KV decode, B = 32 requests with 32K-128K cached tokens, 256 splits; timed with the
+    fp32 split workspace (the figure) and the half-size bf16 workspace."""
     cfg = si.CONFIGS["decode_b32_32k_128k"]
     B, n_h, n_kv, d, S = cfg["batch"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["n_splits"]
     lens = si.decode_lengths(seed, B, cfg["len_lo"], cfg["len_hi"])
     offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
     total = int(lens.sum())
     toks = np.arange(total)
-    kc = bf16_tokens(torch, si, seed, si.TID_K, toks, (n_kv, d))
-    vc = bf16_tokens(torch, si, seed, si.TID_V, toks, (n_kv, d))
-    q = bf16_tokens(torch, si, seed, si.TID_Q, np.arange(B), (n_h, d))
-    ws_o, ws_l = cp.decode_workspace(B, n_h, d, S)
+    kc = tokens_bf16(torch, si, seed, si.TID_K, toks, (n_kv, d))[0]
+    vc = tokens_bf16(torch, si, seed, si.TID_V, toks, (n_kv, d))[0]
+    q = tokens_bf16(torch, si, seed, si.TID_Q, np.arange(B), (n_h, d))[0]
     o = torch.empty(B, n_h, d, device="cuda")
     l = torch.empty(B, n_h, device="cuda")
     offs_d = torch.from_numpy(offs).cuda()
     lens_d = torch.from_numpy(lens).cuda()
     scale = 1.0 / math.sqrt(d)
-    fn = lambda: cp.decode_splitkv(q, kc, vc, offs_d, lens_d, S, scale, ws_o, ws_l, o, l)
-    ms = time_reps(torch, fn, 20)
     kv_bytes = total * n_kv * d * 2 * 2
     alg_bytes = kv_bytes + B * n_h * d * 2 + B * n_h * (d * 4 + 4)
-    ws_bytes = cp.decode_workspace_bytes(B, n_h, d, S)
-    gbs = alg_bytes / (ms * 1e-3) / 1e9
-    log(f"decode: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM), "
-        f"{total} cached keys")
-    return {"metric": "decode KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "us_per_call": round(ms * 1e3, 2),
-            "algorithmic_bytes": alg_bytes, "workspace_bytes_each_way": ws_bytes,
-            "cached_keys": total, "batch": B, "n_splits": S}
+    res = {}
+    for ws in ("bf16", "f32"):   # f32 last: its outputs stay for the oracle leg
+        ws_o, ws_l = cp.decode_workspace(B, n_h, d, S, ws_dtype=ws)
+        fn = lambda: cp.decode_splitkv(q, kc, vc, offs_d, lens_d, S, scale, ws_o, ws_l, o, l, check=False)
+        ms = time_reps(torch, fn, 20)
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        res[ws] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                   "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                   "workspace_bytes": cp.decode_workspace_bytes(B, n_h, d, S, ws)}
+        log(f"decode ({ws} workspace): {ms * 1e3:.1f} us, {gbs:.0f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM), {total} cached keys")
+        del ws_o, ws_l
+    out = {"metric": "decode KV GB/s", "value": res["f32"]["GBps"], "unit": "GB/s",
+           "frac_of_hbm_peak": res["f32"]["frac_of_hbm_peak"], "us_per_call": res["f32"]["us_per_call"],
+           "workspace": "f32", "algorithmic_bytes": alg_bytes, "cached_keys": total, "batch": B,
+           "n_splits": S, "by_workspace": res}
+    kept = {"o": o.cpu().numpy(), "lse": l.cpu().numpy(), "lens": lens, "offs": offs}
+    return out, kept
 
 
 def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
@@ -163,16 +364,16 @@ def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
     cfg = si.CONFIGS["decode_b32_32k_128k"]
     n_h, n_kv, d, S = cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["n_splits"]
     toks = np.arange(L)
-    kc = bf16_tokens(torch, si, seed, si.TID_K, toks, (n_kv, d))
-    vc = bf16_tokens(torch, si, seed, si.TID_V, toks, (n_kv, d))
-    q = bf16_tokens(torch, si, seed, si.TID_Q, np.arange(1), (n_h, d))
+    kc = tokens_bf16(torch, si, seed, si.TID_K, toks, (n_kv, d))[0]
+    vc = tokens_bf16(torch, si, seed, si.TID_V, toks, (n_kv, d))[0]
+    q = tokens_bf16(torch, si, seed, si.TID_Q, np.arange(1), (n_h, d))[0]
     ws_o, ws_l = cp.decode_workspace(1, n_h, d, S)
     o = torch.empty(1, n_h, d, device="cuda")
     l = torch.empty(1, n_h, device="cuda")
     offs = torch.zeros(1, dtype=torch.int64, device="cuda")
     lens = torch.full((1,), L, dtype=torch.int64, device="cuda")
     scale = 1.0 / math.sqrt(d)
-    fn = lambda: cp.decode_splitkv(q, kc, vc, offs, lens, S, scale, ws_o, ws_l, o, l)
+    fn = lambda: cp.decode_splitkv(q, kc, vc, offs, lens, S, scale, ws_o, ws_l, o, l, check=False)
     eager_ms = time_reps(torch, fn, reps)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -206,7 +407,31 @@ def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
             "eager_GBps": round(alg / (eager_ms * 1e-3) / 1e9, 1), "cached_keys": L, "n_splits": S}
 
 
-def device_rooflines(torch, probe=True):
+def run_tiny_ring(torch, cp, si):
+    """The tiny fp32 Pass-KV ring (T=256, CP 4, 4 query heads, 1 KV head, D=64): all 4 ranks on
+    the device; the outputs are kept for the oracle leg."""
+    cfg = si.CONFIGS["tiny_ring_fp32"]
+    N, n_h, n_kv, d, L = cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["seqs"][0]
+    ranges = [(0, 0, L)]
+    shards = [cp.shard_map(ranges, N, r) for r in range(N)]
+    dev = lambda tid, toks, shape: si.normal_tokens(0, tid, toks, shape, cfg["std"]).cuda()
+    ks = [dev(si.TID_K, t, (n_kv, d)) for _, t in shards]
+    vs = [dev(si.TID_V, t, (n_kv, d)) for _, t in shards]
+    outs = []
+    t = Timer(torch)
+    with t:
+        for r in range(N):
+            q = dev(si.TID_Q, shards[r][1], (n_h, d))
+            o = torch.empty(q.shape[0], n_h, d, device="cuda")
+            lse = torch.empty(q.shape[0], n_h, device="cuda")
+            cp.ring_pass_kv(q, shards[r][0], r, ks, vs, [s for s, _ in shards], True,
+                            1.0 / math.sqrt(d), o, lse, o_acc=o, lse_acc=lse)
+            outs.append((o, lse))
+    ms = t.ms()
+    return {"ms_all_ranks_incl_uploads": round(ms, 3)}, [(o.cpu().numpy(), l.cpu().numpy()) for o, l in outs]
+
+
+def device_rooflines(torch):
     """Peaks derived from the device's reported attributes, next to the published figures, and
     the achievable device-to-device copy bandwidth (1 GiB read + 1 GiB written)."""
     import ctypes
@@ -234,132 +459,11 @@ def device_rooflines(torch, probe=True):
     info["copy_gbs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
     info["published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     del src, dst
-    info["mfma_probe"] = run_mfma_probe() if probe else None
     log(f"device: {info}")
     return info
 
 
-def run_mfma_probe():
-    """The MFMA clock probe (a separate program, run as a child process): the bf16 MFMA rate and
-    shader clock the chip sustains with random and with near-constant operands. None if the probe
-    is not built or fails."""
-    import subprocess
-    exe = os.path.join(ROOT, "context_ring_attention_amd", "probe_mfma_clock")
-    if not os.path.exists(exe):
-        log("mfma probe: not built")
-        return None
-    try:
-        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
-    except subprocess.TimeoutExpired:
-        log("mfma probe: timed out")
-        return None
-    if res.returncode != 0:
-        log(f"mfma probe failed ({res.returncode}): {res.stderr.strip()[-300:]}")
-        return None
-    info = json.loads(res.stdout.strip().splitlines()[-1])
-    log(f"mfma probe: {info}")
-    return info
-
-
-def run_pass_q(torch, cp, si, seed=0):
-    cfg = si.CONFIGS["persistent_kv_8k_on_120k"]
-    P, T, N, n_h, n_kv, d = cfg["cached"], cfg["new"], cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
-    q_ranges = [(0, P, P + T)]
-    kv_ranges = [(0, 0, P), (0, P, P + T)]
-    qsh = [cp.shard_map(q_ranges, N, r) for r in range(N)]
-    ksh = [cp.shard_map(kv_ranges, N, r) for r in range(N)]
-    qs = [bf16_tokens(torch, si, seed, si.TID_Q, t, (n_h, d)) for _, t in qsh]
-    ks = [bf16_tokens(torch, si, seed, si.TID_K, t, (n_kv, d)) for _, t in ksh]
-    vs = [bf16_tokens(torch, si, seed, si.TID_V, t, (n_kv, d)) for _, t in ksh]
-    parts_o = [torch.empty(qs[i // N].shape[0], n_h, d, device="cuda") for i in range(N * N)]
-    parts_l = [torch.empty(qs[i // N].shape[0], n_h, device="cuda") for i in range(N * N)]
-    o = [torch.empty(x.shape[0], n_h, d, device="cuda") for x in qs]
-    l = [torch.empty(x.shape[0], n_h, device="cuda") for x in qs]
-    scale = 1.0 / math.sqrt(d)
-    fn = lambda: cp.ring_pass_q(qs, [s for s, _ in qsh], ks, vs, [s for s, _ in ksh], True, scale,
-                                parts_o, parts_l, o, l)
-    ms = time_reps(torch, fn, 5)
-    pairs = sum(visible_pairs(qsh[a][0], ksh[b][0]) for a in range(N) for b in range(N))
-    flops = 4 * d * n_h * pairs
-    tf = flops / (ms * 1e-3) / 1e12
-    log(f"pass-q: {ms:.2f} ms, {tf:.1f} useful TFLOP/s")
-    return {"metric": "causal-useful TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
-            "ms_per_call": round(ms, 3), "useful_tflop": round(flops / 1e12, 3),
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-
-
-def run_merge(torch, cp, parts_o, parts_l, d):
-    rows = parts_o[0].numel() // d
-    out = torch.empty(rows, d, device="cuda")
-    lse = torch.empty(rows, device="cuda")
-    fn = lambda: cp.merge_lse(parts_o, parts_l, out, lse)
-    ms = time_reps(torch, fn, 10)
-    seen = sum(int(torch.isfinite(x).sum()) for x in parts_l)
-    alg = seen * d * 4 + len(parts_l) * rows * 4 + rows * (d * 4 + 4)
-    gbs = alg / (ms * 1e-3) / 1e9
-    log(f"merge: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
-    return {"metric": "merge GB/s", "value": round(gbs, 1), "unit": "GB/s",
-            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": alg, "parts": len(parts_l),
-            "rows": rows, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-
-
-def run_prefill_1m(torch, cp, si, seed=0, rank=0):
-    cfg = si.CONFIGS["prefill_1m_varlen_cp8"]
-    N, n_h, n_kv, d = cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
-    ranges = [(i, 0, L) for i, L in enumerate(cfg["seqs"])]
-    shards = [cp.shard_map(ranges, N, r) for r in range(N)]
-    ks = [bf16_tokens(torch, si, seed, si.TID_K, t, (n_kv, d)) for _, t in shards]
-    vs = [bf16_tokens(torch, si, seed, si.TID_V, t, (n_kv, d)) for _, t in shards]
-    q = bf16_tokens(torch, si, seed, si.TID_Q, shards[rank][1], (n_h, d))
-    o = torch.empty(q.shape[0], n_h, d, device="cuda")
-    l = torch.empty(q.shape[0], n_h, device="cuda")
-    scale = 1.0 / math.sqrt(d)
-    fn = lambda: cp.ring_pass_kv(q, shards[rank][0], rank, ks, vs, [s for s, _ in shards], True,
-                                 scale, o, l, o_acc=o, lse_acc=l)
-    ms = time_reps(torch, fn, 3, warm=1)
-    pairs = sum(visible_pairs(shards[rank][0], shards[s][0]) for s in range(N))
-    flops = 4 * d * n_h * pairs
-    tf = flops / (ms * 1e-3) / 1e12
-    log(f"prefill 1M varlen CP8 rank {rank}: {ms:.1f} ms, {tf:.1f} useful TFLOP/s")
-    return {"metric": "causal-useful TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
-            "ms_per_rank": round(ms, 2), "useful_tflop": round(flops / 1e12, 3), "rank": rank,
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-
-
-def run_cpu_baseline(si, ranges, N, n_h, n_kv, d, seed, budget_s):
-    """The fp64 oracle as it stands, on rank 0's Q shard: whole query tokens (all 16 heads),
-    spread evenly over the shard, each against its full visible key set (all 4 KV shards)."""
-    import oracle
-    q_seq, q_pos, q_glob = oracle.shard_tokens(ranges, N, 0)
-    ks, vs, kseq, kpos = [], [], [], []
-    for s in range(N):
-        sq, ps, gl = oracle.shard_tokens(ranges, N, s)
-        ks.append(si.to_dtype(si.normal_tokens(seed, si.TID_K, gl, (n_kv, d)), "bf16")[1].numpy())
-        vs.append(si.to_dtype(si.normal_tokens(seed, si.TID_V, gl, (n_kv, d)), "bf16")[1].numpy())
-        kseq.append(sq)
-        kpos.append(ps)
-    kf, vf = np.concatenate(ks), np.concatenate(vs)
-    kseq, kpos = np.concatenate(kseq), np.concatenate(kpos)
-    qf = si.to_dtype(si.normal_tokens(seed, si.TID_Q, q_glob, (n_h, d)), "bf16")[1].numpy()
-    order = np.random.default_rng(seed).permutation(len(q_glob))
-    done, flops, spent = 0, 0, 0.0
-    batch = 8
-    while spent < budget_s and done < len(order):
-        rows = np.sort(order[done:done + batch])
-        t0 = time.perf_counter()
-        oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, True, 1.0 / math.sqrt(d),
-                         rows=rows)
-        spent += time.perf_counter() - t0
-        flops += 4 * d * n_h * int((q_pos[rows] + 1).sum())
-        done += len(rows)
-    tf = flops / spent / 1e12
-    log(f"oracle: {done} query tokens in {spent:.1f}s on {oracle.num_threads()} threads, {tf * 1e3:.2f} GFLOP/s")
-    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} random query tokens (x{n_h} heads) of rank 0's 32K-token Q shard of "
-                      f"prefill_128k_cp4, each against its full visible key set; {spent:.1f} s of fp64 work",
-            "host": {"cpu_model": host_cpu_model(), "logical_cpus": os.cpu_count()}}
-
-
+# --------------------------------------------------------------------------- the oracle leg
 def host_cpu_model():
     """The host CPU's model name from /proc/cpuinfo (None where it is not available)."""
     try:
@@ -370,6 +474,161 @@ def host_cpu_model():
     except OSError:
         pass
     return None
+
+
+def run_cpu_baseline(si, budget_s, headline, kept):
+    """The fp64 oracle as it stands, timed on the host cores.
+
+    - Headline (value): rank 0's Q shard of the 1M-token workload: the first and last token of
+      every chunk, then random tokens (all 16 heads each) until budget_s of oracle time, each
+      against its full visible key set. The rows are compared with the device's output of the
+      same run. The whole-workload oracle time is extrapolated from the measured rate.
+    - The 128K CP4 and persistent-KV workloads: a few tokens each, timed, compared with the
+      device's output, and extrapolated the same way (labelled).
+    - The tiny fp32 ring and the B = 32 decode: run in full, timed, compared with the device.
+    """
+    import oracle
+
+    def max_err(o_dev, l_dev, o_ref, l_ref):
+        fin = np.isfinite(l_ref)
+        return (float(np.max(np.abs(o_dev - o_ref))),
+                float(np.max(np.abs(l_dev[fin] - l_ref[fin]))) if fin.any() else 0.0,
+                bool(np.array_equal(np.isneginf(l_dev), np.isneginf(l_ref))))
+
+    def keys_of(ranges, N, seed, n_kv, d):
+        seq, pos, glob = [], [], []
+        for s in range(N):
+            a, b, c = oracle.shard_tokens(ranges, N, s)
+            seq.append(a), pos.append(b), glob.append(c)
+        seq, pos, glob = np.concatenate(seq), np.concatenate(pos), np.concatenate(glob)
+        kf = si.to_dtype(si.normal_tokens(seed, si.TID_K, glob, (n_kv, d)), "bf16")[1].numpy()
+        vf = si.to_dtype(si.normal_tokens(seed, si.TID_V, glob, (n_kv, d)), "bf16")[1].numpy()
+        return kf, vf, seq, pos
+
+    def sampled(ranges, N, q_ranges, n_h, n_kv, d, rows_first, budget, seed=0, per_seq=True):
+        """Oracle rows of Q shard 0 (ranks' Q from q_ranges), rows_first first, then random rows
+        until `budget` seconds. Returns rows, (o, lse), seconds, useful flops."""
+        kf, vf, kseq, kpos = keys_of(ranges, N, seed, n_kv, d)
+        q_seq, q_pos, q_glob = oracle.shard_tokens(q_ranges, N, 0)
+        rng = np.random.default_rng(seed)
+        order = list(rows_first) + [int(x) for x in rng.permutation(len(q_glob)) if x not in set(rows_first)]
+        done, spent, flops = [], 0.0, 0
+        outs_o, outs_l = [], []
+        scale = 1.0 / math.sqrt(d)
+        by_seq = {s: np.flatnonzero(kseq == s) for s in np.unique(kseq)} if per_seq else None
+        i = 0
+        while i < len(order) and (i < len(rows_first) or spent < budget):
+            row = order[i]
+            i += 1
+            qf = si.to_dtype(si.normal_tokens(seed, si.TID_Q, q_glob[row:row + 1], (n_h, d)), "bf16")[1].numpy()
+            sel = by_seq[q_seq[row]]
+            t0 = time.perf_counter()
+            o, l = oracle.attention(qf, kf[sel], vf[sel], n_h, n_kv, q_seq[row:row + 1], q_pos[row:row + 1],
+                                    kseq[sel], kpos[sel], True, scale)
+            spent += time.perf_counter() - t0
+            vis = int(np.sum(kpos[sel] <= q_pos[row]))
+            flops += 4 * d * n_h * vis
+            done.append(row)
+            outs_o.append(o)
+            outs_l.append(l)
+        return np.array(done), np.concatenate(outs_o), np.concatenate(outs_l), spent, flops
+
+    res = {"kind": "oracle", "cores": oracle.num_threads(),
+           "host": {"cpu_model": host_cpu_model(), "logical_cpus": os.cpu_count()}, "configs": {}}
+    wl = headline
+    # ---- headline: 1M varlen CP8, rank 0
+    first = sample_tokens(wl.shards[0][0], 0, 0).tolist()
+    rows, o_ref, l_ref, spent, flops = sampled(wl.ranges, wl.N, wl.ranges, wl.n_h, wl.n_kv, wl.d,
+                                                first, budget_s)
+    o_dev, l_dev = wl.sample_outputs(0, rows)
+    eo, el, pattern = max_err(o_dev, l_dev, o_ref, l_ref)
+    rate = flops / spent
+    res["value"] = round(rate / 1e12, 6)
+    res["unit"] = "TFLOP/s"
+    res["sample"] = (f"{len(rows)} query tokens x {wl.n_h} heads = {len(rows) * wl.n_h} rows of rank 0's "
+                     f"128K-token Q shard of {HEADLINE} (the first and last token of each of its "
+                     f"{len(first) // 2} chunks, then random tokens), each against its full visible key "
+                     f"set; {spent:.1f} s of fp64 work")
+    full_s = wl.flops / rate
+    res["configs"][HEADLINE] = {
+        "oracle_s_per_rank_extrapolated": round(full_s, 1), "label": "extrapolated from the sample's rate",
+        "sample_rows": int(len(rows) * wl.n_h), "sample_s": round(spent, 2),
+        "parity_vs_gpu": {"max_abs_dO": eo, "max_abs_dLSE": el, "empty_rows_match": pattern,
+                          "pass": bool(eo <= 2e-2 and el <= 1e-3 and pattern)}}
+    log(f"oracle {HEADLINE}: {len(rows)} tokens in {spent:.1f}s on {res['cores']} threads "
+        f"({rate / 1e9:.2f} GFLOP/s useful); vs GPU max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+
+    # ---- 128K CP4 (rank 0) and persistent KV (Q shard 0): sampled, extrapolated
+    for name, key in (("prefill_128k_cp4", "r128k"), ("persistent_kv_8k_on_120k", "pkv")):
+        if key not in kept:
+            continue
+        cfg = si.CONFIGS[name]
+        if name == "prefill_128k_cp4":
+            ranges = q_ranges = [(0, 0, cfg["seqs"][0])]
+        else:
+            P, T = cfg["cached"], cfg["new"]
+            ranges, q_ranges = [(0, 0, P), (0, P, P + T)], [(0, P, P + T)]
+        dev = kept[key]
+        rows, o_ref, l_ref, spent, flops = sampled(ranges, cfg["cp"], q_ranges, cfg["n_h"], cfg["n_kv"],
+                                                    cfg["d_h"], dev["rows"].tolist(), 0.0)
+        assert np.array_equal(rows, dev["rows"])
+        eo, el, pattern = max_err(dev["o"], dev["lse"], o_ref, l_ref)
+        total_flops = dev["flops"]
+        res["configs"][name] = {
+            "oracle_s_extrapolated": round(total_flops / (flops / spent), 1),
+            "label": "extrapolated from the sample's rate", "sample_rows": int(len(rows) * cfg["n_h"]),
+            "sample_s": round(spent, 2),
+            "parity_vs_gpu": {"max_abs_dO": eo, "max_abs_dLSE": el, "empty_rows_match": pattern,
+                              "pass": bool(eo <= 2e-2 and el <= 1e-3 and pattern)}}
+        log(f"oracle {name}: {len(rows)} tokens in {spent:.1f}s; vs GPU max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+
+    # ---- tiny fp32 ring: full
+    if "tiny" in kept:
+        cfg = si.CONFIGS["tiny_ring_fp32"]
+        N, n_h, n_kv, d, L = cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"], cfg["seqs"][0]
+        ranges = [(0, 0, L)]
+        kseq, kpos, kglob = [np.concatenate(x) for x in zip(*[oracle.shard_tokens(ranges, N, s) for s in range(N)])]
+        kf = si.normal_tokens(0, si.TID_K, kglob, (n_kv, d), cfg["std"]).numpy()
+        vf = si.normal_tokens(0, si.TID_V, kglob, (n_kv, d), cfg["std"]).numpy()
+        t0 = time.perf_counter()
+        errs = []
+        for r in range(N):
+            q_seq, q_pos, q_glob = oracle.shard_tokens(ranges, N, r)
+            qf = si.normal_tokens(0, si.TID_Q, q_glob, (n_h, d), cfg["std"]).numpy()
+            o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, q_seq, q_pos, kseq, kpos, True,
+                                            1.0 / math.sqrt(d))
+            errs.append(max_err(kept["tiny"][r][0], kept["tiny"][r][1], o_ref, l_ref))
+        spent = time.perf_counter() - t0
+        eo, el = max(e[0] for e in errs), max(e[1] for e in errs)
+        res["configs"]["tiny_ring_fp32"] = {
+            "oracle_s_full": round(spent, 3), "label": "full run (all 4 ranks)",
+            "parity_vs_gpu": {"max_abs_dO": eo, "max_abs_dLSE": el,
+                              "pass": bool(eo <= 1e-5 and el <= 1e-5 and all(e[2] for e in errs))}}
+        log(f"oracle tiny ring: {spent:.3f}s; vs GPU max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+
+    # ---- decode B=32: full
+    if "decode" in kept:
+        cfg = si.CONFIGS["decode_b32_32k_128k"]
+        B, n_h, n_kv, d = cfg["batch"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
+        dev = kept["decode"]
+        qf = si.to_dtype(si.normal_tokens(0, si.TID_Q, np.arange(B), (n_h, d)), "bf16")[1].numpy()
+        spent, eo, el = 0.0, 0.0, 0.0
+        for b in range(B):
+            lo, L = int(dev["offs"][b]), int(dev["lens"][b])
+            kf = si.to_dtype(si.normal_tokens(0, si.TID_K, np.arange(lo, lo + L), (n_kv, d)), "bf16")[1].numpy()
+            vf = si.to_dtype(si.normal_tokens(0, si.TID_V, np.arange(lo, lo + L), (n_kv, d)), "bf16")[1].numpy()
+            t0 = time.perf_counter()
+            o_ref, l_ref = oracle.attention(qf[b:b + 1], kf, vf, n_h, n_kv, np.zeros(1, np.int32),
+                                            np.array([L], np.int64), np.zeros(L, np.int32), np.arange(L),
+                                            False, 1.0 / math.sqrt(d))
+            spent += time.perf_counter() - t0
+            e = max_err(dev["o"][b:b + 1], dev["lse"][b:b + 1], o_ref, l_ref)
+            eo, el = max(eo, e[0]), max(el, e[1])
+        res["configs"]["decode_b32_32k_128k"] = {
+            "oracle_s_full": round(spent, 2), "label": "full run (all 32 requests, fp32 workspace output)",
+            "parity_vs_gpu": {"max_abs_dO": eo, "max_abs_dLSE": el, "pass": bool(eo <= 2e-2 and el <= 1e-3)}}
+        log(f"oracle decode B=32: {spent:.1f}s; vs GPU max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+    return res
 
 
 # --------------------------------------------------------------------------- main
@@ -391,94 +650,49 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     log(f"device {dev.name} {getattr(dev, 'gcnArchName', '')} CUs={dev.multi_processor_count}")
 
-    cfg = si.CONFIGS["prefill_128k_cp4"]
-    N, n_h, n_kv, d = cfg["cp"], cfg["n_h"], cfg["n_kv"], cfg["d_h"]
-    L = cfg["seqs"][0]
-    scale = 1.0 / math.sqrt(d)
-    seed = 0
-    ranges = [(0, 0, L)]
-    shards = [cp.shard_map(ranges, N, r) for r in range(N)]
-    t0 = time.time()
-    ks = [bf16_tokens(torch, si, seed, si.TID_K, t, (n_kv, d)) for _, t in shards]
-    vs = [bf16_tokens(torch, si, seed, si.TID_V, t, (n_kv, d)) for _, t in shards]
-    qs = [bf16_tokens(torch, si, seed, si.TID_Q, t, (n_h, d)) for _, t in shards]
-    log(f"inputs generated in {time.time() - t0:.1f}s")
-    kv_segs = [s for s, _ in shards]
-    tq = [q.shape[0] for q in qs]
-    o = [torch.empty(t, n_h, d, device="cuda") for t in tq]
-    lse = [torch.empty(t, n_h, device="cuda") for t in tq]
-    parts = None
-    if args.mode == "partials":
-        parts = [([torch.empty(t, n_h, d, device="cuda") for _ in range(N)],
-                  [torch.empty(t, n_h, device="cuda") for _ in range(N)]) for t in tq]
-
-    pairs = [[visible_pairs(shards[r][0], shards[s][0]) for s in range(N)] for r in range(N)]
-    flops_step = sum(4 * d * n_h * sum(row) for row in pairs)
-
-    def step():
-        for r in range(N):
-            if parts is None:
-                cp.ring_pass_kv(qs[r], shards[r][0], r, ks, vs, kv_segs, True, scale, o[r], lse[r],
-                                o_acc=o[r], lse_acc=lse[r])
-            else:
-                cp.ring_pass_kv(qs[r], shards[r][0], r, ks, vs, kv_segs, True, scale, o[r], lse[r],
-                                o_parts=parts[r][0], lse_parts=parts[r][1])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_step = elapsed * 1e3 / args.steps
-    value = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"prefill_128k_cp4: {ms_step:.2f} ms/step (4 ranks), {value:.1f} useful TFLOP/s")
+    # ---- headline: rank 0's ring over the 1M-token varlen batch at CP 8
+    wl = PassKV(torch, cp, si, HEADLINE, ranks=[0], mode=args.mode)
+    ms_step = run_timed_steps(torch, wl, cp, args.steps, args.warmup)
+    value = wl.flops / (ms_step * 1e-3) / 1e12
+    log(f"{HEADLINE}: {ms_step:.2f} ms/step (rank 0's ring of {wl.N} steps), {value:.1f} useful TFLOP/s")
 
     # ---- dominant kernel: per-launch time of cp_partial_attn (one ring step of one rank) ----
-    launch_ms, launch_flops = [], []
-    tmr = Timer(torch)
-    for _ in range(2):
-        for r in range(N):
-            for t in range(N):
-                s = (r - t) % N
-                with tmr:
-                    cp.partial_attn(qs[r], ks[s], vs[s], shards[r][0], shards[s][0], True, scale,
-                                    o[r], lse[r], accumulate=t > 0)
-                launch_ms.append(tmr.ms())
-                launch_flops.append(4 * d * n_h * pairs[r][s])
-    avg_ms = float(np.mean(launch_ms))
-    avg_flops = float(np.mean(launch_flops))
+    avg_ms, avg_flops, n_launch = wl.per_launch(torch, cp, passes=2)
     achieved = avg_flops / (avg_ms * 1e-3) / 1e12
     rec = recorded_traffic()
     traffic = None if rec is None else rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "attn_bf16_kernel<128> (cp_partial_attn)",
-                "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": avg_flops}
+                "kernel": "attn_bf16_kernel<128, 8> (cp_partial_attn)",
+                "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": avg_flops,
+                "launches_timed": n_launch}
     if rec is not None:
         roofline["traffic_detail"] = {"unit": "bytes per launch", "read": rec["fetch_bytes_per_launch"],
                                       "write": rec["write_bytes_per_launch"],
+                                      "algorithmic": rec.get("algorithmic_bytes_per_launch"),
                                       "source": os.path.relpath(COUNTERS_MD, ROOT)}
     log(f"cp_partial_attn: avg {avg_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s, "
         f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    # the per-launch timing re-ran the whole ring, so the outputs are rank 0's result again
 
-    secondary = {}
+    secondary, kept = {}, {}
     if not args.no_secondary:
-        # merge of rank 0's four ring partials (the partials mode of the same workload)
-        po = [torch.empty(tq[0], n_h, d, device="cuda") for _ in range(N)]
-        pl = [torch.empty(tq[0], n_h, device="cuda") for _ in range(N)]
-        for t in range(N):
-            cp.partial_attn(qs[0], ks[(0 - t) % N], vs[(0 - t) % N], shards[0][0],
-                            shards[(0 - t) % N][0], True, scale, po[t], pl[t])
-        secondary["merge_4parts_128k_cp4"] = run_merge(torch, cp, po, pl, d)
-        del po, pl
-        secondary["decode_b32_32k_128k"] = run_decode(torch, cp, si)
+        s128, wl128, r0 = run_prefill_128k(torch, cp, si, args.steps)
+        secondary["prefill_128k_cp4"] = s128
+        r0["flops"] = wl128.flops
+        kept["r128k"] = r0
+        secondary["merge_4parts_128k_cp4"] = run_merge(torch, cp, wl128)
+        del wl128
+        torch.cuda.empty_cache()
+        spkv, r0 = run_persistent_kv(torch, cp, si)
+        cfg3 = si.CONFIGS["persistent_kv_8k_on_120k"]
+        r0["flops"] = spkv["useful_tflop"] * 1e12
+        secondary["persistent_kv_8k_on_120k"] = spkv
+        kept["pkv"] = r0
+        secondary["decode_b32_32k_128k"], kept["decode"] = run_decode(torch, cp, si)
         secondary["decode_step_b1_128k_graph"] = run_decode_step_graph(torch, cp, si)
-        secondary["persistent_kv_8k_on_120k"] = run_pass_q(torch, cp, si)
-        if args.extended:
-            secondary["prefill_1m_varlen_cp8"] = run_prefill_1m(torch, cp, si)
+        secondary["tiny_ring_fp32"], kept["tiny"] = run_tiny_ring(torch, cp, si)
+        del cfg3
 
     if args.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -487,15 +701,11 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 1 GiB read, 1 GiB written")
 
-    device_info = device_rooflines(torch, probe=not args.no_mfma_probe) if not args.no_secondary else None
-    probe = (device_info or {}).get("mfma_probe")
-    if probe and probe.get("random", {}).get("tflops"):
-        # the same kernel rate against what MFMA-only code sustains on random operands
-        roofline["frac_of_mfma_probe_random"] = round(achieved / probe["random"]["tflops"], 3)
+    device_info = device_rooflines(torch) if not args.no_secondary else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = run_cpu_baseline(si, ranges, N, n_h, n_kv, d, seed, args.cpu_seconds)
+        cpu = run_cpu_baseline(si, args.cpu_seconds, wl, kept)
 
     out = {
         "metric": "causal-useful attention TFLOP/s per rank shard",
@@ -510,10 +720,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_128k_cp4", "seq_len": L, "cp_world": N,
-                   "ranks_per_step": N, "q_heads": n_h, "kv_heads": n_kv, "head_dim": d,
+        "config": {"workload": HEADLINE, "seq_lens": wl.cfg["seqs"], "cp_world": wl.N,
+                   "rank": 0, "q_heads": wl.n_h, "kv_heads": wl.n_kv, "head_dim": wl.d,
                    "causal": True, "ring": "pass_kv", "merge_mode": args.mode,
-                   "useful_tflop_per_step": round(flops_step / 1e12, 3)},
+                   "useful_tflop_per_step": round(wl.flops / 1e12, 3)},
         "roofline": roofline,
         "device": device_info,
         "cpu_baseline": cpu,
