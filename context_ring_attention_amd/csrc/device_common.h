@@ -53,17 +53,23 @@ __device__ inline void running_merge_weights(float lse_prev, float lse_new, floa
 
 // Max of x over lanes l and l ^ 32 (the two half-waves), without going through LDS: swapping
 // the upper half of one copy with the lower half of another leaves each lane holding both values.
+// Each result is copied out of the returned vector before its bit cast: a bit cast of a vector
+// element expression reads element 0 whatever the index (seen with this compiler), which would
+// leave each lane with one half-wave's value only (harmless while scores are close, an exp2
+// overflow once they spread over more than 128 base-2 units).
 __device__ inline float max_xor32(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+  const uint32_t r0 = sw[0], r1 = sw[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // Max of x over lanes l and l ^ 16 (odd and even 16-lane rows), without going through LDS.
 __device__ inline float max_xor16(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+  const uint32_t r0 = sw[0], r1 = sw[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 }  // namespace cpk
