@@ -20,11 +20,13 @@ CP_OK, CP_E_ARG, CP_E_SHAPE, CP_E_UNSUPPORTED, CP_E_CAPACITY, CP_E_HIP = 0, -1, 
 CP_F32, CP_BF16 = 0, 1
 CP_MAX_SEGMENTS = 64
 CP_MAX_MERGE_PARTS = 64
+CP_DECODE_NOALLOC_MAX_BYTES = 72 * 1024 * 1024
 
 CP_PASS_KV, CP_PASS_Q = 0, 1
 
 EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
             "cp_decode_workspace_bytes", "cp_decode_splitkv_ex", "cp_decode_workspace_bytes_ex",
+            "cp_decode_splitkv_noalloc",
             "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant", "cp_status_string",
             "cp_last_error")
 
@@ -81,6 +83,8 @@ def load():
     lib.cp_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.cp_decode_splitkv_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f, i32, vp,
                                          vp, vp, i32, vp, vp]
+    lib.cp_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f, i32,
+                                              vp, i32, vp, vp]
     lib.cp_decode_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32]
     lib.cp_decode_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.cp_ring_pass_kv.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
@@ -96,7 +100,7 @@ def load():
                                            ctypes.c_double, ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]
     for name in ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
-                 "cp_decode_splitkv_ex", "cp_ring_pass_kv", "cp_ring_pass_q",
+                 "cp_decode_splitkv_ex", "cp_decode_splitkv_noalloc", "cp_ring_pass_kv", "cp_ring_pass_q",
                  "cp_select_ring_variant"):
         getattr(lib, name).restype = ctypes.c_int
     lib.cp_status_string.argtypes = [ctypes.c_int]
@@ -331,6 +335,31 @@ def decode_splitkv(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int, softma
                                      _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
                                      float(softmax_scale), _ptr(ws_o), _ptr(ws_lse), _ptr(o_out),
                                      _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def decode_splitkv_noalloc(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int,
+                           softmax_scale: float, o_out, lse_out=None, ws_dtype="f32", stream=None,
+                           check: bool = True):
+    """cp_decode_splitkv_noalloc: decode with the split workspace in the library's own device
+    array (no workspace argument, nothing allocated). Arguments as decode_splitkv."""
+    lib = load()
+    B, n_h, d = q.shape
+    n_kv = k_cache.shape[1]
+    if check:
+        bf16, i64, f32 = _types("bf16"), _types("i64"), _types("f32")
+        _req(q, "q", bf16)
+        _req(k_cache, "k_cache", bf16)
+        _req(v_cache, "v_cache", bf16, k_cache.shape)
+        if k_cache.dim() != 3 or k_cache.shape[2] != d:
+            raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected [tokens, n_kv, {d}]")
+        _req(kv_offset, "kv_offset", i64, (B,))
+        _req(kv_len, "kv_len", i64, (B,))
+        _req(o_out, "o_out", _types("inp"), (B, n_h, d))
+        _req(lse_out, "lse_out", f32, numel=B * n_h)
+    _check(lib.cp_decode_splitkv_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offset),
+                                         _ptr(kv_len), B, n_h, n_kv, d, _dtype_code(q), n_splits,
+                                         float(softmax_scale), _ws_code(ws_dtype), _ptr(o_out),
+                                         _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,

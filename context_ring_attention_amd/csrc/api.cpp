@@ -348,11 +348,13 @@ size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits) {
   return cp_decode_workspace_bytes_ex(batch, n_h, d_h, n_splits, CP_F32);
 }
 
-int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache,
-                         const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
-                         int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
-                         cp_dtype ws_dtype, void* ws_o, float* ws_lse, void* o_out,
-                         cp_dtype out_dtype, float* lse_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a decode call, apart from the workspace (nothing is launched).
+int validate_decode(int batch, int n_h, int n_kv, int d_h, cp_dtype in_dtype, int n_splits,
+                    float softmax_scale, cp_dtype ws_dtype, cp_dtype out_dtype) {
   int st = check_heads(n_h, n_kv, d_h);
   if (st) return st;
   if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "decode supports bf16 inputs only");
@@ -367,6 +369,20 @@ int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache
   // the merge grid has one workgroup per (request, head) in one 32-bit dimension, 256 threads each
   if ((int64_t)batch * n_h * 256 > (int64_t)UINT32_MAX)
     return fail(CP_E_UNSUPPORTED, "batch * n_h = %lld too large", (long long)batch * n_h);
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                         int n_kv, int d_h, cp_dtype in_dtype, int n_splits, float softmax_scale,
+                         cp_dtype ws_dtype, void* ws_o, float* ws_lse, void* o_out,
+                         cp_dtype out_dtype, float* lse_out, void* stream) {
+  int st = validate_decode(batch, n_h, n_kv, d_h, in_dtype, n_splits, softmax_scale, ws_dtype, out_dtype);
+  if (st) return st;
   if (batch == 0) return ok();
   if (!q || !k_cache || !v_cache || !kv_offset || !kv_len || !ws_o || !ws_lse || !o_out)
     return fail(CP_E_ARG, "NULL pointer argument");
@@ -385,13 +401,35 @@ int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache
   p.batch = batch;
   p.n_h = n_h;
   p.n_kv = n_kv;
-  p.group = group;
+  p.group = n_h / n_kv;
   p.n_splits = n_splits;
   p.out_bf16 = out_dtype == CP_BF16;
   p.ws_bf16 = ws_dtype == CP_BF16;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_status(cpk::launch_decode(p, d_h, static_cast<hipStream_t>(stream)), "cp_decode_splitkv");
+}
+
+int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                              int n_kv, int d_h, cp_dtype in_dtype, int n_splits,
+                              float softmax_scale, cp_dtype ws_dtype, void* o_out,
+                              cp_dtype out_dtype, float* lse_out, void* stream) {
+  int st = validate_decode(batch, n_h, n_kv, d_h, in_dtype, n_splits, softmax_scale, ws_dtype, out_dtype);
+  if (st) return st;
+  const size_t need = cp_decode_workspace_bytes_ex(batch, n_h, d_h, n_splits, ws_dtype);
+  if (need > (size_t)CP_DECODE_NOALLOC_MAX_BYTES)
+    return fail(CP_E_CAPACITY, "the split workspace needs %zu bytes; the library's scratch array holds %zu",
+                need, (size_t)CP_DECODE_NOALLOC_MAX_BYTES);
+  if (batch == 0) return ok();
+  void* ws = nullptr;
+  const hipError_t e = cpk::decode_scratch(&ws);
+  if (e != hipSuccess) return fail(CP_E_HIP, "cp_decode_splitkv_noalloc: scratch lookup: %s", hipGetErrorString(e));
+  const size_t o_bytes = (size_t)batch * n_splits * n_h * d_h * (ws_dtype == CP_BF16 ? 2 : 4);
+  float* ws_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + o_bytes);
+  return cp_decode_splitkv_ex(q, k_cache, v_cache, kv_offset, kv_len, batch, n_h, n_kv, d_h,
+                              in_dtype, n_splits, softmax_scale, ws_dtype, ws, ws_lse, o_out,
+                              out_dtype, lse_out, stream);
 }
 
 int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,

@@ -92,6 +92,9 @@ hipError_t launch_attn_f32(const AttnParams& p, int d_h, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream);
+// Device address of the allocation-free decode workspace (CP_DECODE_NOALLOC_MAX_BYTES) on the
+// current device; looked up once per device, then cached.
+hipError_t decode_scratch(void** out);
 
 // Rows per workgroup tile of each attention kernel (the host plans tiles with these).
 constexpr int kTileRowsF32 = 64;

@@ -24,6 +24,8 @@
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
+#include <mutex>
+
 #include "device_common.h"
 
 namespace cpk {
@@ -428,6 +430,36 @@ hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
     else launch_decode_d<128, false>(p, grid, mgrid, wide, stream);
   }
   return hipGetLastError();
+}
+
+// ---- the allocation-free variant: the split workspace in a file-scope device array -------------
+// For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+// loops, harnesses that forbid allocation). Each device the library runs on holds its own copy of
+// this array until the process ends. Host code never uses the array's name as an address (on the
+// host it is only a stand-in): the device address is looked up once per device with
+// hipGetSymbolAddress and cached.
+static __device__ __align__(256) unsigned char scratch[CP_DECODE_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // on the current device
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace cpk

@@ -160,6 +160,27 @@ int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache
                          cp_dtype out_dtype, float* lse_out, void* stream);
 size_t cp_decode_workspace_bytes_ex(int batch, int n_h, int d_h, int n_splits, cp_dtype ws_dtype);
 
+/* Bytes of the device array cp_decode_splitkv_noalloc keeps its split workspace in (72 MiB: the
+ * fp32 workspace of 32 requests x 256 splits x 16 heads x D_H 128 takes 64.5 MiB). */
+#define CP_DECODE_NOALLOC_MAX_BYTES (72u * 1024u * 1024u)
+
+/* cp_decode_splitkv_noalloc -- cp_decode_splitkv_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the split workspace lives in a file-scope device array of CP_DECODE_NOALLOC_MAX_BYTES inside
+ * the library, not in an argument. Each device the library runs on holds its own copy until the
+ * process ends; the call allocates and frees nothing. The caller still passes inputs and outputs.
+ * Returns CP_E_CAPACITY (nothing launched) when cp_decode_workspace_bytes_ex(batch, n_h, d_h,
+ * n_splits, ws_dtype) exceeds CP_DECODE_NOALLOC_MAX_BYTES; CP_E_HIP if the array's device address
+ * cannot be looked up. Every call on a device shares that device's array, which keeps the last
+ * call's partials (every split's partial is rewritten, so nothing needs clearing): calls that
+ * overlap on one device (different streams, threads or processes) race and must not be issued.
+ * Other arguments and errors as cp_decode_splitkv_ex. */
+int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int64_t* kv_offset, const int64_t* kv_len, int batch, int n_h,
+                              int n_kv, int d_h, cp_dtype in_dtype, int n_splits,
+                              float softmax_scale, cp_dtype ws_dtype, void* o_out,
+                              cp_dtype out_dtype, float* lse_out, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * cp_ring_pass_kv -- one rank's ring Pass-KV on one device ([CPMTI §3 "核心公式": each rank keeps
  * its Q shard while KV shards travel the ring for N-1 rounds; §3 Fig. 3). At step t the rank

@@ -17,5 +17,6 @@ hipError_t launch_attn_f32(const AttnParams&, int, hipStream_t) { return unexpec
 hipError_t launch_attn_bf16(const AttnParams&, int, hipStream_t) { return unexpected("launch_attn_bf16"); }
 hipError_t launch_merge(const MergeParams&, hipStream_t) { return unexpected("launch_merge"); }
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return unexpected("launch_decode"); }
+hipError_t decode_scratch(void**) { return unexpected("decode_scratch"); }
 
 }  // namespace cpk

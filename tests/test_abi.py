@@ -161,6 +161,16 @@ def test_merge_and_decode_reject_bad_arguments():
                None) == cp.CP_E_ARG                                    # bad workspace dtype
     assert dex(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 2000, 0.1, cp.CP_BF16, 16, 16, 16,
                cp.CP_F32, None, None) == cp.CP_E_UNSUPPORTED
+    # the allocation-free variant rejects a workspace beyond its array before any device call
+    noalloc = lib.cp_decode_splitkv_noalloc
+    assert noalloc(16, 16, 16, 16, 16, 64, 16, 1, 128, cp.CP_BF16, 256, 0.1, cp.CP_F32, 16, cp.CP_F32,
+                   None, None) == cp.CP_E_CAPACITY
+    assert "scratch array" in cp.last_error()
+    assert noalloc(16, 16, 16, 16, 16, 0, 16, 1, 128, cp.CP_BF16, 256, 0.1, cp.CP_F32, 16, cp.CP_F32,
+                   None, None) == cp.CP_OK                             # nothing to do, no lookup
+    assert noalloc(16, 16, 16, 16, 16, 2, 16, 1, 128, cp.CP_BF16, 256, 0.1, 9, 16, cp.CP_F32,
+                   None, None) == cp.CP_E_ARG
+    assert lib.cp_decode_workspace_bytes(32, 16, 128, 256) <= cp.CP_DECODE_NOALLOC_MAX_BYTES
     # grid limits are checked on the host: one merge workgroup of 256 threads per (request, head)
     assert dec(16, 16, 16, 16, 16, 65535, 4096, 4096, 128, cp.CP_BF16, 256, 0.1, 16, 16, 16,
                cp.CP_F32, None, None) == cp.CP_E_UNSUPPORTED
