@@ -41,10 +41,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kI32Max = 0x7fffffff;
 
-// Validates a segment table against a shard of `rows` rows and packs it for the kernels.
-int pack_segments(const cp_segment* segs, int n, int64_t rows, const char* what, cpk::Seg* out) {
-  if (n < 0 || n > cpk::kMaxSegs)
-    return fail(CP_E_CAPACITY, "%s: %d segments (1..%d supported)", what, n, cpk::kMaxSegs);
+// Segment tables longer than this are rejected (a sanity bound; tables of any length up to it are
+// split over as many launches as needed).
+constexpr int kMaxTableSegs = 1 << 20;
+
+// Validates a segment table against a shard of `rows` rows (nothing is packed or launched).
+int check_segments(const cp_segment* segs, int n, int64_t rows, const char* what) {
+  if (n < 0 || n > kMaxTableSegs)
+    return fail(CP_E_CAPACITY, "%s: %d segments (0..%d supported)", what, n, kMaxTableSegs);
   if (n > 0 && !segs) return fail(CP_E_ARG, "%s: segment table is NULL", what);
   for (int i = 0; i < n; ++i) {
     const cp_segment& s = segs[i];
@@ -56,9 +60,13 @@ int pack_segments(const cp_segment* segs, int n, int64_t rows, const char* what,
                   (long long)s.local_start, (long long)s.len, (long long)rows);
     if (s.len > kI32Max || s.pos_start > kI32Max - s.len)
       return fail(CP_E_UNSUPPORTED, "%s[%d]: positions beyond 2^31", what, i);
-    out[i] = cpk::Seg{s.seq_id, (int32_t)s.pos_start, (int32_t)s.len, (int32_t)s.local_start};
   }
   return CP_OK;
+}
+
+// The kernels' compact copy of a validated segment.
+cpk::Seg to_seg(const cp_segment& s) {
+  return cpk::Seg{s.seq_id, (int32_t)s.pos_start, (int32_t)s.len, (int32_t)s.local_start};
 }
 
 // Orders the Q runs (of all problems) by the causal work of their heaviest (last) tile,
@@ -131,10 +139,9 @@ int validate_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int 
     const Problem& pr = probs[i];
     if (pr.tq < 0 || pr.tk < 0) return fail(CP_E_ARG, "negative token count");
     if (pr.tq > kI32Max || pr.tk > kI32Max) return fail(CP_E_UNSUPPORTED, "token counts beyond 2^31");
-    cpk::Seg scratch[cpk::kMaxSegs];
-    st = pack_segments(pr.q_segs, pr.n_q_segs, pr.tq, "q_segs", scratch);
+    st = check_segments(pr.q_segs, pr.n_q_segs, pr.tq, "q_segs");
     if (st) return st;
-    st = pack_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs", scratch);
+    st = check_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs");
     if (st) return st;
     // the kernels index a Q run's (token, head-in-group) rows in 32 bits
     for (int j = 0; j < pr.n_q_segs; ++j)
@@ -170,8 +177,89 @@ int validate_merge(int n_parts, const float* const* o_parts, const float* const*
   return CP_OK;
 }
 
+// One launchable piece of a partial attention: a subset of a problem's Q runs (at most
+// kMaxSegs) against a subset of its KV runs (at most kMaxSegs), in one accumulation phase.
+// Phase 0 takes the caller's accumulate flag; later phases fold into what phase 0 wrote.
+struct Piece {
+  const Problem* pr;
+  std::vector<cp_segment> q, kv;
+  int phase;
+};
+
+// Splits a problem whose tables exceed one launch. Q runs are grouped by sequence (in order of
+// first appearance) and packed into groups of at most kMaxSegs runs; a group takes only the KV
+// runs of its own sequences (runs of other sequences are never visible to it). A group whose KV
+// runs exceed kMaxSegs is repeated with the next kMaxSegs KV runs in phase 1, 2, ...: each Q row
+// then merges the partials of its KV runs in order, as a ring step does. Rows stay disjoint
+// between the pieces of one phase.
+void split_problem(const Problem& pr, std::vector<Piece>& out) {
+  const int cap = cpk::kMaxSegs;
+  if (pr.n_q_segs <= cap && pr.n_kv_segs <= cap) {
+    out.push_back(Piece{&pr, std::vector<cp_segment>(pr.q_segs, pr.q_segs + pr.n_q_segs),
+                        std::vector<cp_segment>(pr.kv_segs, pr.kv_segs + pr.n_kv_segs), 0});
+    return;
+  }
+  std::map<int32_t, std::vector<cp_segment>> kv_by_seq;
+  for (int j = 0; j < pr.n_kv_segs; ++j)
+    if (pr.kv_segs[j].len > 0) kv_by_seq[pr.kv_segs[j].seq_id].push_back(pr.kv_segs[j]);
+  std::vector<int32_t> seq_order;
+  std::map<int32_t, std::vector<cp_segment>> q_by_seq;
+  for (int i = 0; i < pr.n_q_segs; ++i) {
+    const cp_segment& q = pr.q_segs[i];
+    if (q.len == 0) continue;
+    auto it = q_by_seq.find(q.seq_id);
+    if (it == q_by_seq.end()) {
+      seq_order.push_back(q.seq_id);
+      it = q_by_seq.emplace(q.seq_id, std::vector<cp_segment>()).first;
+    }
+    it->second.push_back(q);
+  }
+  // Groups of whole sequences while they fit; a sequence with more Q runs than one launch takes
+  // is cut into chunks of kMaxSegs runs, each with all of that sequence's KV runs.
+  struct Group {
+    std::vector<cp_segment> q, kv;
+  };
+  std::vector<Group> groups;
+  Group cur;
+  auto flush = [&]() {
+    if (!cur.q.empty()) groups.push_back(std::move(cur));
+    cur = Group();
+  };
+  for (int32_t sid : seq_order) {
+    const std::vector<cp_segment>& qs = q_by_seq[sid];
+    const std::vector<cp_segment>& ks = kv_by_seq[sid];
+    const int kv_first = (int)std::min<size_t>(ks.size(), cap);  // what phase 0 would add
+    if (qs.size() <= (size_t)cap && ks.size() <= (size_t)cap) {
+      if (cur.q.size() + qs.size() > (size_t)cap || cur.kv.size() + kv_first > (size_t)cap) flush();
+      cur.q.insert(cur.q.end(), qs.begin(), qs.end());
+      cur.kv.insert(cur.kv.end(), ks.begin(), ks.end());
+      continue;
+    }
+    flush();
+    for (size_t a = 0; a < qs.size(); a += cap) {
+      Group g;
+      g.q.assign(qs.begin() + a, qs.begin() + std::min(qs.size(), a + cap));
+      g.kv = ks;
+      groups.push_back(std::move(g));
+    }
+  }
+  flush();
+  for (const Group& g : groups) {
+    if (g.kv.empty()) {  // no visible key: phase 0 still writes the empty result (or keeps it)
+      out.push_back(Piece{&pr, g.q, {}, 0});
+      continue;
+    }
+    for (size_t b = 0, ph = 0; b < g.kv.size(); b += cap, ++ph)
+      out.push_back(Piece{&pr, g.q,
+                          std::vector<cp_segment>(g.kv.begin() + b, g.kv.begin() + std::min(g.kv.size(), b + cap)),
+                          (int)ph});
+  }
+}
+
 // Validates, then launches independent partial attentions, as few launches as the pooled segment
-// tables allow (problems are packed in order; a problem always fits a launch on its own).
+// tables allow (pieces are packed in order; a piece always fits a launch on its own). Problems
+// whose tables exceed one launch are split (split_problem); their later phases run after every
+// phase-0 launch, in order, on the same stream.
 int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, int d_h,
                           cp_dtype in_dtype, int causal, float softmax_scale, int accumulate,
                           void* stream, const char* what) {
@@ -179,40 +267,52 @@ int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, 
   if (st) return st;
   const bool bf16 = in_dtype == CP_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int next = 0;
-  while (next < n_probs) {
-    cpk::AttnParams p{};
-    p.n_h = n_h;
-    p.n_kv = n_kv;
-    p.group = n_h / n_kv;
-    p.causal = causal ? 1 : 0;
-    p.accumulate = accumulate;
-    p.scale = softmax_scale;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-    int nq = 0, nk = 0, np = 0;
-    while (next < n_probs && np < cpk::kMaxProblems &&
-           nq + probs[next].n_q_segs <= cpk::kMaxSegs && nk + probs[next].n_kv_segs <= cpk::kMaxSegs) {
-      const Problem& pr = probs[next++];
-      pack_segments(pr.q_segs, pr.n_q_segs, pr.tq, "q_segs", p.qs + nq);
-      pack_segments(pr.kv_segs, pr.n_kv_segs, pr.tk, "kv_segs", p.ks + nk);
-      for (int i = 0; i < pr.n_q_segs; ++i) p.q_prob[nq + i] = (int8_t)np;
-      p.kv_lo[np] = (int8_t)nk;
-      p.kv_hi[np] = (int8_t)(nk + pr.n_kv_segs);
-      p.q[np] = pr.q;
-      p.k[np] = pr.k;
-      p.v[np] = pr.v;
-      p.o[np] = pr.o;
-      p.lse[np] = pr.lse;
-      nq += pr.n_q_segs;
-      nk += pr.n_kv_segs;
-      ++np;
+  std::vector<Piece> pieces;
+  for (int i = 0; i < n_probs; ++i) split_problem(probs[i], pieces);
+  int n_phases = 0;
+  for (const Piece& pc : pieces) n_phases = std::max(n_phases, pc.phase + 1);
+  for (int phase = 0; phase < n_phases; ++phase) {
+    std::vector<const Piece*> todo;
+    for (const Piece& pc : pieces)
+      if (pc.phase == phase) todo.push_back(&pc);
+    size_t next = 0;
+    while (next < todo.size()) {
+      cpk::AttnParams p{};
+      p.n_h = n_h;
+      p.n_kv = n_kv;
+      p.group = n_h / n_kv;
+      p.causal = causal ? 1 : 0;
+      p.accumulate = phase == 0 ? accumulate : 1;
+      p.scale = softmax_scale;
+      p.scale_log2 = softmax_scale * 1.4426950408889634f;
+      int nq = 0, nk = 0, np = 0;
+      while (next < todo.size() && np < cpk::kMaxProblems &&
+             nq + (int)todo[next]->q.size() <= cpk::kMaxSegs &&
+             nk + (int)todo[next]->kv.size() <= cpk::kMaxSegs) {
+        const Piece& pc = *todo[next++];
+        for (size_t i = 0; i < pc.q.size(); ++i) {
+          p.qs[nq + i] = to_seg(pc.q[i]);
+          p.q_prob[nq + i] = (int8_t)np;
+        }
+        for (size_t j = 0; j < pc.kv.size(); ++j) p.ks[nk + j] = to_seg(pc.kv[j]);
+        p.kv_lo[np] = (int8_t)nk;
+        p.kv_hi[np] = (int8_t)(nk + pc.kv.size());
+        p.q[np] = pc.pr->q;
+        p.k[np] = pc.pr->k;
+        p.v[np] = pc.pr->v;
+        p.o[np] = pc.pr->o;
+        p.lse[np] = pc.pr->lse;
+        nq += (int)pc.q.size();
+        nk += (int)pc.kv.size();
+        ++np;
+      }
+      p.n_q_segs = nq;
+      plan_tiles(p, bf16 ? cpk::kTileRowsBf16 : cpk::kTileRowsF32);
+      if (p.total_tiles == 0) continue;
+      const hipError_t e = bf16 ? cpk::launch_attn_bf16(p, d_h, s) : cpk::launch_attn_f32(p, d_h, s);
+      st = launch_status(e, what);
+      if (st) return st;
     }
-    p.n_q_segs = nq;
-    plan_tiles(p, bf16 ? cpk::kTileRowsBf16 : cpk::kTileRowsF32);
-    if (p.total_tiles == 0) continue;
-    const hipError_t e = bf16 ? cpk::launch_attn_bf16(p, d_h, s) : cpk::launch_attn_f32(p, d_h, s);
-    st = launch_status(e, what);
-    if (st) return st;
   }
   return ok();
 }

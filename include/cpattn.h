@@ -58,7 +58,10 @@ typedef struct {
   int64_t local_start;
 } cp_segment;
 
-/* Largest segment table cp_partial_attn accepts per shard (tables travel in kernel arguments). */
+/* Runs of a segment table one kernel launch takes (tables travel in kernel arguments). Longer
+   tables are accepted (up to 2^20 runs) and split over several launches: the Q runs in groups of
+   whole sequences, each with only its own sequences' KV runs, and KV runs beyond this count of one
+   group folded in by further launches in order. */
 #define CP_MAX_SEGMENTS 64
 /* Largest number of parts cp_merge_lse merges in one call. */
 #define CP_MAX_MERGE_PARTS 64
@@ -89,8 +92,9 @@ int cp_shard_map(int n_ranges, const int32_t* seq_id, const int64_t* range_begin
  * of its local Q against the KV it holds; [CPEP §5.1] per-token attention and causal mask;
  * [CPEP §4.1]/§6 block-wise attention with online softmax).
  *   q: device [tq, n_h, d_h]; k, v: device [tk, n_kv, d_h]; dtype in_dtype (all three).
- *   q_segs / kv_segs: host tables (at most CP_MAX_SEGMENTS each) describing which sequence and
- *     positions every shard row holds; rows outside all segments are not read or written.
+ *   q_segs / kv_segs: host tables (any length up to 2^20 runs; see CP_MAX_SEGMENTS) describing
+ *     which sequence and positions every shard row holds; rows outside all segments are not read
+ *     or written.
  *   causal: key visible iff same sequence and key position <= query position; 0: same sequence.
  *   o: device fp32 [tq, n_h, d_h]; lse: device fp32 [tq, n_h].
  *   accumulate = 0: overwrite (o, lse) with this step's partial.

@@ -117,8 +117,12 @@ def test_partial_attn_rejects_bad_arguments_without_launching():
     big, n = cp.segments([(0, 0, 17, 0)])
     assert _partial(qs=big, nq=n) == cp.CP_E_SHAPE   # runs past the shard
     assert "outside the shard" in cp.last_error()
+    # tables longer than one launch takes are accepted (split over launches); nothing to do with
+    # no query run, so nothing is launched here
     many, n = cp.segments([(0, i, 1, 0) for i in range(65)])
-    assert _partial(ks=many, nk=n) == cp.CP_E_CAPACITY
+    assert _partial(ks=many, nk=n, nq=0) == cp.CP_OK
+    bad_many, n = cp.segments([(0, i, 1, 0) for i in range(64)] + [(0, 0, 17, 0)])
+    assert _partial(ks=bad_many, nk=n) == cp.CP_E_SHAPE         # every run is still validated
     neg, n = cp.segments([(-1, 0, 1, 0)])
     assert _partial(ks=neg, nk=n) == cp.CP_E_SHAPE
     assert _partial(tq=1 << 31) == cp.CP_E_UNSUPPORTED
