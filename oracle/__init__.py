@@ -51,6 +51,11 @@ def _declare(lib):
     lib.orc_merge.restype = None
     lib.orc_split_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, i64p, i64p]
     lib.orc_split_bounds.restype = None
+    lib.orc_attention_backward.argtypes = [f32p, f32p, f32p, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i64p, i32p,
+                                           i64p, ctypes.c_int, ctypes.c_double, f64p, f64p, f32p,
+                                           f64p, f64p, f64p]
+    lib.orc_attention_backward.restype = ctypes.c_int
     for name in ("orc_pass_kv_shard", "orc_pass_q_query", "orc_pass_q_slot"):
         getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         getattr(lib, name).restype = ctypes.c_int
@@ -153,6 +158,46 @@ def attention(q, k, v, n_h: int, n_kv: int, q_seq, q_pos, k_seq, k_pos, causal: 
     if rc != 0:
         raise ValueError("orc_attention: bad arguments")
     return o, lse
+
+
+def attention_backward(q, k, v, n_h: int, n_kv: int, q_seq, q_pos, k_seq, k_pos, causal: bool,
+                       scale: float, o, lse, d_o):
+    """fp64 gradients of the partial attention of the query tokens over the given keys, from the
+    final forward (o [tq, n_h, d], lse [tq, n_h]) and the output gradient d_o [tq, n_h, d].
+
+    Returns (dq float64 [tq, n_h, d], dk float64 [tk, n_kv, d], dv float64 [tk, n_kv, d]).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    d_o = np.ascontiguousarray(d_o, dtype=np.float32)
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    tq, tk, d = q.shape[0], k.shape[0], q.shape[-1]
+    assert q.shape == (tq, n_h, d) and k.shape == (tk, n_kv, d) and v.shape == (tk, n_kv, d)
+    assert o.shape == (tq, n_h, d) and d_o.shape == (tq, n_h, d) and lse.shape == (tq, n_h)
+    q_seq = np.ascontiguousarray(q_seq, dtype=np.int32)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int64)
+    k_seq = np.ascontiguousarray(k_seq, dtype=np.int32)
+    k_pos = np.ascontiguousarray(k_pos, dtype=np.int64)
+    dq = np.zeros((tq, n_h, d), np.float64)
+    dk = np.zeros((max(tk, 1), n_kv, d), np.float64)
+    dv = np.zeros((max(tk, 1), n_kv, d), np.float64)
+    kk = k if tk else np.zeros((1, n_kv, d), np.float32)
+    vv = v if tk else np.zeros((1, n_kv, d), np.float32)
+    ks = k_seq if tk else np.zeros(1, np.int32)
+    kp = k_pos if tk else np.zeros(1, np.int64)
+    rc = lib.orc_attention_backward(_ptr(q, ctypes.c_float), _ptr(kk, ctypes.c_float),
+                                    _ptr(vv, ctypes.c_float), tq, tk, n_h, n_kv, d,
+                                    _ptr(q_seq, ctypes.c_int32), _ptr(q_pos, ctypes.c_int64),
+                                    _ptr(ks, ctypes.c_int32), _ptr(kp, ctypes.c_int64), int(causal),
+                                    float(scale), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                                    _ptr(d_o, ctypes.c_float), _ptr(dq, ctypes.c_double),
+                                    _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("orc_attention_backward: bad arguments")
+    return dq, dk[:tk], dv[:tk]
 
 
 def merge(o_parts, lse_parts):

@@ -243,3 +243,71 @@ int orc_pass_q_slot(int cp_world, int q_shard, int kv_shard) {
     return -1;
   return q_shard * cp_world + kv_shard;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Backward of the partial attention of query tokens over a set of keys.
+ * [CPEP §6]: with CP the forward gathers K/V for each rank's Q chunk, and the backward sends the
+ * K/V gradient contributions back to the ranks that own those K/V chunks (a reduce-scatter, i.e.
+ * a sum per chunk).  On the ring, each step's gradient contribution is that of the step's key
+ * subset.
+ * Definition (the gradient of O = softmax(scale * q.K^T) V written out, [CPEP §5.1]): for row
+ * (t, h) with the FINAL output O and log-sum-exp LSE over all the keys the row sees (every shard),
+ * and every key j of the given subset visible to it,
+ *   p_j  = exp(s_j - LSE)                  (its softmax weight in the full attention)
+ *   dp_j = sum_d dO[d] V[j][d]
+ *   D    = sum_d dO[d] O[d]                (= sum over all visible keys of p_j dp_j)
+ *   ds_j = p_j (dp_j - D)
+ *   dQ[t][h]  += scale * ds_j * K[j]
+ *   dK[j][g]  += scale * ds_j * Q[t][h]     (g = the row's KV head)
+ *   dV[j][g]  += p_j * dO[t][h]
+ * Summed over a partition of the keys these contributions give the full gradient, which is what
+ * makes the per-shard reduce-scatter exact.  Rows with LSE = -inf saw no key and contribute 0.
+ * q: [tq, n_h, d_h]; k, v: [tk, n_kv, d_h] (fp32 values); o: [tq, n_h, d_h] and lse: [tq, n_h]
+ * (fp64, the final forward results); d_o: [tq, n_h, d_h] (fp32 values).  Outputs (fp64, written,
+ * not accumulated): dq [tq, n_h, d_h], dk and dv [tk, n_kv, d_h].
+ * Plain loops: serial over everything (the dK/dV sums run over all rows of the key's sequence).
+ * ------------------------------------------------------------------------------------------ */
+int orc_attention_backward(const float* q, const float* k, const float* v, int64_t tq, int64_t tk,
+                           int n_h, int n_kv, int d_h, const int32_t* q_seq, const int64_t* q_pos,
+                           const int32_t* k_seq, const int64_t* k_pos, int causal, double scale,
+                           const double* o, const double* lse, const float* d_o, double* dq,
+                           double* dk, double* dv) {
+  if (n_h < 1 || n_kv < 1 || n_h % n_kv != 0 || d_h < 1) return -1;
+  int group = n_h / n_kv;
+  for (int64_t i = 0; i < tq * n_h * (int64_t)d_h; ++i) dq[i] = 0.0;
+  for (int64_t i = 0; i < tk * n_kv * (int64_t)d_h; ++i) dk[i] = dv[i] = 0.0;
+  for (int64_t t = 0; t < tq; ++t) {
+    for (int h = 0; h < n_h; ++h) {
+      double L = lse[t * n_h + h];
+      if (L == -INFINITY) continue;
+      int kvh = h / group; /* the row's KV head */
+      const float* qv = q + (t * n_h + h) * (int64_t)d_h;
+      const float* gv = d_o + (t * n_h + h) * (int64_t)d_h;
+      const double* ov = o + (t * n_h + h) * (int64_t)d_h;
+      double D = 0.0;
+      for (int d = 0; d < d_h; ++d) D += (double)gv[d] * ov[d];
+      for (int64_t j = 0; j < tk; ++j) {
+        if (k_seq[j] != q_seq[t]) continue;
+        if (causal && q_pos[t] < k_pos[j]) continue; /* a later key is invisible */
+        const float* kv = k + (j * n_kv + kvh) * (int64_t)d_h;
+        const float* vv = v + (j * n_kv + kvh) * (int64_t)d_h;
+        double s = 0.0, dp = 0.0;
+        for (int d = 0; d < d_h; ++d) {
+          s += (double)qv[d] * (double)kv[d];
+          dp += (double)gv[d] * (double)vv[d];
+        }
+        double p = exp(s * scale - L);
+        double ds = p * (dp - D);
+        double* dqr = dq + (t * n_h + h) * (int64_t)d_h;
+        double* dkr = dk + (j * n_kv + kvh) * (int64_t)d_h;
+        double* dvr = dv + (j * n_kv + kvh) * (int64_t)d_h;
+        for (int d = 0; d < d_h; ++d) {
+          dqr[d] += scale * ds * (double)kv[d];
+          dkr[d] += scale * ds * (double)qv[d];
+          dvr[d] += p * (double)gv[d];
+        }
+      }
+    }
+  }
+  return 0;
+}

@@ -35,6 +35,14 @@ void orc_merge(int n_parts, const double* const* o_parts, const double* const* l
 /* Key range [lo, hi) of decode split c out of n_splits for a request with len cached keys. */
 void orc_split_bounds(int64_t len, int n_splits, int c, int64_t* lo, int64_t* hi);
 
+/* Gradients (fp64) of the partial attention of query tokens over the given keys, from the final
+   forward output o and lse and the output gradient d_o. Returns -1 on bad arguments. */
+int orc_attention_backward(const float* q, const float* k, const float* v, int64_t tq, int64_t tk,
+                           int n_h, int n_kv, int d_h, const int32_t* q_seq, const int64_t* q_pos,
+                           const int32_t* k_seq, const int64_t* k_pos, int causal, double scale,
+                           const double* o, const double* lse, const float* d_o, double* dq,
+                           double* dk, double* dv);
+
 /* Ring schedules: KV shard rank `rank` holds at Pass-KV step `step`; Q shard hosted by the owner of
    KV shard `kv_shard` at Pass-Q step `step`; storage slot of the partial (q_shard, kv_shard).
    Each returns -1 on bad arguments. */

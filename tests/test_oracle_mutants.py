@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle as T
+import test_oracle_backward as B
 import test_oracle_shard_map as S
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -55,6 +56,19 @@ MUTANTS = [
      "return kv_shard;"),
     ("Pass-Q slots transposed", "return q_shard * cp_world + kv_shard;",
      "return kv_shard * cp_world + q_shard;"),
+    ("backward: score gradient with the wrong sign", "double ds = p * (dp - D);",
+     "double ds = p * (D - dp);"),
+    ("backward: dQ without the scale", "dqr[d] += scale * ds * (double)kv[d];",
+     "dqr[d] += ds * (double)kv[d];"),
+    ("backward: dK from the key instead of the query", "dkr[d] += scale * ds * (double)qv[d];",
+     "dkr[d] += scale * ds * (double)kv[d];"),
+    ("backward: weights without the final LSE", "double p = exp(s * scale - L);",
+     "double p = exp(s * scale);"),
+    ("backward: dV from the score gradient", "dvr[d] += p * (double)gv[d];",
+     "dvr[d] += ds * (double)gv[d];"),
+    ("backward: D from dO alone", "D += (double)gv[d] * ov[d];", "D += (double)gv[d];"),
+    ("backward: causal mask ignored", "if (causal && q_pos[t] < k_pos[j]) continue;", ""),
+    ("backward: GQA heads interleaved", "int kvh = h / group;", "int kvh = h % n_kv;"),
 ]
 
 PINS = [
@@ -72,6 +86,12 @@ PINS = [
     ("merge identity and ln 2", T.test_merge_single_part_is_identity_and_two_equal_parts_add_ln2),
     ("decode splits", T.test_decode_splits_cover_keys_and_merge_exactly),
     ("golden decode split table", T.test_decode_split_table_golden_l300_s32),
+    ("backward finite differences", lambda: B.test_finite_differences_of_the_forward(True)),
+    ("backward autograd", lambda: B.test_matches_torch_autograd_on_a_dense_formulation(2, True)),
+    ("backward partition sums", lambda: B.test_contributions_over_a_key_partition_sum_to_the_full_gradient(3)),
+    ("backward uniform V", B.test_uniform_values_give_zero_score_gradients_and_dv_sums_to_do),
+    ("backward zero query", B.test_zero_query_gives_uniform_weights),
+    ("backward GQA", B.test_gqa_gradients_come_from_the_heads_of_the_group),
     ("golden shard map", S.test_golden_t256_cp4_layout_and_pair_counts),
     ("golden shard map, T=257", S.test_golden_t257_cp4_floor_edges_and_pair_counts),
     ("golden ring schedules", S.test_golden_ring_schedules_cp4),
