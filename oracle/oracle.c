@@ -265,8 +265,25 @@ int orc_pass_q_slot(int cp_world, int q_shard, int kv_shard) {
  * q: [tq, n_h, d_h]; k, v: [tk, n_kv, d_h] (fp32 values); o: [tq, n_h, d_h] and lse: [tq, n_h]
  * (fp64, the final forward results); d_o: [tq, n_h, d_h] (fp32 values).  Outputs (fp64, written,
  * not accumulated): dq [tq, n_h, d_h], dk and dv [tk, n_kv, d_h].
- * Plain loops: serial over everything (the dK/dV sums run over all rows of the key's sequence).
+ * Plain loops in two passes over the same per-pair terms: pass 1 (rows in parallel) sums dQ of
+ * each row over its visible keys; pass 2 (keys in parallel) sums dK and dV of each key over the
+ * rows that see it.  The score gradient of a (row, key) pair is computed the same way in both.
  * ------------------------------------------------------------------------------------------ */
+/* Terms of one visible (row t, head h; key j) pair of the backward: p = exp(s - LSE) and
+ * ds = p * (dO.V[j] - D).  kvh is the row's KV head; D = dO.O of the row. */
+static void bwd_pair(const float* qv, const float* gv, const float* kv, const float* vv, int d_h,
+                     double scale, double L, double D, double* p_out, double* ds_out) {
+  double s = 0.0, dp = 0.0;
+  for (int d = 0; d < d_h; ++d) {
+    s += (double)qv[d] * (double)kv[d];
+    dp += (double)gv[d] * (double)vv[d];
+  }
+  double p = exp(s * scale - L);
+  double ds = p * (dp - D);
+  *p_out = p;
+  *ds_out = ds;
+}
+
 int orc_attention_backward(const float* q, const float* k, const float* v, int64_t tq, int64_t tk,
                            int n_h, int n_kv, int d_h, const int32_t* q_seq, const int64_t* q_pos,
                            const int32_t* k_seq, const int64_t* k_pos, int causal, double scale,
@@ -274,40 +291,64 @@ int orc_attention_backward(const float* q, const float* k, const float* v, int64
                            double* dk, double* dv) {
   if (n_h < 1 || n_kv < 1 || n_h % n_kv != 0 || d_h < 1) return -1;
   int group = n_h / n_kv;
-  for (int64_t i = 0; i < tq * n_h * (int64_t)d_h; ++i) dq[i] = 0.0;
-  for (int64_t i = 0; i < tk * n_kv * (int64_t)d_h; ++i) dk[i] = dv[i] = 0.0;
-  for (int64_t t = 0; t < tq; ++t) {
-    for (int h = 0; h < n_h; ++h) {
-      double L = lse[t * n_h + h];
-      if (L == -INFINITY) continue;
-      int kvh = h / group; /* the row's KV head */
-      const float* qv = q + (t * n_h + h) * (int64_t)d_h;
-      const float* gv = d_o + (t * n_h + h) * (int64_t)d_h;
-      const double* ov = o + (t * n_h + h) * (int64_t)d_h;
-      double D = 0.0;
-      for (int d = 0; d < d_h; ++d) D += (double)gv[d] * ov[d];
-      for (int64_t j = 0; j < tk; ++j) {
-        if (k_seq[j] != q_seq[t]) continue;
-        if (causal && q_pos[t] < k_pos[j]) continue; /* a later key is invisible */
-        const float* kv = k + (j * n_kv + kvh) * (int64_t)d_h;
-        const float* vv = v + (j * n_kv + kvh) * (int64_t)d_h;
-        double s = 0.0, dp = 0.0;
+  /* D of every row */
+  double* Drow = (double*)calloc((size_t)(tq * n_h) + 1, sizeof(double));
+  for (int64_t r = 0; r < tq * n_h; ++r) {
+    double D = 0.0;
+    for (int d = 0; d < d_h; ++d) D += (double)d_o[r * d_h + d] * o[r * d_h + d];
+    Drow[r] = D;
+  }
+  /* pass 1: dQ of each row over its visible keys */
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < tq * n_h; ++r) {
+    int64_t t = r / n_h;
+    int h = (int)(r % n_h);
+    int kvh = h / group; /* the row's KV head */
+    double* dqr = dq + r * (int64_t)d_h;
+    for (int d = 0; d < d_h; ++d) dqr[d] = 0.0;
+    double L = lse[r];
+    if (L == -INFINITY) continue;
+    const float* qv = q + r * (int64_t)d_h;
+    const float* gv = d_o + r * (int64_t)d_h;
+    for (int64_t j = 0; j < tk; ++j) {
+      if (k_seq[j] != q_seq[t]) continue;
+      if (causal && q_pos[t] < k_pos[j]) continue; /* a later key is invisible */
+      const float* kv = k + (j * n_kv + kvh) * (int64_t)d_h;
+      const float* vv = v + (j * n_kv + kvh) * (int64_t)d_h;
+      double p, ds;
+      bwd_pair(qv, gv, kv, vv, d_h, scale, L, Drow[r], &p, &ds);
+      for (int d = 0; d < d_h; ++d) dqr[d] += scale * ds * (double)kv[d];
+    }
+  }
+  /* pass 2: dK and dV of each key over the rows that see it */
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t c = 0; c < tk * n_kv; ++c) {
+    int64_t j = c / n_kv;
+    int g = (int)(c % n_kv);
+    double* dkr = dk + c * (int64_t)d_h;
+    double* dvr = dv + c * (int64_t)d_h;
+    for (int d = 0; d < d_h; ++d) dkr[d] = dvr[d] = 0.0;
+    const float* kv = k + c * (int64_t)d_h;
+    const float* vv = v + c * (int64_t)d_h;
+    for (int64_t t = 0; t < tq; ++t) {
+      if (k_seq[j] != q_seq[t]) continue;
+      if (causal && q_pos[t] < k_pos[j]) continue;
+      for (int h = 0; h < n_h; ++h) {
+        if (h / group != g) continue; /* only the query heads of this KV head */
+        int64_t r = t * n_h + h;
+        double L = lse[r];
+        if (L == -INFINITY) continue;
+        const float* qv = q + r * (int64_t)d_h;
+        const float* gv = d_o + r * (int64_t)d_h;
+        double p, ds;
+        bwd_pair(qv, gv, kv, vv, d_h, scale, L, Drow[r], &p, &ds);
         for (int d = 0; d < d_h; ++d) {
-          s += (double)qv[d] * (double)kv[d];
-          dp += (double)gv[d] * (double)vv[d];
-        }
-        double p = exp(s * scale - L);
-        double ds = p * (dp - D);
-        double* dqr = dq + (t * n_h + h) * (int64_t)d_h;
-        double* dkr = dk + (j * n_kv + kvh) * (int64_t)d_h;
-        double* dvr = dv + (j * n_kv + kvh) * (int64_t)d_h;
-        for (int d = 0; d < d_h; ++d) {
-          dqr[d] += scale * ds * (double)kv[d];
           dkr[d] += scale * ds * (double)qv[d];
           dvr[d] += p * (double)gv[d];
         }
       }
     }
   }
+  free(Drow);
   return 0;
 }

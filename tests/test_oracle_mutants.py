@@ -66,9 +66,12 @@ MUTANTS = [
      "double p = exp(s * scale);"),
     ("backward: dV from the score gradient", "dvr[d] += p * (double)gv[d];",
      "dvr[d] += ds * (double)gv[d];"),
-    ("backward: D from dO alone", "D += (double)gv[d] * ov[d];", "D += (double)gv[d];"),
+    ("backward: D from dO alone", "D += (double)d_o[r * d_h + d] * o[r * d_h + d];",
+     "D += (double)d_o[r * d_h + d];"),
     ("backward: causal mask ignored", "if (causal && q_pos[t] < k_pos[j]) continue;", ""),
     ("backward: GQA heads interleaved", "int kvh = h / group;", "int kvh = h % n_kv;"),
+    ("backward: dK/dV from the wrong query heads", "if (h / group != g) continue;",
+     "if (h % n_kv != g) continue;"),
 ]
 
 PINS = [
