@@ -26,7 +26,8 @@ CP_PASS_KV, CP_PASS_Q = 0, 1
 
 EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
             "cp_decode_workspace_bytes", "cp_decode_splitkv_ex", "cp_decode_workspace_bytes_ex",
-            "cp_decode_splitkv_noalloc",
+            "cp_decode_splitkv_noalloc", "cp_attn_bwd_delta", "cp_partial_attn_bwd",
+            "cp_ring_pass_kv_bwd",
             "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant", "cp_status_string",
             "cp_last_error")
 
@@ -96,11 +97,19 @@ def load():
                                    i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
                                    i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), i32, ctypes.POINTER(vp), vp]
+    lib.cp_attn_bwd_delta.argtypes = [vp, vp, i32, i64, i32, vp, vp]
+    lib.cp_partial_attn_bwd.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, segp, i32, segp, i32,
+                                        i32, f, vp, vp, vp, vp, vp, vp, vp]
+    lib.cp_ring_pass_kv_bwd.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), i64p, ctypes.POINTER(segp),
+                                        ctypes.POINTER(ctypes.c_int), i32, i32, i32, i32, i32, f, vp,
+                                        vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
     lib.cp_select_ring_variant.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_double,
                                            ctypes.c_double, ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]
     for name in ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
                  "cp_decode_splitkv_ex", "cp_decode_splitkv_noalloc", "cp_ring_pass_kv", "cp_ring_pass_q",
+                 "cp_attn_bwd_delta", "cp_partial_attn_bwd", "cp_ring_pass_kv_bwd",
                  "cp_select_ring_variant"):
         getattr(lib, name).restype = ctypes.c_int
     lib.cp_status_string.argtypes = [ctypes.c_int]
@@ -467,3 +476,84 @@ def ring_pass_q(q_shards, q_segs, k_shards, v_shards, kv_segs, causal: bool, sof
     _check(lib.cp_ring_pass_q(N, qs, tq, qsg, nqs, ks, vs, tk, ksg, nks, n_h, n_kv, d,
                               _dtype_code(q_shards[0]), int(causal), float(softmax_scale), op, lp,
                               oo, _dtype_code(o_out[0]), lo, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------------- backward
+def attn_bwd_delta(o, d_o, delta, stream=None, check: bool = True):
+    """cp_attn_bwd_delta: delta = rowsum(dO * O). o fp32 [..., d], d_o [..., d], delta fp32 [...]."""
+    lib = load()
+    d = o.shape[-1]
+    rows = o.numel() // d
+    if check:
+        _req(o, "o", _float_types(), numel=rows * d)
+        _req(d_o, "d_o", _in_types(), numel=rows * d)
+        _req(delta, "delta", _float_types(), numel=rows)
+    _check(lib.cp_attn_bwd_delta(_ptr(o), _ptr(d_o), _dtype_code(d_o), rows, d, _ptr(delta),
+                                 _stream(stream)))
+
+
+def partial_attn_bwd(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: float, lse, delta, d_o,
+                     dq, dk, dv, stream=None, check: bool = True):
+    """cp_partial_attn_bwd: adds one ring step's gradient contributions into dq, dk, dv (fp32)."""
+    lib = load()
+    qa, nq = _segarg(q_segs)
+    ka, nk = _segarg(kv_segs)
+    tq, n_h, d = q.shape
+    tk, n_kv = k.shape[0], k.shape[1]
+    if check:
+        bf16 = _types("bf16")
+        _req(q, "q", bf16)
+        _req(k, "k", bf16, (tk, n_kv, d))
+        _req(v, "v", bf16, (tk, n_kv, d))
+        _req(lse, "lse", _float_types(), numel=tq * n_h)
+        _req(delta, "delta", _float_types(), numel=tq * n_h)
+        _req(d_o, "d_o", bf16, (tq, n_h, d))
+        _req(dq, "dq", _float_types(), (tq, n_h, d))
+        _req(dk, "dk", _float_types(), (tk, n_kv, d))
+        _req(dv, "dv", _float_types(), (tk, n_kv, d))
+    _check(lib.cp_partial_attn_bwd(_ptr(q), _ptr(k), _ptr(v), tq, tk, n_h, n_kv, d, _dtype_code(q),
+                                   qa, nq, ka, nk, int(causal), float(softmax_scale), _ptr(lse),
+                                   _ptr(delta), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _stream(stream)))
+
+
+def ring_pass_kv_bwd(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,
+                     softmax_scale: float, o, lse, d_o, delta, dq, dk_shards, dv_shards, stream=None,
+                     check: bool = True):
+    """cp_ring_pass_kv_bwd for one rank: adds its gradient contributions into dq and into every
+    KV shard's dk_shards[s] / dv_shards[s]."""
+    lib = load()
+    N = len(k_shards)
+    qa, nq = _segarg(q_segs)
+    tq, n_h, d = q.shape
+    n_kv = k_shards[0].shape[1]
+    if not (len(v_shards) == len(kv_segs) == len(dk_shards) == len(dv_shards) == N):
+        raise ValueError("k_shards, v_shards, kv_segs, dk_shards and dv_shards need one entry per shard")
+    if check:
+        bf16 = _types("bf16")
+        _req(q, "q", bf16)
+        _req(o, "o", _float_types(), (tq, n_h, d))
+        _req(lse, "lse", _float_types(), numel=tq * n_h)
+        _req(d_o, "d_o", bf16, (tq, n_h, d))
+        _req(delta, "delta", _float_types(), numel=tq * n_h)
+        _req(dq, "dq", _float_types(), (tq, n_h, d))
+        for i in range(N):
+            shp = tuple(k_shards[i].shape)
+            _req(k_shards[i], f"k_shards[{i}]", bf16)
+            _req(v_shards[i], f"v_shards[{i}]", bf16, shp)
+            _req(dk_shards[i], f"dk_shards[{i}]", _float_types(), shp)
+            _req(dv_shards[i], f"dv_shards[{i}]", _float_types(), shp)
+    vp = ctypes.c_void_p
+    segp = ctypes.POINTER(CpSegment)
+    ks = (vp * N)(*[_ptr(t) for t in k_shards])
+    vs = (vp * N)(*[_ptr(t) for t in v_shards])
+    tk = (ctypes.c_int64 * N)(*[t.shape[0] for t in k_shards])
+    seg_objs = [_segarg(s_) for s_ in kv_segs]
+    kvs = (segp * N)(*[ctypes.cast(a, segp) for a, _ in seg_objs])
+    nkv = (ctypes.c_int * N)(*[n for _, n in seg_objs])
+    dks = (vp * N)(*[_ptr(t) for t in dk_shards])
+    dvs = (vp * N)(*[_ptr(t) for t in dv_shards])
+    _check(lib.cp_ring_pass_kv_bwd(_ptr(q), tq, qa, nq, N, rank, ks, vs, tk, kvs, nkv, n_h, n_kv, d,
+                                   _dtype_code(q), int(causal), float(softmax_scale), _ptr(o),
+                                   _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dq), dks, dvs,
+                                   _stream(stream)))

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libcpattn.so")
 
-SOURCES = ["api.cpp", "attn_f32.hip", "attn_bf16.hip", "merge.hip", "decode.hip"]
+SOURCES = ["api.cpp", "attn_f32.hip", "attn_bf16.hip", "attn_bwd.hip", "merge.hip", "decode.hip"]
 ARCH = "gfx950"
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -317,6 +317,67 @@ int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, 
   return ok();
 }
 
+// Tile plan of one backward launch pair over one piece's tables: Q runs ordered by the causal
+// work of their last tile (dQ workgroups, last tile of a run first), KV runs by the work of their
+// first tile (dK/dV workgroups, first tile of a run first), heaviest first.
+void plan_bwd(cpk::BwdParams& p, const Piece& pc) {
+  p.n_q_segs = (int)pc.q.size();
+  p.n_kv_segs = (int)pc.kv.size();
+  for (int i = 0; i < p.n_q_segs; ++i) p.qs[i] = to_seg(pc.q[i]);
+  for (int j = 0; j < p.n_kv_segs; ++j) p.ks[j] = to_seg(pc.kv[j]);
+  std::vector<std::pair<int64_t, int>> qw, kw;
+  for (int i = 0; i < p.n_q_segs; ++i) {
+    const cpk::Seg& q = p.qs[i];
+    const int64_t last = (int64_t)q.pos + q.len - 1;
+    int64_t w = 0;
+    for (int j = 0; j < p.n_kv_segs; ++j) {
+      const cpk::Seg& k = p.ks[j];
+      if (k.seq != q.seq) continue;
+      w += p.causal ? std::min<int64_t>(k.len, std::max<int64_t>(0, last - k.pos + 1)) : k.len;
+    }
+    qw.push_back({w, i});
+  }
+  for (int j = 0; j < p.n_kv_segs; ++j) {
+    const cpk::Seg& k = p.ks[j];
+    int64_t w = 0;
+    for (int i = 0; i < p.n_q_segs; ++i) {
+      const cpk::Seg& q = p.qs[i];
+      if (q.seq != k.seq) continue;
+      w += p.causal ? std::min<int64_t>(q.len, std::max<int64_t>(0, (int64_t)q.pos + q.len - k.pos)) : q.len;
+    }
+    kw.push_back({w, j});
+  }
+  auto heavier = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) { return a.first > b.first; };
+  std::stable_sort(qw.begin(), qw.end(), heavier);
+  std::stable_sort(kw.begin(), kw.end(), heavier);
+  p.q_prefix[0] = 0;
+  for (int s2 = 0; s2 < p.n_q_segs; ++s2) {
+    const int i = qw[s2].second;
+    p.q_order[s2] = (int8_t)i;
+    const int64_t rows = (int64_t)p.qs[i].len * p.group;
+    p.q_prefix[s2 + 1] = p.q_prefix[s2] + (int)((rows + cpk::kBwdQRows - 1) / cpk::kBwdQRows);
+  }
+  p.q_tiles = p.q_prefix[p.n_q_segs];
+  p.kv_prefix[0] = 0;
+  for (int s2 = 0; s2 < p.n_kv_segs; ++s2) {
+    const int j = kw[s2].second;
+    p.kv_order[s2] = (int8_t)j;
+    p.kv_prefix[s2 + 1] = p.kv_prefix[s2] + (p.ks[j].len + cpk::kBwdKeys - 1) / cpk::kBwdKeys;
+  }
+  p.kv_tiles = p.kv_prefix[p.n_kv_segs];
+}
+
+// Argument checks of one backward step beyond those of its forward problem.
+int validate_bwd_extra(const float* lse, const float* delta, const void* d_o, const float* dq,
+                       const float* dk, const float* dv, cp_dtype in_dtype, int n_q_segs, int n_kv_segs) {
+  if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "the backward supports bf16 inputs only");
+  if (n_q_segs > 0 && (!lse || !delta || !d_o || !dq)) return fail(CP_E_ARG, "lse, delta, d_o or dq is NULL");
+  if (n_kv_segs > 0 && (!dk || !dv)) return fail(CP_E_ARG, "dk or dv is NULL");
+  if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(CP_E_ARG, "d_o, dq, dk and dv must be 16-byte aligned");
+  return CP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -540,6 +601,101 @@ int cp_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   return cp_decode_splitkv_ex(q, k_cache, v_cache, kv_offset, kv_len, batch, n_h, n_kv, d_h,
                               in_dtype, n_splits, softmax_scale, CP_F32, ws_o, ws_lse, o_out,
                               out_dtype, lse_out, stream);
+}
+
+// delta = dO . O per row, the row term of the softmax gradient ([CPEP §6] backward).
+int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_t rows, int d_h,
+                      float* delta, void* stream) {
+  if (rows < 0) return fail(CP_E_ARG, "rows=%lld", (long long)rows);
+  if (d_h != 64 && d_h != 128) return fail(CP_E_UNSUPPORTED, "d_h=%d (64 or 128 supported)", d_h);
+  if (do_dtype != CP_F32 && do_dtype != CP_BF16) return fail(CP_E_ARG, "do_dtype=%d", (int)do_dtype);
+  if (rows > ((int64_t)1 << 40)) return fail(CP_E_UNSUPPORTED, "rows=%lld", (long long)rows);
+  if (rows == 0) return ok();
+  if (!o || !d_o || !delta) return fail(CP_E_ARG, "NULL pointer argument");
+  return launch_status(cpk::launch_bwd_delta(o, d_o, do_dtype == CP_BF16, rows, d_h, delta,
+                                             static_cast<hipStream_t>(stream)),
+                       "cp_attn_bwd_delta");
+}
+
+// One ring step's backward ([CPEP §6]): gradient contributions of a Q shard against one KV shard,
+// added into dq (the Q shard's) and dk, dv (the KV shard's, summed over the ranks that visit it).
+int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq, int64_t tk,
+                        int n_h, int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs,
+                        int n_q_segs, const cp_segment* kv_segs, int n_kv_segs, int causal,
+                        float softmax_scale, const float* lse, const float* delta, const void* d_o,
+                        float* dq, float* dk, float* dv, void* stream) {
+  const Problem pr{q, k, v, tq, tk, q_segs, n_q_segs, kv_segs, n_kv_segs, dq, const_cast<float*>(lse)};
+  int st = validate_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, softmax_scale, 0);
+  if (st) return st;
+  st = validate_bwd_extra(lse, delta, d_o, dq, dk, dv, in_dtype, n_q_segs, n_kv_segs);
+  if (st) return st;
+  std::vector<Piece> pieces;
+  split_problem(pr, pieces);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (const Piece& pc : pieces) {  // pieces may share rows or keys: one launch pair each, in order
+    cpk::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.d_o = d_o;
+    p.lse = lse;
+    p.delta = delta;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.n_h = n_h;
+    p.n_kv = n_kv;
+    p.group = n_h / n_kv;
+    p.causal = causal ? 1 : 0;
+    p.scale = softmax_scale;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    plan_bwd(p, pc);
+    if (p.q_tiles == 0 || p.kv_tiles == 0) continue;  // no pair of this piece can be visible
+    st = launch_status(cpk::launch_bwd(p, d_h, s), "cp_partial_attn_bwd");
+    if (st) return st;
+  }
+  return ok();
+}
+
+// Ring Pass-KV backward on one device ([CPEP §6]; [CPMTI §3 Fig. 3]): delta of the rank's rows,
+// then at step t the rank's contributions against KV shard (rank - t) mod N, its dK/dV added into
+// that shard's accumulators (on one device the reduce-scatter is this sum).
+int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
+                        int cp_world, int rank, const void* const* k_shards,
+                        const void* const* v_shards, const int64_t* tk,
+                        const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
+                        int d_h, cp_dtype in_dtype, int causal, float softmax_scale, const float* o,
+                        const float* lse, const void* d_o, float* delta, float* dq,
+                        float* const* dk_shards, float* const* dv_shards, void* stream) {
+  if (cp_world < 1 || cp_world > cpk::kMaxParts) return fail(CP_E_ARG, "cp_world=%d", cp_world);
+  if (rank < 0 || rank >= cp_world) return fail(CP_E_ARG, "rank=%d", rank);
+  if (!k_shards || !v_shards || !tk || !kv_segs || !n_kv_segs || !dk_shards || !dv_shards)
+    return fail(CP_E_ARG, "shard arrays are NULL");
+  if (!o && tq > 0) return fail(CP_E_ARG, "o is NULL");
+  std::vector<Problem> steps(cp_world);
+  for (int t = 0; t < cp_world; ++t) {
+    const int s = ((rank - t) % cp_world + cp_world) % cp_world;
+    steps[t] = Problem{q, k_shards[s], v_shards[s], tq, tk[s], q_segs, n_q_segs, kv_segs[s],
+                       n_kv_segs[s], dq, const_cast<float*>(lse)};
+  }
+  int st = validate_problems(steps.data(), cp_world, n_h, n_kv, d_h, in_dtype, softmax_scale, 0);
+  if (st) return st;
+  for (int t = 0; t < cp_world; ++t) {
+    const int s = ((rank - t) % cp_world + cp_world) % cp_world;
+    st = validate_bwd_extra(lse, delta, d_o, dq, dk_shards[s], dv_shards[s], in_dtype, n_q_segs,
+                            n_kv_segs[s]);
+    if (st) return st;
+  }
+  st = cp_attn_bwd_delta(o, d_o, in_dtype, tq * (int64_t)n_h, d_h, delta, stream);
+  if (st) return st;
+  for (int t = 0; t < cp_world; ++t) {
+    const int s = ((rank - t) % cp_world + cp_world) % cp_world;
+    st = cp_partial_attn_bwd(q, k_shards[s], v_shards[s], tq, tk[s], n_h, n_kv, d_h, in_dtype,
+                             q_segs, n_q_segs, kv_segs[s], n_kv_segs[s], causal, softmax_scale, lse,
+                             delta, d_o, dq, dk_shards[s], dv_shards[s], stream);
+    if (st) return st;
+  }
+  return ok();
 }
 
 // Ring Pass-KV ([CPMTI §3 "核心公式"; Fig. 3]): the rank keeps its Q shard; at step t it holds the

@@ -1,0 +1,472 @@
+// attn_bwd.hip -- backward of one ring step's partial attention, bf16 inputs, gfx950 MFMA.
+//
+// What it computes ([CPEP §6]: in context parallelism the backward returns every rank's K/V
+// gradient contributions to the owners of those K/V chunks, a reduce-scatter, i.e. a sum per
+// chunk): for the Q shard's rows and the KV shard's keys each row may see, with the row's FINAL
+// output O and log-sum-exp LSE (over every shard) and the output gradient dO,
+//   P  = exp(scale * q.k - LSE),   dP = dO.v,   delta = dO.O (per row),   dS = P (dP - delta)
+//   dQ += scale * dS K,   dK += scale * dS^T Q,   dV += P^T dO
+// accumulated into the caller's fp32 buffers. Summed over the ring steps (dQ) and over the ranks
+// that visit a KV shard (dK, dV) this is the exact gradient of the whole attention.
+//
+// Two kernels, neither needing atomics:
+//  - bwd_dq_kernel: a workgroup of 8 waves owns 256 query rows (GQA rows = token * G + head, as
+//    in the forward) and walks the KV tiles they see. S^T = K Q^T and dP^T = V dO^T run on
+//    v_mfma_f32_32x32x16_bf16 with K and V rows from LDS and Q^T, dO^T in registers, so each lane
+//    holds 16 keys of one row: P, dS and the row's LSE and delta are per-lane values. dS^T,
+//    rounded to bf16, is then directly the B operand of dQ^T += K^T dS^T, whose K^T operand comes
+//    from the same K tile through the transposing ds_read_b64_tr_b16.
+//  - bwd_dkdv_kernel: a workgroup of 4 waves owns 128 keys (32 per wave, their K and V kept in
+//    registers as B operands) and walks the blocks of 32 query rows that see them. S = Q K^T and
+//    dP = dO V^T leave each lane with 16 rows of one key, which is the A operand layout of
+//    dV += P^T dO and dK += dS^T Q; dO and Q come from LDS through the transposing read.
+// Both stage their shared operands through LDS with register prefetch of the next tile, and
+// swizzle 16-byte chunks so that row reads and transposing reads of one tile are conflict-free.
+//
+// Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
+// 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
+#include <algorithm>
+
+#include "device_common.h"
+
+namespace cpk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// An LDS tile of rows of D bf16 values, row-major without padding; the 16-byte chunk c of row r
+// sits in slot c ^ sw(r). Row reads (16 lanes, 16 consecutive rows, one chunk) and transposing
+// reads (a half-wave: 4 consecutive rows x 4 consecutive chunks) then touch 16 distinct slots.
+template <int D>
+struct BwdTile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowBytes = D * 2;
+  static __device__ constexpr int sw(int r) { return (((r & 3) << 2) | ((r >> 2) & 3)) & (kChunks - 1); }
+  // byte offset of element (r, c8 * 8 + e) for e in [0, 8): chunk c8, byte 2e
+  static __device__ int off(int r, int col) {
+    return r * kRowBytes + (((col >> 3) ^ sw(r)) << 4) + ((col & 7) << 1);
+  }
+};
+
+__device__ inline bf16x8 lds_b128(const unsigned char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// Transposing read of rows r0 + {0..3} + 4 * (lane / 32) and the same 8 rows further, at column
+// col0 + (lane % 32) of a BwdTile: lane l gets 8 values, entry e = row r0 + 8 (e / 4) +
+// 4 (l / 32) + e % 4. That is the k order of the 32x32x16 MFMA operand built from a register
+// tile whose k index runs over rows 8 (v / 4) + 4 (l / 32) + v % 4 (the accumulator layout).
+template <int D>
+__device__ inline bf16x8 lds_tr8(const unsigned char* base, int r0, int col0, int lane) {
+  using T = BwdTile<D>;
+  const int r = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + T::off(r, c)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + T::off(r + 8, c)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Workgroup tile -> (run, tile index in the run) over a table ordered by `order`, prefix sums in
+// `prefix`; first_tile_last: the first workgroup of a run takes its last tile.
+__device__ inline void bwd_locate(const int32_t* prefix, const int8_t* order, int n_segs, int block,
+                                  bool first_tile_last, int& seg, int& tile) {
+  int slot = 0;
+  while (slot + 1 < n_segs && prefix[slot + 1] <= block) ++slot;
+  seg = order[slot];
+  const int n = prefix[slot + 1] - prefix[slot];
+  tile = first_tile_last ? n - 1 - (block - prefix[slot]) : block - prefix[slot];
+}
+
+// ------------------------------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int kBN = 64;                           // keys per tile
+  constexpr int kTileBytes = kBN * T::kRowBytes;
+  constexpr int kLoads = kBN * T::kChunks / 512;    // 16-byte loads per thread per operand
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
+  unsigned char* Ks = smem;
+  unsigned char* Vs = smem + kTileBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int g = blockIdx.y;
+  int seg, tile;
+  bwd_locate(p.q_prefix, p.q_order, p.n_q_segs, blockIdx.x, true, seg, tile);
+  const Seg qs = p.qs[seg];
+  const int rows = qs.len * p.group;
+  const int row0 = tile * 256;
+  const int row_last = min(row0 + 256, rows) - 1;
+  const int qpos_lo = qs.pos + row0 / p.group;
+  const int qpos_hi = qs.pos + row_last / p.group;
+
+  const int r = row0 + wave * 32 + col;
+  const bool live = r < rows;
+  const int rc = live ? r : rows - 1;
+  const int qtok = rc / p.group;
+  const int qpos = qs.pos + qtok;
+  const int64_t qrow = (int64_t)(qs.loc + qtok) * p.n_h + g * p.group + rc % p.group;
+  // Q^T and dO^T operands: k-step s covers d = 8 (half * D/16 + s) + e (the K rows are read with
+  // the same order of d, so every MFMA's reduction covers each d once)
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + qrow * D + half * (D / 2);
+    const __bf16* gp = static_cast<const __bf16*>(p.d_o) + qrow * D + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+      doreg[s] = *reinterpret_cast<const bf16x8*>(gp + s * 8);
+    }
+  }
+  const float L = p.lse[qrow];
+  const float lse2 = L == -INFINITY ? INFINITY : L * kLog2e;  // a row that saw no key: P = 0
+  const float dlt = p.delta[qrow];
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+  const __bf16* Kg = static_cast<const __bf16*>(p.k);
+  const __bf16* Vg = static_cast<const __bf16*>(p.v);
+  u32x4 kpre[kLoads], vpre[kLoads];
+  // loads of tile rows [kt, kt + kBN) of run ks (rows past the run repeat its last key: masked)
+  auto load_tile = [&](const Seg& ks, int kt) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = i * 512 + tid;
+      const int row = idx / T::kChunks, ch = idx % T::kChunks;
+      const int key = min(kt + row, ks.len - 1);
+      const int64_t src = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + ch * 8;
+      kpre[i] = *reinterpret_cast<const u32x4*>(Kg + src);
+      vpre[i] = *reinterpret_cast<const u32x4*>(Vg + src);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = i * 512 + tid;
+      const int row = idx / T::kChunks, ch = idx % T::kChunks;
+      const int o = T::off(row, ch * 8);
+      *reinterpret_cast<u32x4*>(Ks + o) = kpre[i];
+      *reinterpret_cast<u32x4*>(Vs + o) = vpre[i];
+    }
+  };
+
+  // the KV tiles this workgroup sees: runs of its sequence, the prefix visible to its last row
+  int j = 0, kt = 0;
+  auto advance = [&](int jj, int tt) {  // next (run, tile) at or after (jj, tt), or j = n_kv_segs
+    for (; jj < p.n_kv_segs; ++jj, tt = 0) {
+      const Seg ks = p.ks[jj];
+      if (ks.seq != qs.seq) continue;
+      if (tt < visible_prefix(ks, qpos_hi, p.causal)) break;
+    }
+    j = jj;
+    kt = tt;
+  };
+  advance(0, 0);
+  if (j < p.n_kv_segs) load_tile(p.ks[j], kt);
+  while (j < p.n_kv_segs) {
+    const Seg ks = p.ks[j];
+    const int cur_kt = kt;
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    advance(j, kt + kBN);
+    if (j < p.n_kv_segs) load_tile(p.ks[j], kt);  // in flight during this tile's math
+
+    // S^T = K Q^T and dP^T = V dO^T: two 32-key halves
+    f32x16 s[2], dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = dpt[kb][v] = 0.f;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const int o = T::off(kb * 32 + col, 8 * (half * (D / 16) + st));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Ks, o), qreg[st], s[kb], 0, 0, 0);
+        dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Vs, o), doreg[st], dpt[kb], 0, 0, 0);
+      }
+    }
+    // keys past the causal frontier of this lane's row or past the run
+    const int n_full = p.causal ? max(0, min(ks.len, qpos_lo - ks.pos + 1)) : ks.len;
+    const bool masked = cur_kt + kBN > n_full;
+    const int lim = p.causal ? min(ks.len, qpos - ks.pos + 1) : ks.len;
+    // dS^T in bf16 as the B operand of dQ^T += K^T dS^T: k-step t holds keys
+    // 16 t + 8 (e / 4) + 4 half + e % 4 == entries 8 (t % 2) + e of score block t / 2
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
+        if (masked) {
+          const int ko = cur_kt + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          pr = ko < lim ? pr : 0.f;
+        }
+        pb[2 * kb + (v >> 3)][v & 7] = (__bf16)(pr * (dpt[kb][v] - dlt));
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr8<D>(Ks, 16 * t, db * 32, lane), pb[t],
+                                                          acc[db], 0, 0, 0);
+  }
+  if (!live) return;
+  // dQ^T accumulator: lane (row, half) holds d = db*32 + 8 (v/4) + 4 half + v % 4
+  float* out = p.dq + qrow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      float4* o4 = reinterpret_cast<float4*>(out + db * 32 + 8 * vq + 4 * half);
+      float4 x = *o4;
+      x.x = fmaf(p.scale, acc[db][4 * vq], x.x);
+      x.y = fmaf(p.scale, acc[db][4 * vq + 1], x.y);
+      x.z = fmaf(p.scale, acc[db][4 * vq + 2], x.z);
+      x.w = fmaf(p.scale, acc[db][4 * vq + 3], x.w);
+      *o4 = x;
+    }
+}
+
+// ------------------------------------------------------------------------------------ dK, dV
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int kBR = 32;                          // query rows per block
+  constexpr int kBlockBytes = kBR * T::kRowBytes;
+  constexpr int kLoads = kBR * T::kChunks / 256;   // 16-byte loads per thread per operand
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBlockBytes + 2 * kBR * 4];
+  unsigned char* Qs = smem;
+  unsigned char* Gs = smem + kBlockBytes;
+  float* Ls = reinterpret_cast<float*>(smem + 2 * kBlockBytes);
+  float* Ds = Ls + kBR;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int g = blockIdx.y;
+  int seg, tile;
+  bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, blockIdx.x, false, seg, tile);
+  const Seg ks = p.ks[seg];
+  const int key_wg = tile * 128;                    // the workgroup's first key in the run
+  const int key0 = key_wg + wave * 32;              // this wave's first key
+  const int kcol = key0 + col;                      // this lane's key (operand column)
+  const int kc = min(kcol, ks.len - 1);
+  const int kpos_wg_first = ks.pos + key_wg;
+  const int kpos_wave_last = ks.pos + min(key0 + 31, ks.len - 1);
+  const int kpos_lane = ks.pos + kcol;
+  const bool wave_keys_whole = key0 + 32 <= ks.len;
+  // K^T and V^T operands of this lane's key: k-step s covers d = 8 (half * D/16 + s) + e
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const int64_t krow = ((int64_t)(ks.loc + kc) * p.n_kv + g) * D + half * (D / 2);
+    const __bf16* kp = static_cast<const __bf16*>(p.k) + krow;
+    const __bf16* vp = static_cast<const __bf16*>(p.v) + krow;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kreg[s] = *reinterpret_cast<const bf16x8*>(kp + s * 8);
+      vreg[s] = *reinterpret_cast<const bf16x8*>(vp + s * 8);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[db][v] = dv[db][v] = 0.f;
+
+  const __bf16* Qg = static_cast<const __bf16*>(p.q);
+  const __bf16* Gg = static_cast<const __bf16*>(p.d_o);
+  u32x4 qpre[kLoads], gpre[kLoads];
+  float lpre = 0.f;
+  // loads of flattened rows [b, b + 32) of Q run qs (rows past the run repeat its last row and get
+  // LSE = +inf in the base-2 scale, hence P = 0); threads 0..31 load LSEs, 32..63 deltas
+  auto load_block = [&](const Seg& qs, int b) {
+    const int rows = qs.len * p.group;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = i * 256 + tid;
+      const int row = idx / T::kChunks, ch = idx % T::kChunks;
+      const int rr = min(b + row, rows - 1);
+      const int64_t src = ((int64_t)(qs.loc + rr / p.group) * p.n_h + g * p.group + rr % p.group) * D + ch * 8;
+      qpre[i] = *reinterpret_cast<const u32x4*>(Qg + src);
+      gpre[i] = *reinterpret_cast<const u32x4*>(Gg + src);
+    }
+    if (tid < 2 * kBR) {
+      const int row = tid & (kBR - 1);
+      const int rr = b + row;
+      if (rr < rows) {
+        const int64_t qrow = (int64_t)(qs.loc + rr / p.group) * p.n_h + g * p.group + rr % p.group;
+        if (tid < kBR) {
+          const float L = p.lse[qrow];
+          lpre = L == -INFINITY ? INFINITY : L * kLog2e;
+        } else {
+          lpre = p.delta[qrow];
+        }
+      } else {
+        lpre = tid < kBR ? INFINITY : 0.f;
+      }
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = i * 256 + tid;
+      const int row = idx / T::kChunks, ch = idx % T::kChunks;
+      const int o = T::off(row, ch * 8);
+      *reinterpret_cast<u32x4*>(Qs + o) = qpre[i];
+      *reinterpret_cast<u32x4*>(Gs + o) = gpre[i];
+    }
+    if (tid < 2 * kBR) Ls[tid] = lpre;  // Ds follows Ls
+  };
+
+  // the query blocks that see this workgroup's keys: runs of its sequence, from the first row
+  // whose token may see the first key
+  int j = 0, b = 0;
+  auto first_row = [&](const Seg& qs) -> int {
+    if (!p.causal) return 0;
+    return max(0, kpos_wg_first - qs.pos) * p.group;
+  };
+  auto advance = [&](int jj, int bb) {  // next (run, block start) at or after (jj, bb)
+    for (; jj < p.n_q_segs; ++jj, bb = -1) {
+      const Seg qs = p.qs[jj];
+      if (qs.seq != ks.seq) continue;
+      if (bb < 0) bb = first_row(qs);
+      if (bb < qs.len * p.group) break;
+    }
+    j = jj;
+    b = bb;
+  };
+  advance(0, -1);
+  if (j < p.n_q_segs) load_block(p.qs[j], b);
+  while (j < p.n_q_segs) {
+    const Seg qs = p.qs[j];
+    const int cur_b = b;
+    __syncthreads();
+    store_block();
+    __syncthreads();
+    advance(j, b + kBR);
+    if (j < p.n_q_segs) load_block(p.qs[j], b);
+
+    // S = Q K^T and dP = dO V^T: lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
+    f32x16 s, dpm;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = dpm[v] = 0.f;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const int o = T::off(col, 8 * (half * (D / 16) + st));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Qs, o), kreg[st], s, 0, 0, 0);
+      dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Gs, o), vreg[st], dpm, 0, 0, 0);
+    }
+    // the block's rows are all visible to all of this wave's keys, or the mask is needed
+    const bool masked = !wave_keys_whole ||
+                        (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
+    bf16x8 pp[2], ps[2];
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
+      const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * vq + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * vq + e;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[v], p.scale_log2, -lv[e]));
+        if (masked) {
+          const int rr = cur_b + 8 * vq + 4 * half + e;
+          const bool vis = kcol < ks.len && (!p.causal || qs.pos + rr / p.group >= kpos_lane);
+          pr = vis ? pr : 0.f;
+        }
+        pp[v >> 3][v & 7] = (__bf16)pr;
+        ps[v >> 3][v & 7] = (__bf16)(pr * (dpm[v] - dlv[e]));
+      }
+    }
+    // dV += P^T dO and dK += dS^T Q: k-step t holds rows 16 t + 8 (e/4) + 4 half + e % 4
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pp[t], lds_tr8<D>(Gs, 16 * t, db * 32, lane),
+                                                         dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ps[t], lds_tr8<D>(Qs, 16 * t, db * 32, lane),
+                                                         dk[db], 0, 0, 0);
+      }
+  }
+  // accumulators: lane (d = db*32 + col, half) holds keys key0 + 8 (v/4) + 4 half + v % 4
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
+    if (key >= ks.len) continue;
+    const int64_t base = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + col;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      p.dk[base + db * 32] = fmaf(p.scale, dk[db][v], p.dk[base + db * 32]);
+      p.dv[base + db * 32] += dv[db][v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------- delta
+// delta = dO . O per row (the row term of the softmax gradient). 16 lanes per row.
+template <int D, bool DO_BF16>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const float* o, const void* d_o, int64_t rows,
+                                                        float* delta) {
+  constexpr int kPer = D / 16;
+  const int sub = threadIdx.x & 15;
+  for (int64_t r = (int64_t)blockIdx.x * 16 + threadIdx.x / 16; r < rows; r += (int64_t)gridDim.x * 16) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t i = r * D + sub * kPer + e;
+      const float gv = DO_BF16 ? (float)static_cast<const __bf16*>(d_o)[i] : static_cast<const float*>(d_o)[i];
+      acc = fmaf(gv, o[i], acc);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (sub == 0) delta[r] = acc;
+  }
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d_h, hipStream_t stream) {
+  if (p.q_tiles > 0) {
+    const dim3 grid(p.q_tiles, p.n_kv);
+    if (d_h == 64)
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(512), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.kv_tiles > 0) {
+    const dim3 grid(p.kv_tiles, p.n_kv);
+    if (d_h == 64)
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(const float* o, const void* d_o, bool do_bf16, int64_t rows, int d_h,
+                            float* delta, hipStream_t stream) {
+  const int64_t blocks = std::min<int64_t>((rows + 15) / 16, 65536);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (d_h == 64) {
+    if (do_bf16) hipLaunchKernelGGL((bwd_delta_kernel<64, true>), grid, block, 0, stream, o, d_o, rows, delta);
+    else hipLaunchKernelGGL((bwd_delta_kernel<64, false>), grid, block, 0, stream, o, d_o, rows, delta);
+  } else {
+    if (do_bf16) hipLaunchKernelGGL((bwd_delta_kernel<128, true>), grid, block, 0, stream, o, d_o, rows, delta);
+    else hipLaunchKernelGGL((bwd_delta_kernel<128, false>), grid, block, 0, stream, o, d_o, rows, delta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpk

@@ -87,6 +87,41 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Arguments of one backward launch pair (dQ kernel, then dK/dV kernel) for one Q shard against
+// one KV shard. Q tiles (256 rows) are numbered over the Q runs in `q_order`, the last tile of a run
+// first; KV tiles (128 keys) over the KV runs in `kv_order`, the first tile of a run first (the
+// causally heaviest tiles start first either way).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;    // final log-sum-exp of each (token, head), natural log
+  const float* delta;  // dO . O of each (token, head)
+  float* dq;           // [tq, n_h, d_h] fp32, accumulated
+  float* dk;           // [tk, n_kv, d_h] fp32, accumulated
+  float* dv;
+  int32_t n_h;
+  int32_t n_kv;
+  int32_t group;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+  int32_t n_q_segs;
+  int32_t n_kv_segs;
+  int32_t q_tiles;
+  int32_t kv_tiles;
+  int32_t q_prefix[kMaxSegs + 1];
+  int32_t kv_prefix[kMaxSegs + 1];
+  int8_t q_order[kMaxSegs];
+  int8_t kv_order[kMaxSegs];
+  Seg qs[kMaxSegs];
+  Seg ks[kMaxSegs];
+};
+static_assert(sizeof(BwdParams) <= 4096, "kernel arguments are limited to 4 KB");
+constexpr int kBwdQRows = 256;  // query rows per dQ workgroup
+constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup
+
 // Launchers (defined next to their kernels). Each returns the HIP launch status.
 hipError_t launch_attn_f32(const AttnParams& p, int d_h, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream);
@@ -95,6 +130,9 @@ hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream);
 // Device address of the allocation-free decode workspace (CP_DECODE_NOALLOC_MAX_BYTES) on the
 // current device; looked up once per device, then cached.
 hipError_t decode_scratch(void** out);
+hipError_t launch_bwd(const BwdParams& p, int d_h, hipStream_t stream);
+hipError_t launch_bwd_delta(const float* o, const void* d_o, bool do_bf16, int64_t rows, int d_h,
+                            float* delta, hipStream_t stream);
 
 // Rows per workgroup tile of each attention kernel (the host plans tiles with these).
 constexpr int kTileRowsF32 = 64;

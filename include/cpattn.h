@@ -230,6 +230,53 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
                    cp_dtype out_dtype, float* const* lse_out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Backward ([CPEP §6]: with context parallelism the backward returns each rank's K/V gradient
+ * contributions to the ranks that own those K/V chunks, a reduce-scatter; on one device that is
+ * a sum per KV shard). For a row (token, head) with FINAL output O and LSE (over every shard the
+ * row sees) and output gradient dO, and a key j it sees: P = exp(scale * q.k_j - LSE),
+ * dS = P (dO.v_j - delta) with delta = dO.O; then dQ += scale * dS k_j, dK_j += scale * dS q,
+ * dV_j += P dO. Summed over ring steps (dQ) and over the ranks that visit a KV shard (dK, dV) the
+ * contributions are the exact gradient of the whole attention.
+ *
+ * cp_attn_bwd_delta -- delta[r] = sum_d dO[r][d] * O[r][d] for rows = T_q * N_H.
+ *   o: device fp32 [rows, d_h] (the final forward output); d_o: device [rows, d_h] in do_dtype;
+ *   delta: device fp32 [rows].
+ * ------------------------------------------------------------------------------------------- */
+int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_t rows, int d_h,
+                      float* delta, void* stream);
+
+/* cp_partial_attn_bwd -- one ring step's backward: the contributions of a Q shard against one KV
+ * shard, ADDED into dq, dk and dv (callers zero them first).
+ *   q, k, v, tq, tk, n_h, n_kv, d_h, segment tables, causal, softmax_scale: as cp_partial_attn
+ *     (in_dtype must be CP_BF16; the products run on bf16 MFMA with fp32 accumulation, the
+ *     probabilities and score gradients rounded to bf16 as operands).
+ *   lse: device fp32 [tq, n_h], the final natural-log LSE of each row (-inf: the row saw no key);
+ *   delta: device fp32 [tq, n_h] from cp_attn_bwd_delta; d_o: device bf16 [tq, n_h, d_h].
+ *   dq: device fp32 [tq, n_h, d_h]; dk, dv: device fp32 [tk, n_kv, d_h]; all 16-byte aligned.
+ * Contributions of one call are summed in a fixed order (deterministic); calls that add into the
+ * same buffers must be ordered on one stream.
+ * ------------------------------------------------------------------------------------------- */
+int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq, int64_t tk,
+                        int n_h, int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs,
+                        int n_q_segs, const cp_segment* kv_segs, int n_kv_segs, int causal,
+                        float softmax_scale, const float* lse, const float* delta, const void* d_o,
+                        float* dq, float* dk, float* dv, void* stream);
+
+/* cp_ring_pass_kv_bwd -- one rank's ring Pass-KV backward on one device: delta of the rank's rows
+ * into `delta` (device fp32 [tq, n_h], caller-owned), then at step t the contributions against KV
+ * shard (rank - t) mod cp_world, added into dq and into that shard's dk_shards[s] / dv_shards[s]
+ * (device fp32 [tk[s], n_kv, d_h]). o, lse: the rank's final forward output and LSE; d_o: bf16.
+ * Other arguments as cp_ring_pass_kv. Every step is validated before the first launch.
+ * ------------------------------------------------------------------------------------------- */
+int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
+                        int cp_world, int rank, const void* const* k_shards,
+                        const void* const* v_shards, const int64_t* tk,
+                        const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
+                        int d_h, cp_dtype in_dtype, int causal, float softmax_scale, const float* o,
+                        const float* lse, const void* d_o, float* delta, float* dq,
+                        float* const* dk_shards, float* const* dv_shards, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * cp_select_ring_variant -- runtime choice between ring Pass-KV and ring Pass-Q ([CPMTI §3
  * "核心公式", Algorithm 1]): Pass-KV when the KV-cache miss rate T / (T + P) exceeds
  * 2 * N_KV / N_H (condition 1), or when the SendRecv of one ring step can be hidden behind that

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 BLOCK = 4096
-TID_Q, TID_K, TID_V, TID_LEN, TID_PO, TID_PL, TID_MISC = 1, 2, 3, 4, 5, 6, 7
+TID_Q, TID_K, TID_V, TID_LEN, TID_PO, TID_PL, TID_MISC, TID_DO = 1, 2, 3, 4, 5, 6, 7, 8
 
 K1 = 1024
 

@@ -18,5 +18,9 @@ hipError_t launch_attn_bf16(const AttnParams&, int, hipStream_t) { return unexpe
 hipError_t launch_merge(const MergeParams&, hipStream_t) { return unexpected("launch_merge"); }
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return unexpected("launch_decode"); }
 hipError_t decode_scratch(void**) { return unexpected("decode_scratch"); }
+hipError_t launch_bwd(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd"); }
+hipError_t launch_bwd_delta(const float*, const void*, bool, int64_t, int, float*, hipStream_t) {
+  return unexpected("launch_bwd_delta");
+}
 
 }  // namespace cpk
