@@ -14,10 +14,10 @@ value = causal-useful TFLOP/s: 4 * D_H flops per visible (query token, query hea
 masked and skipped work is not counted. The same JSON line reports the dominant kernel's roofline
 (cp_partial_attn's MFMA kernel, per-launch time from HIP events on the launch stream), secondary
 measurements (the 128K CP4 prefill, the persistent-KV workload as Pass-Q and as Pass-KV with the
-ring-variant selector's choice, the merge, split-KV decode with both workspace precisions, the
-one-request decode step eager and graph-replayed), and the fp64 oracle timed on the host cores:
-measured on a bounded sample of each large workload (and checked against the GPU output of the
-same run), in full on the small ones.
+ring-variant selector's choice, the merge, the ring backward, split-KV decode with both workspace
+precisions, the one-request decode step eager and graph-replayed), and the fp64 oracle timed on the
+host cores: measured on a bounded sample of each large workload (and checked against the GPU output
+of the same run), in full on the small ones.
 """
 from __future__ import annotations
 
@@ -242,6 +242,32 @@ def run_prefill_128k(torch, cp, si, steps):
            "per_launch": {"avg_ms": round(avg_ms, 4), "tflops": round(ach, 1), "launches": n,
                           "frac_of_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}}
     return out, wl, r0
+
+
+def run_backward(torch, cp, si, wl, seed=0):
+    """The ring Pass-KV backward of every rank of a Pass-KV workload (after its forward ran, its
+    outputs and LSEs serve as the saved activations; dO is seeded bf16). Useful backward flops:
+    10 * D_H per visible (token, head, key) triple (S recomputed, dP, dV, dK, dQ: five products of
+    2 D_H), i.e. 2.5 times the forward's."""
+    N, n_h, d = wl.N, wl.n_h, wl.d
+    d_o = {r: tokens_bf16(torch, si, seed, si.TID_DO, wl.shards[r][1], (n_h, d))[0] for r in wl.ranks}
+    delta = {r: torch.empty(wl.qs[r].shape[0], n_h, device="cuda") for r in wl.ranks}
+    dq = {r: torch.zeros(wl.qs[r].shape[0], n_h, d, device="cuda") for r in wl.ranks}
+    dks = [torch.zeros(k.shape, device="cuda") for k in wl.ks]
+    dvs = [torch.zeros(k.shape, device="cuda") for k in wl.ks]
+
+    def step():
+        for r in wl.ranks:
+            cp.ring_pass_kv_bwd(wl.qs[r], wl.shards[r][0], r, wl.ks, wl.vs, wl.kv_segs, True, wl.scale,
+                                wl.o[r], wl.lse[r], d_o[r], delta[r], dq[r], dks, dvs, check=False)
+    ms = time_reps(torch, step, 3, warm=1)
+    flops = wl.flops * 2.5
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"backward {wl.name}: {ms:.2f} ms for {len(wl.ranks)} ranks, {tf:.1f} useful TFLOP/s")
+    return {"metric": "causal-useful backward TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
+            "ms_all_ranks": round(ms, 3), "ranks": len(wl.ranks),
+            "useful_tflop": round(flops / 1e12, 3), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_visible_pair": 10 * d}
 
 
 def run_persistent_kv(torch, cp, si, seed=0):
@@ -682,6 +708,7 @@ def main():
         r0["flops"] = wl128.flops
         kept["r128k"] = r0
         secondary["merge_4parts_128k_cp4"] = run_merge(torch, cp, wl128)
+        secondary["backward_128k_cp4"] = run_backward(torch, cp, si, wl128)
         del wl128
         torch.cuda.empty_cache()
         spkv, r0 = run_persistent_kv(torch, cp, si)

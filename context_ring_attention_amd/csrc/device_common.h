@@ -51,6 +51,19 @@ __device__ inline void running_merge_weights(float lse_prev, float lse_new, floa
   lse_out = M + logf(s);
 }
 
+// max(a, b) as one v_max_f32 (the compiler's fmaxf also quiets each operand first, two more VALU
+// instructions on the row max's critical path; scores are never signalling NaNs). Device pass
+// only, like every AMDGPU-constraint asm here.
+__device__ inline float vmax(float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+#else
+  return a > b ? a : b;
+#endif
+}
+
 // Max of x over lanes l and l ^ 32 (the two half-waves), without going through LDS: swapping
 // the upper half of one copy with the lower half of another leaves each lane holding both values.
 // Each result is copied out of the returned vector before its bit cast: a bit cast of a vector
@@ -61,7 +74,7 @@ __device__ inline float max_xor32(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   const uint32_t r0 = sw[0], r1 = sw[1];
-  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  return vmax(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 // Max of x over lanes l and l ^ 16 (odd and even 16-lane rows), without going through LDS.
@@ -69,7 +82,7 @@ __device__ inline float max_xor16(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   const uint32_t r0 = sw[0], r1 = sw[1];
-  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  return vmax(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
 }  // namespace cpk
