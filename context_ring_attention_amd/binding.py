@@ -501,13 +501,12 @@ def partial_attn_bwd(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: floa
     tq, n_h, d = q.shape
     tk, n_kv = k.shape[0], k.shape[1]
     if check:
-        bf16 = _types("bf16")
-        _req(q, "q", bf16)
-        _req(k, "k", bf16, (tk, n_kv, d))
-        _req(v, "v", bf16, (tk, n_kv, d))
+        _req(q, "q", _in_types())
+        _req(k, "k", (q.dtype,), (tk, n_kv, d))
+        _req(v, "v", (q.dtype,), (tk, n_kv, d))
         _req(lse, "lse", _float_types(), numel=tq * n_h)
         _req(delta, "delta", _float_types(), numel=tq * n_h)
-        _req(d_o, "d_o", bf16, (tq, n_h, d))
+        _req(d_o, "d_o", (q.dtype,), (tq, n_h, d))
         _req(dq, "dq", _float_types(), (tq, n_h, d))
         _req(dk, "dk", _float_types(), (tk, n_kv, d))
         _req(dv, "dv", _float_types(), (tk, n_kv, d))
@@ -530,17 +529,16 @@ def ring_pass_kv_bwd(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: 
     if not (len(v_shards) == len(kv_segs) == len(dk_shards) == len(dv_shards) == N):
         raise ValueError("k_shards, v_shards, kv_segs, dk_shards and dv_shards need one entry per shard")
     if check:
-        bf16 = _types("bf16")
-        _req(q, "q", bf16)
+        _req(q, "q", _in_types())
         _req(o, "o", _float_types(), (tq, n_h, d))
         _req(lse, "lse", _float_types(), numel=tq * n_h)
-        _req(d_o, "d_o", bf16, (tq, n_h, d))
+        _req(d_o, "d_o", (q.dtype,), (tq, n_h, d))
         _req(delta, "delta", _float_types(), numel=tq * n_h)
         _req(dq, "dq", _float_types(), (tq, n_h, d))
         for i in range(N):
             shp = tuple(k_shards[i].shape)
-            _req(k_shards[i], f"k_shards[{i}]", bf16)
-            _req(v_shards[i], f"v_shards[{i}]", bf16, shp)
+            _req(k_shards[i], f"k_shards[{i}]", (q.dtype,))
+            _req(v_shards[i], f"v_shards[{i}]", (q.dtype,), shp)
             _req(dk_shards[i], f"dk_shards[{i}]", _float_types(), shp)
             _req(dv_shards[i], f"dv_shards[{i}]", _float_types(), shp)
     vp = ctypes.c_void_p

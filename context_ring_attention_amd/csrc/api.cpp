@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "bwd_f32.h"
 #include "cp_internal.h"
 #include "cpattn.h"
 
@@ -320,7 +321,7 @@ int partial_attn_problems(const Problem* probs, int n_probs, int n_h, int n_kv, 
 // Tile plan of one backward launch pair over one piece's tables: Q runs ordered by the causal
 // work of their last tile (dQ workgroups, last tile of a run first), KV runs by the work of their
 // first tile (dK/dV workgroups, first tile of a run first), heaviest first.
-void plan_bwd(cpk::BwdParams& p, const Piece& pc) {
+void plan_bwd(cpk::BwdParams& p, const Piece& pc, int q_rows_per_tile, int keys_per_tile) {
   p.n_q_segs = (int)pc.q.size();
   p.n_kv_segs = (int)pc.kv.size();
   for (int i = 0; i < p.n_q_segs; ++i) p.qs[i] = to_seg(pc.q[i]);
@@ -355,14 +356,14 @@ void plan_bwd(cpk::BwdParams& p, const Piece& pc) {
     const int i = qw[s2].second;
     p.q_order[s2] = (int8_t)i;
     const int64_t rows = (int64_t)p.qs[i].len * p.group;
-    p.q_prefix[s2 + 1] = p.q_prefix[s2] + (int)((rows + cpk::kBwdQRows - 1) / cpk::kBwdQRows);
+    p.q_prefix[s2 + 1] = p.q_prefix[s2] + (int)((rows + q_rows_per_tile - 1) / q_rows_per_tile);
   }
   p.q_tiles = p.q_prefix[p.n_q_segs];
   p.kv_prefix[0] = 0;
   for (int s2 = 0; s2 < p.n_kv_segs; ++s2) {
     const int j = kw[s2].second;
     p.kv_order[s2] = (int8_t)j;
-    p.kv_prefix[s2 + 1] = p.kv_prefix[s2] + (p.ks[j].len + cpk::kBwdKeys - 1) / cpk::kBwdKeys;
+    p.kv_prefix[s2 + 1] = p.kv_prefix[s2] + (p.ks[j].len + keys_per_tile - 1) / keys_per_tile;
   }
   p.kv_tiles = p.kv_prefix[p.n_kv_segs];
 }
@@ -370,7 +371,7 @@ void plan_bwd(cpk::BwdParams& p, const Piece& pc) {
 // Argument checks of one backward step beyond those of its forward problem.
 int validate_bwd_extra(const float* lse, const float* delta, const void* d_o, const float* dq,
                        const float* dk, const float* dv, cp_dtype in_dtype, int n_q_segs, int n_kv_segs) {
-  if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "the backward supports bf16 inputs only");
+  if (in_dtype != CP_BF16 && in_dtype != CP_F32) return fail(CP_E_ARG, "in_dtype=%d", (int)in_dtype);
   if (n_q_segs > 0 && (!lse || !delta || !d_o || !dq)) return fail(CP_E_ARG, "lse, delta, d_o or dq is NULL");
   if (n_kv_segs > 0 && (!dk || !dv)) return fail(CP_E_ARG, "dk or dv is NULL");
   if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -649,9 +650,11 @@ int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq,
     p.causal = causal ? 1 : 0;
     p.scale = softmax_scale;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
-    plan_bwd(p, pc);
+    const bool bf16 = in_dtype == CP_BF16;
+    plan_bwd(p, pc, bf16 ? cpk::kBwdQRows : cpk::kBwdF32Rows, bf16 ? cpk::kBwdKeys : cpk::kBwdF32Keys);
     if (p.q_tiles == 0 || p.kv_tiles == 0) continue;  // no pair of this piece can be visible
-    st = launch_status(cpk::launch_bwd(p, d_h, s), "cp_partial_attn_bwd");
+    st = launch_status(bf16 ? cpk::launch_bwd(p, d_h, s) : cpk::launch_bwd_f32(p, d_h, s),
+                       "cp_partial_attn_bwd");
     if (st) return st;
   }
   return ok();

@@ -470,3 +470,129 @@ hipError_t launch_bwd_delta(const float* o, const void* d_o, bool do_bf16, int64
 }
 
 }  // namespace cpk
+
+// --------------------------------------------------------------------------- fp32 inputs
+// The same gradients for fp32 inputs in fp32 arithmetic throughout (no reduced-precision MFMA),
+// for small workloads where exactness to ~1e-5 matters more than speed.
+namespace cpk {
+
+// One thread per query row (token, head): dQ over the keys it sees.
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(const BwdParams p) {
+  int seg, tile;
+  bwd_locate(p.q_prefix, p.q_order, p.n_q_segs, blockIdx.x, false, seg, tile);
+  const int g = blockIdx.y;
+  const Seg qs = p.qs[seg];
+  const int rows = qs.len * p.group;
+  const int r = tile * 64 + (int)threadIdx.x;
+  if (r >= rows) return;
+  const int tok = r / p.group;
+  const int64_t qrow = (int64_t)(qs.loc + tok) * p.n_h + g * p.group + r % p.group;
+  const int qpos = qs.pos + tok;
+  const float L = p.lse[qrow];
+  if (L == -INFINITY) return;  // the row saw no key
+  const float dlt = p.delta[qrow];
+  const float* Q = static_cast<const float*>(p.q) + qrow * D;
+  const float* G = static_cast<const float*>(p.d_o) + qrow * D;
+  const float* K = static_cast<const float*>(p.k);
+  const float* V = static_cast<const float*>(p.v);
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  for (int j = 0; j < p.n_kv_segs; ++j) {
+    const Seg ks = p.ks[j];
+    if (ks.seq != qs.seq) continue;
+    const int n = visible_prefix(ks, qpos, p.causal);
+    for (int key = 0; key < n; ++key) {
+      const float* kr = K + ((int64_t)(ks.loc + key) * p.n_kv + g) * D;
+      const float* vr = V + ((int64_t)(ks.loc + key) * p.n_kv + g) * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(Q[d], kr[d], s);
+        dp = fmaf(G[d], vr[d], dp);
+      }
+      const float pr = expf(s * p.scale - L);
+      const float ds = pr * (dp - dlt);
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+    }
+  }
+  float* out = p.dq + qrow * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) out[d] = fmaf(p.scale, acc[d], out[d]);
+}
+
+// One thread per key (and KV head): dK and dV over the rows that see it, accumulated in LDS.
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(const BwdParams p) {
+  __shared__ float acc_k[64 * D];
+  __shared__ float acc_v[64 * D];
+  int seg, tile;
+  bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, blockIdx.x, false, seg, tile);
+  const int g = blockIdx.y;
+  const Seg ks = p.ks[seg];
+  const int t = threadIdx.x;
+  const int key = tile * 64 + t;
+  if (key >= ks.len) return;  // no barrier below: threads are independent
+  float* ak = acc_k + t * D;
+  float* av = acc_v + t * D;
+  for (int d = 0; d < D; ++d) ak[d] = av[d] = 0.f;
+  const int kpos = ks.pos + key;
+  const int64_t krow = ((int64_t)(ks.loc + key) * p.n_kv + g) * D;
+  const float* kr = static_cast<const float*>(p.k) + krow;
+  const float* vr = static_cast<const float*>(p.v) + krow;
+  for (int i = 0; i < p.n_q_segs; ++i) {
+    const Seg qs = p.qs[i];
+    if (qs.seq != ks.seq) continue;
+    const int tok0 = p.causal ? max(0, kpos - qs.pos) : 0;
+    for (int tok = tok0; tok < qs.len; ++tok) {
+      for (int h = 0; h < p.group; ++h) {
+        const int64_t qrow = (int64_t)(qs.loc + tok) * p.n_h + g * p.group + h;
+        const float L = p.lse[qrow];
+        if (L == -INFINITY) continue;
+        const float* Q = static_cast<const float*>(p.q) + qrow * D;
+        const float* G = static_cast<const float*>(p.d_o) + qrow * D;
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+          s = fmaf(Q[d], kr[d], s);
+          dp = fmaf(G[d], vr[d], dp);
+        }
+        const float pr = expf(s * p.scale - L);
+        const float ds = pr * (dp - p.delta[qrow]);
+        for (int d = 0; d < D; ++d) {
+          ak[d] = fmaf(ds, Q[d], ak[d]);
+          av[d] = fmaf(pr, G[d], av[d]);
+        }
+      }
+    }
+  }
+  float* dk = p.dk + krow;
+  float* dv = p.dv + krow;
+  for (int d = 0; d < D; ++d) {
+    dk[d] = fmaf(p.scale, ak[d], dk[d]);
+    dv[d] += av[d];
+  }
+}
+
+hipError_t launch_bwd_f32(const BwdParams& p, int d_h, hipStream_t stream) {
+  if (p.q_tiles > 0) {
+    const dim3 grid(p.q_tiles, p.n_kv);
+    if (d_h == 64)
+      hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.kv_tiles > 0) {
+    const dim3 grid(p.kv_tiles, p.n_kv);
+    if (d_h == 64)
+      hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpk

@@ -247,11 +247,11 @@ int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_
 
 /* cp_partial_attn_bwd -- one ring step's backward: the contributions of a Q shard against one KV
  * shard, ADDED into dq, dk and dv (callers zero them first).
- *   q, k, v, tq, tk, n_h, n_kv, d_h, segment tables, causal, softmax_scale: as cp_partial_attn
- *     (in_dtype must be CP_BF16; the products run on bf16 MFMA with fp32 accumulation, the
- *     probabilities and score gradients rounded to bf16 as operands).
+ *   q, k, v, tq, tk, n_h, n_kv, d_h, segment tables, causal, softmax_scale: as cp_partial_attn.
+ *     bf16 inputs run the products on bf16 MFMA with fp32 accumulation (probabilities and score
+ *     gradients rounded to bf16 as operands); fp32 inputs run in fp32 arithmetic throughout.
  *   lse: device fp32 [tq, n_h], the final natural-log LSE of each row (-inf: the row saw no key);
- *   delta: device fp32 [tq, n_h] from cp_attn_bwd_delta; d_o: device bf16 [tq, n_h, d_h].
+ *   delta: device fp32 [tq, n_h] from cp_attn_bwd_delta; d_o: device [tq, n_h, d_h] in in_dtype.
  *   dq: device fp32 [tq, n_h, d_h]; dk, dv: device fp32 [tk, n_kv, d_h]; all 16-byte aligned.
  * Contributions of one call are summed in a fixed order (deterministic); calls that add into the
  * same buffers must be ordered on one stream.
@@ -265,7 +265,7 @@ int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq,
 /* cp_ring_pass_kv_bwd -- one rank's ring Pass-KV backward on one device: delta of the rank's rows
  * into `delta` (device fp32 [tq, n_h], caller-owned), then at step t the contributions against KV
  * shard (rank - t) mod cp_world, added into dq and into that shard's dk_shards[s] / dv_shards[s]
- * (device fp32 [tk[s], n_kv, d_h]). o, lse: the rank's final forward output and LSE; d_o: bf16.
+ * (device fp32 [tk[s], n_kv, d_h]). o, lse: the rank's final forward output and LSE; d_o in in_dtype.
  * Other arguments as cp_ring_pass_kv. Every step is validated before the first launch.
  * ------------------------------------------------------------------------------------------- */
 int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "bwd_f32.h"
 #include "cp_internal.h"
 
 namespace cpk {
@@ -19,6 +20,7 @@ hipError_t launch_merge(const MergeParams&, hipStream_t) { return unexpected("la
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return unexpected("launch_decode"); }
 hipError_t decode_scratch(void**) { return unexpected("decode_scratch"); }
 hipError_t launch_bwd(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd"); }
+hipError_t launch_bwd_f32(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd_f32"); }
 hipError_t launch_bwd_delta(const float*, const void*, bool, int64_t, int, float*, hipStream_t) {
   return unexpected("launch_bwd_delta");
 }

@@ -8,10 +8,11 @@ they must equal the oracle's gradient of the whole attention restricted to each 
 and every rank's dQ the gradient of its rows. Both sides take the same saved forward results: the
 oracle's forward output and LSE rounded to fp32.
 
-Bound (derived in the design notes): the products run on bf16 MFMA with fp32 accumulation, and the
-probabilities P and score gradients dS are rounded to bf16 (at most 2^-8 relative each) as MFMA
-operands, so each gradient element may differ from the exact value by a small fraction of the
-largest element of its tensor: max|err| <= 1e-2 * max|ref| + 1e-3.
+Bound (derived in the design notes): for bf16 inputs the products run on bf16 MFMA with fp32
+accumulation, and the probabilities P and score gradients dS are rounded to bf16 (at most 2^-8
+relative each) as MFMA operands, so each gradient element may differ from the exact value by a small
+fraction of the largest element of its tensor: max|err| <= 1e-2 * max|ref| + 1e-3. fp32 inputs run
+in fp32 throughout: max|err| <= 1e-5 * max(1, max|ref|).
 """
 import numpy as np
 import pytest
@@ -23,7 +24,7 @@ from ring_cases import Planted, device_tensor, log, oracle_view, product_shards,
 
 pytestmark = pytest.mark.gpu
 
-REL, ABS = 1e-2, 1e-3
+BOUND = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-5)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,46 +33,49 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _check(gpu, ref, what):
+def _check(gpu, ref, what, dtype="bf16"):
+    rel, tol_abs = BOUND[dtype]
     g = gpu.float().cpu().numpy().astype(np.float64).reshape(ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite"
     err = float(np.max(np.abs(g - ref))) if ref.size else 0.0
     scale = float(np.max(np.abs(ref))) if ref.size else 0.0
     log(f"  {what}: max|err|={err:.3e} max|ref|={scale:.3e} rel={err / max(scale, 1e-30):.2e}")
-    assert err <= REL * scale + ABS, what
+    bound = rel * scale + tol_abs if dtype == "bf16" else rel * max(1.0, scale)
+    assert err <= bound, what
 
 
-def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=None):
+def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=None, dtype="bf16"):
     from context_ring_attention_amd import binding as cp
     ranges = [(i, 0, L) for i, L in enumerate(seqs)]
     scale = scale_of(d)
+    std = 1.0 / np.sqrt(d) if dtype == "f32" else 1.0
     log(f"bwd seqs={seqs[:8]}{'...' if len(seqs) > 8 else ''} N={N} n_h={n_h} n_kv={n_kv} d={d} "
-        f"causal={causal}")
+        f"causal={causal} {dtype}")
     sh = product_shards(ranges, N)
     # oracle side: the whole batch in global token order
     T = int(sum(seqs))
     g_all = np.arange(T)
     seq_all = np.concatenate([np.full(L, i, np.int32) for i, L in enumerate(seqs)])
     pos_all = np.concatenate([np.arange(L, dtype=np.int64) for L in seqs])
-    qf = oracle_view(seed, si.TID_Q, g_all, (n_h, d), 1.0, "bf16", gen)
-    kf = oracle_view(seed, si.TID_K, g_all, (n_kv, d), 1.0, "bf16", gen)
-    vf = oracle_view(seed, si.TID_V, g_all, (n_kv, d), 1.0, "bf16", gen)
-    gf = oracle_view(seed, si.TID_DO, g_all, (n_h, d), 1.0, "bf16")
+    qf = oracle_view(seed, si.TID_Q, g_all, (n_h, d), std, dtype, gen)
+    kf = oracle_view(seed, si.TID_K, g_all, (n_kv, d), std, dtype, gen)
+    vf = oracle_view(seed, si.TID_V, g_all, (n_kv, d), std, dtype, gen)
+    gf = oracle_view(seed, si.TID_DO, g_all, (n_h, d), 1.0, dtype)
     o_ref, l_ref = oracle.attention(qf, kf, vf, n_h, n_kv, seq_all, pos_all, seq_all, pos_all, causal, scale)
     o32, l32 = o_ref.astype(np.float32), l_ref.astype(np.float32)
     dq_ref, dk_ref, dv_ref = oracle.attention_backward(qf, kf, vf, n_h, n_kv, seq_all, pos_all, seq_all,
                                                        pos_all, causal, scale, o32, l32, gf)
     # device side: every rank's ring backward, dK/dV summed per shard
-    ks = [device_tensor(seed, si.TID_K, sh[s].tokens, (n_kv, d), 1.0, "bf16", gen=gen) for s in range(N)]
-    vs = [device_tensor(seed, si.TID_V, sh[s].tokens, (n_kv, d), 1.0, "bf16", gen=gen) for s in range(N)]
+    ks = [device_tensor(seed, si.TID_K, sh[s].tokens, (n_kv, d), std, dtype, gen=gen) for s in range(N)]
+    vs = [device_tensor(seed, si.TID_V, sh[s].tokens, (n_kv, d), std, dtype, gen=gen) for s in range(N)]
     dks = [torch.zeros(k.shape, device="cuda") for k in ks]
     dvs = [torch.zeros(k.shape, device="cuda") for k in ks]
     kv_segs = [sh[s].segs for s in range(N)]
     dqs = {}
     for r in range(N):
         toks = sh[r].tokens
-        q = device_tensor(seed, si.TID_Q, toks, (n_h, d), 1.0, "bf16", gen=gen)
-        d_o = device_tensor(seed, si.TID_DO, toks, (n_h, d), 1.0, "bf16")
+        q = device_tensor(seed, si.TID_Q, toks, (n_h, d), std, dtype, gen=gen)
+        d_o = device_tensor(seed, si.TID_DO, toks, (n_h, d), 1.0, dtype)
         o = torch.from_numpy(o32[toks]).cuda()
         lse = torch.from_numpy(l32[toks]).cuda()
         delta = torch.empty(len(toks), n_h, device="cuda")
@@ -92,15 +96,15 @@ def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=Non
             p_dq, p_dk, p_dv = oracle.attention_backward(
                 qf[toks], kf[kt], vf[kt], n_h, n_kv, seq_all[toks], pos_all[toks], seq_all[kt],
                 pos_all[kt], causal, scale, o32[toks], l32[toks], gf[toks])
-            _check(dq1, p_dq, f"rank {r} step {t} dQ")
-            _check(dk1, p_dk, f"rank {r} step {t} dK (shard {s})")
-            _check(dv1, p_dv, f"rank {r} step {t} dV (shard {s})")
+            _check(dq1, p_dq, f"rank {r} step {t} dQ", dtype)
+            _check(dk1, p_dk, f"rank {r} step {t} dK (shard {s})", dtype)
+            _check(dv1, p_dv, f"rank {r} step {t} dV (shard {s})", dtype)
     torch.cuda.synchronize()
     for r in range(N):
-        _check(dqs[r], dq_ref[sh[r].tokens], f"rank {r} dQ")
+        _check(dqs[r], dq_ref[sh[r].tokens], f"rank {r} dQ", dtype)
     for s in range(N):
-        _check(dks[s], dk_ref[sh[s].tokens], f"shard {s} dK (all ranks)")
-        _check(dvs[s], dv_ref[sh[s].tokens], f"shard {s} dV (all ranks)")
+        _check(dks[s], dk_ref[sh[s].tokens], f"shard {s} dK (all ranks)", dtype)
+        _check(dvs[s], dv_ref[sh[s].tokens], f"shard {s} dV (all ranks)", dtype)
 
 
 def test_bwd_ring_cp4_two_sequences():
@@ -133,3 +137,13 @@ def test_bwd_wide_scores():
 def test_bwd_many_sequences_split_over_launches():
     lens = [int(x) for x in np.random.default_rng(60).integers(1, 60, size=70)]
     run_bwd(lens, 2, 16, 1, 128, seed=60)
+
+
+def test_bwd_tiny_ring_fp32():
+    """The tiny fp32 ring's backward: T=256, 4 query heads, 1 KV head, D=64, CP=4."""
+    run_bwd([256], 4, 4, 1, 64, seed=61, step_check=(2, 1), dtype="f32")
+
+
+def test_bwd_fp32_ragged_gqa_d128():
+    run_bwd([77, 300, 5], 3, 8, 2, 128, seed=62, dtype="f32")
+    run_bwd([200], 2, 4, 4, 64, seed=63, causal=False, dtype="f32")
