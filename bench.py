@@ -256,18 +256,24 @@ def run_backward(torch, cp, si, wl, seed=0):
     dks = [torch.zeros(k.shape, device="cuda") for k in wl.ks]
     dvs = [torch.zeros(k.shape, device="cuda") for k in wl.ks]
 
-    def step():
+    ws = cp.attn_bwd_workspace(d)
+
+    def step(workspace):
         for r in wl.ranks:
             cp.ring_pass_kv_bwd(wl.qs[r], wl.shards[r][0], r, wl.ks, wl.vs, wl.kv_segs, True, wl.scale,
-                                wl.o[r], wl.lse[r], d_o[r], delta[r], dq[r], dks, dvs, check=False)
-    ms = time_reps(torch, step, 3, warm=1)
+                                wl.o[r], wl.lse[r], d_o[r], delta[r], dq[r], dks, dvs,
+                                workspace=workspace, check=False)
+    ms = time_reps(torch, lambda: step(ws), 3, warm=1)
+    ms_nows = time_reps(torch, lambda: step(None), 2, warm=1)
     flops = wl.flops * 2.5
     tf = flops / (ms * 1e-3) / 1e12
-    log(f"backward {wl.name}: {ms:.2f} ms for {len(wl.ranks)} ranks, {tf:.1f} useful TFLOP/s")
+    log(f"backward {wl.name}: {ms:.2f} ms for {len(wl.ranks)} ranks, {tf:.1f} useful TFLOP/s "
+        f"(without the workspace: {ms_nows:.2f} ms)")
     return {"metric": "causal-useful backward TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
             "ms_all_ranks": round(ms, 3), "ranks": len(wl.ranks),
             "useful_tflop": round(flops / 1e12, 3), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "flops_per_visible_pair": 10 * d}
+            "flops_per_visible_pair": 10 * d, "workspace_bytes": ws.numel(),
+            "ms_all_ranks_without_workspace": round(ms_nows, 3)}
 
 
 def run_persistent_kv(torch, cp, si, seed=0):

@@ -26,8 +26,8 @@ CP_PASS_KV, CP_PASS_Q = 0, 1
 
 EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitkv",
             "cp_decode_workspace_bytes", "cp_decode_splitkv_ex", "cp_decode_workspace_bytes_ex",
-            "cp_decode_splitkv_noalloc", "cp_attn_bwd_delta", "cp_partial_attn_bwd",
-            "cp_ring_pass_kv_bwd",
+            "cp_decode_splitkv_noalloc", "cp_attn_bwd_delta", "cp_attn_bwd_workspace_bytes",
+            "cp_partial_attn_bwd", "cp_ring_pass_kv_bwd",
             "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant", "cp_status_string",
             "cp_last_error")
 
@@ -98,12 +98,15 @@ def load():
                                    i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), i32, ctypes.POINTER(vp), vp]
     lib.cp_attn_bwd_delta.argtypes = [vp, vp, i32, i64, i32, vp, vp]
+    lib.cp_attn_bwd_workspace_bytes.argtypes = [i32]
+    lib.cp_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.cp_partial_attn_bwd.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, segp, i32, segp, i32,
-                                        i32, f, vp, vp, vp, vp, vp, vp, vp]
+                                        i32, f, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.cp_ring_pass_kv_bwd.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), i64p, ctypes.POINTER(segp),
                                         ctypes.POINTER(ctypes.c_int), i32, i32, i32, i32, i32, f, vp,
-                                        vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+                                        vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                        ctypes.c_size_t, vp]
     lib.cp_select_ring_variant.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_double,
                                            ctypes.c_double, ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]
@@ -492,9 +495,25 @@ def attn_bwd_delta(o, d_o, delta, stream=None, check: bool = True):
                                  _stream(stream)))
 
 
+def attn_bwd_workspace_bytes(d_h: int) -> int:
+    """cp_attn_bwd_workspace_bytes: size of the optional backward workspace for head dim d_h."""
+    return int(load().cp_attn_bwd_workspace_bytes(int(d_h)))
+
+
+def attn_bwd_workspace(d_h: int, device="cuda"):
+    """A device workspace of cp_attn_bwd_workspace_bytes(d_h) bytes (uint8, 256-byte aligned)."""
+    import torch
+    return torch.empty(attn_bwd_workspace_bytes(d_h), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace):
+    return (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+
+
 def partial_attn_bwd(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: float, lse, delta, d_o,
-                     dq, dk, dv, stream=None, check: bool = True):
-    """cp_partial_attn_bwd: adds one ring step's gradient contributions into dq, dk, dv (fp32)."""
+                     dq, dk, dv, workspace=None, stream=None, check: bool = True):
+    """cp_partial_attn_bwd: adds one ring step's gradient contributions into dq, dk, dv (fp32).
+    workspace: optional device tensor (see attn_bwd_workspace) that lets the dK/dV work split."""
     lib = load()
     qa, nq = _segarg(q_segs)
     ka, nk = _segarg(kv_segs)
@@ -510,15 +529,16 @@ def partial_attn_bwd(q, k, v, q_segs, kv_segs, causal: bool, softmax_scale: floa
         _req(dq, "dq", _float_types(), (tq, n_h, d))
         _req(dk, "dk", _float_types(), (tk, n_kv, d))
         _req(dv, "dv", _float_types(), (tk, n_kv, d))
+        _req(workspace, "workspace")
     _check(lib.cp_partial_attn_bwd(_ptr(q), _ptr(k), _ptr(v), tq, tk, n_h, n_kv, d, _dtype_code(q),
                                    qa, nq, ka, nk, int(causal), float(softmax_scale), _ptr(lse),
                                    _ptr(delta), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
-                                   _stream(stream)))
+                                   *_ws(workspace), _stream(stream)))
 
 
 def ring_pass_kv_bwd(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,
-                     softmax_scale: float, o, lse, d_o, delta, dq, dk_shards, dv_shards, stream=None,
-                     check: bool = True):
+                     softmax_scale: float, o, lse, d_o, delta, dq, dk_shards, dv_shards,
+                     workspace=None, stream=None, check: bool = True):
     """cp_ring_pass_kv_bwd for one rank: adds its gradient contributions into dq and into every
     KV shard's dk_shards[s] / dv_shards[s]."""
     lib = load()
@@ -541,6 +561,7 @@ def ring_pass_kv_bwd(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: 
             _req(v_shards[i], f"v_shards[{i}]", (q.dtype,), shp)
             _req(dk_shards[i], f"dk_shards[{i}]", _float_types(), shp)
             _req(dv_shards[i], f"dv_shards[{i}]", _float_types(), shp)
+        _req(workspace, "workspace")
     vp = ctypes.c_void_p
     segp = ctypes.POINTER(CpSegment)
     ks = (vp * N)(*[_ptr(t) for t in k_shards])
@@ -554,4 +575,4 @@ def ring_pass_kv_bwd(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: 
     _check(lib.cp_ring_pass_kv_bwd(_ptr(q), tq, qa, nq, N, rank, ks, vs, tk, kvs, nkv, n_h, n_kv, d,
                                    _dtype_code(q), int(causal), float(softmax_scale), _ptr(o),
                                    _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dq), dks, dvs,
-                                   _stream(stream)))
+                                   *_ws(workspace), _stream(stream)))

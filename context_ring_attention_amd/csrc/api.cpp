@@ -15,7 +15,7 @@
 #include <string>
 #include <vector>
 
-#include "bwd_f32.h"
+#include "attn_bwd.h"
 #include "cp_internal.h"
 #include "cpattn.h"
 
@@ -620,16 +620,23 @@ int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_
 
 // One ring step's backward ([CPEP §6]): gradient contributions of a Q shard against one KV shard,
 // added into dq (the Q shard's) and dk, dv (the KV shard's, summed over the ranks that visit it).
+size_t cp_attn_bwd_workspace_bytes(int d_h) {
+  if (d_h != 64 && d_h != 128) return 0;
+  return (size_t)cpk::kBwdMaxSlots * cpk::bwd_slot_bytes(d_h);
+}
+
 int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq, int64_t tk,
                         int n_h, int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs,
                         int n_q_segs, const cp_segment* kv_segs, int n_kv_segs, int causal,
                         float softmax_scale, const float* lse, const float* delta, const void* d_o,
-                        float* dq, float* dk, float* dv, void* stream) {
+                        float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   const Problem pr{q, k, v, tq, tk, q_segs, n_q_segs, kv_segs, n_kv_segs, dq, const_cast<float*>(lse)};
   int st = validate_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, softmax_scale, 0);
   if (st) return st;
   st = validate_bwd_extra(lse, delta, d_o, dq, dk, dv, in_dtype, n_q_segs, n_kv_segs);
   if (st) return st;
+  if (workspace && !aligned16(workspace)) return fail(CP_E_ARG, "workspace must be 16-byte aligned");
   std::vector<Piece> pieces;
   split_problem(pr, pieces);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -653,7 +660,16 @@ int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq,
     const bool bf16 = in_dtype == CP_BF16;
     plan_bwd(p, pc, bf16 ? cpk::kBwdQRows : cpk::kBwdF32Rows, bf16 ? cpk::kBwdKeys : cpk::kBwdF32Keys);
     if (p.q_tiles == 0 || p.kv_tiles == 0) continue;  // no pair of this piece can be visible
-    st = launch_status(bf16 ? cpk::launch_bwd(p, d_h, s) : cpk::launch_bwd_f32(p, d_h, s),
+    // With a workspace, a launch with fewer key tiles than the split target divides each tile's
+    // query rows into up to kBwdMaxParts parts (as many as the workspace holds).
+    cpk::BwdSplit sp{nullptr, 1};
+    const int64_t tiles = (int64_t)p.kv_tiles * n_kv;
+    if (bf16 && workspace && tiles < cpk::kBwdSplitTarget) {
+      int64_t parts = std::min<int64_t>(cpk::kBwdMaxParts, (cpk::kBwdSplitTarget + tiles - 1) / tiles);
+      parts = std::min<int64_t>(parts, (int64_t)(workspace_bytes / cpk::bwd_slot_bytes(d_h)) / tiles);
+      if (parts > 1) sp = cpk::BwdSplit{static_cast<float*>(workspace), (int32_t)parts};
+    }
+    st = launch_status(bf16 ? cpk::launch_bwd_split(p, sp, d_h, s) : cpk::launch_bwd_f32(p, d_h, s),
                        "cp_partial_attn_bwd");
     if (st) return st;
   }
@@ -669,7 +685,8 @@ int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int
                         const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
                         int d_h, cp_dtype in_dtype, int causal, float softmax_scale, const float* o,
                         const float* lse, const void* d_o, float* delta, float* dq,
-                        float* const* dk_shards, float* const* dv_shards, void* stream) {
+                        float* const* dk_shards, float* const* dv_shards, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (cp_world < 1 || cp_world > cpk::kMaxParts) return fail(CP_E_ARG, "cp_world=%d", cp_world);
   if (rank < 0 || rank >= cp_world) return fail(CP_E_ARG, "rank=%d", rank);
   if (!k_shards || !v_shards || !tk || !kv_segs || !n_kv_segs || !dk_shards || !dv_shards)
@@ -689,13 +706,15 @@ int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int
                             n_kv_segs[s]);
     if (st) return st;
   }
+  if (workspace && !aligned16(workspace)) return fail(CP_E_ARG, "workspace must be 16-byte aligned");
   st = cp_attn_bwd_delta(o, d_o, in_dtype, tq * (int64_t)n_h, d_h, delta, stream);
   if (st) return st;
   for (int t = 0; t < cp_world; ++t) {
     const int s = ((rank - t) % cp_world + cp_world) % cp_world;
     st = cp_partial_attn_bwd(q, k_shards[s], v_shards[s], tq, tk[s], n_h, n_kv, d_h, in_dtype,
                              q_segs, n_q_segs, kv_segs[s], n_kv_segs[s], causal, softmax_scale, lse,
-                             delta, d_o, dq, dk_shards[s], dv_shards[s], stream);
+                             delta, d_o, dq, dk_shards[s], dv_shards[s], workspace,
+                             workspace_bytes, stream);
     if (st) return st;
   }
   return ok();

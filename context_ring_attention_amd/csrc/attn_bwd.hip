@@ -27,6 +27,7 @@
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
 #include <algorithm>
 
+#include "attn_bwd.h"
 #include "device_common.h"
 
 namespace cpk {
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
 
 // ------------------------------------------------------------------------------------ dK, dV
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
   using T = BwdTile<D>;
   constexpr int kBR = 32;                          // query rows per block
   constexpr int kBlockBytes = kBR * T::kRowBytes;
@@ -254,8 +255,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
+  const int tt = blockIdx.x / sp.parts;  // key tile in plan order
+  const int part = blockIdx.x - tt * sp.parts;
   int seg, tile;
-  bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, blockIdx.x, false, seg, tile);
+  bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, tt, false, seg, tile);
   const Seg ks = p.ks[seg];
   const int key_wg = tile * 128;                    // the workgroup's first key in the run
   const int key0 = key_wg + wave * 32;              // this wave's first key
@@ -345,16 +348,38 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     j = jj;
     b = bb;
   };
+  // This workgroup's share: part `part` of the tile's visible blocks, split into equal runs.
+  int n_blocks = 0;
+  for (int jj = 0; jj < p.n_q_segs; ++jj) {
+    const Seg qs = p.qs[jj];
+    if (qs.seq != ks.seq) continue;
+    const int rows = qs.len * p.group, fr = first_row(qs);
+    if (fr < rows) n_blocks += (rows - fr + kBR - 1) / kBR;
+  }
+  const int blk_lo = (int)((int64_t)n_blocks * part / sp.parts);
+  int left = (int)((int64_t)n_blocks * (part + 1) / sp.parts) - blk_lo;
   advance(0, -1);
-  if (j < p.n_q_segs) load_block(p.qs[j], b);
-  while (j < p.n_q_segs) {
+  for (int skip = blk_lo; skip > 0 && j < p.n_q_segs;) {  // move to visible block blk_lo
+    const int here = (p.qs[j].len * p.group - b + kBR - 1) / kBR;  // blocks of run j from b on
+    if (skip < here) {
+      b += skip * kBR;
+      skip = 0;
+    } else {
+      skip -= here;
+      advance(j + 1, -1);
+    }
+  }
+  if (left > 0) load_block(p.qs[j], b);
+  while (left > 0) {
     const Seg qs = p.qs[j];
     const int cur_b = b;
     __syncthreads();
     store_block();
     __syncthreads();
-    advance(j, b + kBR);
-    if (j < p.n_q_segs) load_block(p.qs[j], b);
+    if (--left > 0) {
+      advance(j, b + kBR);
+      load_block(p.qs[j], b);
+    }
 
     // S = Q K^T and dP = dO V^T: lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
     f32x16 s, dpm;
@@ -401,17 +426,70 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
       }
   }
   // accumulators: lane (d = db*32 + col, half) holds keys key0 + 8 (v/4) + 4 half + v % 4
+  if (sp.parts == 1) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
-    if (key >= ks.len) continue;
-    const int64_t base = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + col;
+    for (int v = 0; v < 16; ++v) {
+      const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (key >= ks.len) continue;
+      const int64_t base = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + col;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      p.dk[base + db * 32] = fmaf(p.scale, dk[db][v], p.dk[base + db * 32]);
-      p.dv[base + db * 32] += dv[db][v];
+      for (int db = 0; db < D / 32; ++db) {
+        p.dk[base + db * 32] = fmaf(p.scale, dk[db][v], p.dk[base + db * 32]);
+        p.dv[base + db * 32] += dv[db][v];
+      }
+    }
+  } else {
+    // this part's sums into its workspace slot: [128 keys][D] unscaled dK, then the same for dV
+    // (keys past the run's end hold zeros: their probabilities were masked)
+    float* wk = sp.ws + ((int64_t)(g * p.kv_tiles + tt) * sp.parts + part) * (2 * kBwdKeys * D);
+    float* wv = wk + kBwdKeys * D;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kl = wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        wk[kl * D + db * 32 + col] = dk[db][v];
+        wv[kl * D + db * 32 + col] = dv[db][v];
+      }
     }
   }
+}
+
+// Sum of the parts of a split dK/dV launch, in part order, added into dk (times scale) and dv.
+// A thread owns 4 consecutive d of one key; a workgroup covers 256 / (D / 4) keys of one tile.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const BwdParams p, const BwdSplit sp) {
+  constexpr int kVec = D / 4;
+  constexpr int kKeysPerBlock = 256 / kVec;
+  constexpr int kBlocksPerTile = kBwdKeys / kKeysPerBlock;
+  const int tt = blockIdx.x / kBlocksPerTile;
+  const int kl = (blockIdx.x - tt * kBlocksPerTile) * kKeysPerBlock + (int)threadIdx.x / kVec;
+  const int d4 = (int)threadIdx.x % kVec;
+  const int g = blockIdx.y;
+  int seg, tile;
+  bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, tt, false, seg, tile);
+  const Seg ks = p.ks[seg];
+  const int key = tile * kBwdKeys + kl;
+  if (key >= ks.len) return;
+  constexpr int64_t kPart4 = 2 * kBwdKeys * D / 4;  // float4s per slot
+  constexpr int64_t kV4 = kBwdKeys * D / 4;         // dV's offset in a slot
+  const float4* src = reinterpret_cast<const float4*>(sp.ws) +
+                      (int64_t)(g * p.kv_tiles + tt) * sp.parts * kPart4 + kl * kVec + d4;
+  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+  for (int c = 0; c < sp.parts; ++c) {
+    const float4 a = src[c * kPart4], b = src[c * kPart4 + kV4];
+    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+    sv.x += b.x; sv.y += b.y; sv.z += b.z; sv.w += b.w;
+  }
+  const int64_t o = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + d4 * 4;
+  float4* k4 = reinterpret_cast<float4*>(p.dk + o);
+  float4* v4 = reinterpret_cast<float4*>(p.dv + o);
+  float4 x = *k4, y = *v4;
+  x.x = fmaf(p.scale, sk.x, x.x); x.y = fmaf(p.scale, sk.y, x.y);
+  x.z = fmaf(p.scale, sk.z, x.z); x.w = fmaf(p.scale, sk.w, x.w);
+  y.x += sv.x; y.y += sv.y; y.z += sv.z; y.w += sv.w;
+  *k4 = x;
+  *v4 = y;
 }
 
 // ---------------------------------------------------------------------------------- delta
@@ -436,6 +514,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const float* o, const vo
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d_h, hipStream_t stream) {
+  return launch_bwd_split(p, BwdSplit{nullptr, 1}, d_h, stream);
+}
+
+hipError_t launch_bwd_split(const BwdParams& p, const BwdSplit& sp, int d_h, hipStream_t stream) {
   if (p.q_tiles > 0) {
     const dim3 grid(p.q_tiles, p.n_kv);
     if (d_h == 64)
@@ -446,11 +528,21 @@ hipError_t launch_bwd(const BwdParams& p, int d_h, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.kv_tiles > 0) {
-    const dim3 grid(p.kv_tiles, p.n_kv);
+    const dim3 grid(p.kv_tiles * sp.parts, p.n_kv);
     if (d_h == 64)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p, sp);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p, sp);
+    if (sp.parts > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // kBwdKeys / (256 / (d_h / 4)) workgroups per tile
+      const dim3 rgrid(p.kv_tiles * (kBwdKeys * d_h / 4 / 256), p.n_kv);
+      if (d_h == 64)
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<64>, rgrid, dim3(256), 0, stream, p, sp);
+      else
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<128>, rgrid, dim3(256), 0, stream, p, sp);
+    }
   }
   return hipGetLastError();
 }

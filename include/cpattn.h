@@ -245,6 +245,13 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
 int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_t rows, int d_h,
                       float* delta, void* stream);
 
+/* cp_attn_bwd_workspace_bytes -- size of the optional device workspace of cp_partial_attn_bwd and
+ * cp_ring_pass_kv_bwd for head dimension d_h (0 if d_h is not 64 or 128): 2048 slots of 128 keys x
+ * d_h x 2 fp32 values (256 MiB at d_h = 128). It depends on d_h only, so one allocation serves
+ * every shape. Host-only.
+ * ------------------------------------------------------------------------------------------- */
+size_t cp_attn_bwd_workspace_bytes(int d_h);
+
 /* cp_partial_attn_bwd -- one ring step's backward: the contributions of a Q shard against one KV
  * shard, ADDED into dq, dk and dv (callers zero them first).
  *   q, k, v, tq, tk, n_h, n_kv, d_h, segment tables, causal, softmax_scale: as cp_partial_attn.
@@ -253,6 +260,13 @@ int cp_attn_bwd_delta(const float* o, const void* d_o, cp_dtype do_dtype, int64_
  *   lse: device fp32 [tq, n_h], the final natural-log LSE of each row (-inf: the row saw no key);
  *   delta: device fp32 [tq, n_h] from cp_attn_bwd_delta; d_o: device [tq, n_h, d_h] in in_dtype.
  *   dq: device fp32 [tq, n_h, d_h]; dk, dv: device fp32 [tk, n_kv, d_h]; all 16-byte aligned.
+ *   workspace, workspace_bytes: optional device scratch (16-byte aligned; NULL or 0 bytes: none),
+ *     caller-owned, at most cp_attn_bwd_workspace_bytes(d_h) of it used. With bf16 inputs and
+ *     fewer than 1024 key tiles of 128 keys (over all KV heads) in a launch, the query rows that
+ *     see each key tile are divided into up to 16 equal parts (as many as the workspace holds)
+ *     worked on by separate workgroups; their dK/dV sums go to the workspace and are then added
+ *     into dk and dv in part order. The part count depends only on the shapes and workspace_bytes.
+ *     Calls sharing one workspace must be ordered on one stream.
  * Contributions of one call are summed in a fixed order (deterministic); calls that add into the
  * same buffers must be ordered on one stream.
  * ------------------------------------------------------------------------------------------- */
@@ -260,12 +274,14 @@ int cp_partial_attn_bwd(const void* q, const void* k, const void* v, int64_t tq,
                         int n_h, int n_kv, int d_h, cp_dtype in_dtype, const cp_segment* q_segs,
                         int n_q_segs, const cp_segment* kv_segs, int n_kv_segs, int causal,
                         float softmax_scale, const float* lse, const float* delta, const void* d_o,
-                        float* dq, float* dk, float* dv, void* stream);
+                        float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* cp_ring_pass_kv_bwd -- one rank's ring Pass-KV backward on one device: delta of the rank's rows
  * into `delta` (device fp32 [tq, n_h], caller-owned), then at step t the contributions against KV
  * shard (rank - t) mod cp_world, added into dq and into that shard's dk_shards[s] / dv_shards[s]
  * (device fp32 [tk[s], n_kv, d_h]). o, lse: the rank's final forward output and LSE; d_o in in_dtype.
+ * workspace, workspace_bytes: as cp_partial_attn_bwd (shared by the steps, which run in order).
  * Other arguments as cp_ring_pass_kv. Every step is validated before the first launch.
  * ------------------------------------------------------------------------------------------- */
 int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
@@ -274,7 +290,8 @@ int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int
                         const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
                         int d_h, cp_dtype in_dtype, int causal, float softmax_scale, const float* o,
                         const float* lse, const void* d_o, float* delta, float* dq,
-                        float* const* dk_shards, float* const* dv_shards, void* stream);
+                        float* const* dk_shards, float* const* dv_shards, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * cp_select_ring_variant -- runtime choice between ring Pass-KV and ring Pass-Q ([CPMTI §3

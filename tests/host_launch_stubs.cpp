@@ -4,7 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 
-#include "bwd_f32.h"
+#include "attn_bwd.h"
 #include "cp_internal.h"
 
 namespace cpk {
@@ -21,6 +21,9 @@ hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return unexpec
 hipError_t decode_scratch(void**) { return unexpected("decode_scratch"); }
 hipError_t launch_bwd(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd"); }
 hipError_t launch_bwd_f32(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd_f32"); }
+hipError_t launch_bwd_split(const BwdParams&, const BwdSplit&, int, hipStream_t) {
+  return unexpected("launch_bwd_split");
+}
 hipError_t launch_bwd_delta(const float*, const void*, bool, int64_t, int, float*, hipStream_t) {
   return unexpected("launch_bwd_delta");
 }

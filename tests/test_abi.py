@@ -137,6 +137,46 @@ def test_partial_attn_rejects_bad_arguments_without_launching():
     assert _partial(nq=0) == cp.CP_OK
 
 
+def _partial_bwd(**kw):
+    lib = cp.load()
+    seg, n = cp.segments([(0, 0, 16, 0)])
+    args = dict(q=16, k=16, v=16, tq=16, tk=16, n_h=4, n_kv=1, d_h=64, dt=cp.CP_BF16, qs=seg, nq=n,
+                ks=seg, nk=n, causal=1, scale=0.125, lse=16, delta=16, d_o=16, dq=16, dk=16, dv=16,
+                ws=None, ws_bytes=0)
+    args.update(kw)
+    return lib.cp_partial_attn_bwd(args["q"], args["k"], args["v"], args["tq"], args["tk"],
+                                   args["n_h"], args["n_kv"], args["d_h"], args["dt"], args["qs"],
+                                   args["nq"], args["ks"], args["nk"], args["causal"], args["scale"],
+                                   args["lse"], args["delta"], args["d_o"], args["dq"], args["dk"],
+                                   args["dv"], args["ws"], args["ws_bytes"], None)
+
+
+def test_backward_workspace_size_and_argument_checks():
+    """The backward workspace bound is fixed per head dimension (2048 slots of 128 keys x d_h x
+    dK and dV in fp32); bad backward arguments fail before any launch (fake pointers here)."""
+    assert cp.attn_bwd_workspace_bytes(128) == 2048 * 128 * 128 * 4 * 2
+    assert cp.attn_bwd_workspace_bytes(64) == 2048 * 128 * 64 * 4 * 2
+    assert cp.attn_bwd_workspace_bytes(96) == 0
+    assert _partial_bwd(ws=0x7000008, ws_bytes=1 << 20) == cp.CP_E_ARG   # misaligned workspace
+    assert "workspace" in cp.last_error()
+    assert _partial_bwd(dt=7) == cp.CP_E_ARG
+    assert _partial_bwd(dk=0) == cp.CP_E_ARG
+    assert _partial_bwd(d_o=8) == cp.CP_E_ARG                            # not 16-byte aligned
+    assert _partial_bwd(n_h=6, n_kv=4) == cp.CP_E_SHAPE
+    assert _partial_bwd(nq=0) == cp.CP_OK                                 # nothing to do
+    # the ring driver checks the workspace before its first launch (the delta kernel)
+    lib = cp.load()
+    N = 2
+    a = _ring_arrays(N)
+    vp = ctypes.c_void_p
+    dks = (vp * N)(*[0x7300000 + 0x100000 * i for i in range(N)])
+    st = lib.cp_ring_pass_kv_bwd(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"],
+                                 a["kv_segs"], a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, 0x7000000,
+                                 0x7100000, 0x7200000, 0x7400000, 0x7500000, dks, dks, 0x7600008,
+                                 1 << 20, None)
+    assert st == cp.CP_E_ARG and "workspace" in cp.last_error()
+
+
 def test_merge_and_decode_reject_bad_arguments():
     lib = cp.load()
     vp = ctypes.c_void_p

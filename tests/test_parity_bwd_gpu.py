@@ -44,13 +44,28 @@ def _check(gpu, ref, what, dtype="bf16"):
     assert err <= bound, what
 
 
-def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=None, dtype="bf16"):
+_WS = {}
+
+
+def workspace(d, nbytes=None):
+    """The backward workspace (one per head dimension, shared by the tests), or its first nbytes."""
     from context_ring_attention_amd import binding as cp
+    if d not in _WS:
+        _WS[d] = cp.attn_bwd_workspace(d)
+    return _WS[d] if nbytes is None else _WS[d][:nbytes]
+
+
+def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=None, dtype="bf16",
+            ws=True, ws_bytes=None):
+    """ws: give the calls the backward workspace (so the dK/dV work of small launches is split
+    over several workgroups per key tile), ws_bytes: only that much of it (fewer parts)."""
+    from context_ring_attention_amd import binding as cp
+    wsp = workspace(d, ws_bytes) if ws else None
     ranges = [(i, 0, L) for i, L in enumerate(seqs)]
     scale = scale_of(d)
     std = 1.0 / np.sqrt(d) if dtype == "f32" else 1.0
     log(f"bwd seqs={seqs[:8]}{'...' if len(seqs) > 8 else ''} N={N} n_h={n_h} n_kv={n_kv} d={d} "
-        f"causal={causal} {dtype}")
+        f"causal={causal} {dtype} workspace={'none' if wsp is None else wsp.numel()}")
     sh = product_shards(ranges, N)
     # oracle side: the whole batch in global token order
     T = int(sum(seqs))
@@ -80,7 +95,8 @@ def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=Non
         lse = torch.from_numpy(l32[toks]).cuda()
         delta = torch.empty(len(toks), n_h, device="cuda")
         dq = torch.zeros(len(toks), n_h, d, device="cuda")
-        cp.ring_pass_kv_bwd(q, sh[r].segs, r, ks, vs, kv_segs, causal, scale, o, lse, d_o, delta, dq, dks, dvs)
+        cp.ring_pass_kv_bwd(q, sh[r].segs, r, ks, vs, kv_segs, causal, scale, o, lse, d_o, delta, dq, dks, dvs,
+                            workspace=wsp)
         dqs[r] = dq
         if step_check is not None and r == step_check[0]:
             # one ring step alone against the oracle's partial backward over that shard's keys
@@ -90,7 +106,7 @@ def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=Non
             dk1 = torch.zeros_like(dks[s])
             dv1 = torch.zeros_like(dvs[s])
             cp.partial_attn_bwd(q, ks[s], vs[s], sh[r].segs, sh[s].segs, causal, scale, lse, delta, d_o,
-                                dq1, dk1, dv1)
+                                dq1, dk1, dv1, workspace=wsp)
             torch.cuda.synchronize()
             kt = sh[s].tokens
             p_dq, p_dk, p_dv = oracle.attention_backward(
@@ -109,6 +125,40 @@ def run_bwd(seqs, N, n_h, n_kv, d, seed=0, causal=True, gen=None, step_check=Non
 
 def test_bwd_ring_cp4_two_sequences():
     run_bwd([700, 1300], 4, 16, 1, 128, seed=51, step_check=(1, 2))
+
+
+def test_bwd_without_workspace_and_with_a_small_one():
+    """No workspace: one workgroup per key tile. A workspace of 3 slots per tile: 3 parts."""
+    run_bwd([700, 1300], 4, 16, 1, 128, seed=51, step_check=(1, 2), ws=False)
+    slot = 128 * 128 * 4 * 2
+    run_bwd([1500], 2, 16, 1, 128, seed=64, step_check=(0, 1), ws_bytes=3 * 6 * slot)
+    run_bwd([333, 64], 2, 8, 2, 64, seed=65, ws=False)
+
+
+def test_bwd_split_is_deterministic():
+    """Two calls with the same workspace add bit-identical contributions."""
+    from context_ring_attention_amd import binding as cp
+    seqs, N, n_h, n_kv, d = [1200], 2, 16, 1, 128
+    sh = product_shards([(0, 0, seqs[0])], N)
+    std, scale = 1.0, scale_of(d)
+    r, s = 0, 1
+    q = device_tensor(70, si.TID_Q, sh[r].tokens, (n_h, d), std, "bf16")
+    d_o = device_tensor(70, si.TID_DO, sh[r].tokens, (n_h, d), 1.0, "bf16")
+    k = device_tensor(70, si.TID_K, sh[s].tokens, (n_kv, d), std, "bf16")
+    v = device_tensor(70, si.TID_V, sh[s].tokens, (n_kv, d), std, "bf16")
+    lse = torch.full((len(sh[r].tokens), n_h), 3.0, device="cuda")
+    delta = torch.full((len(sh[r].tokens), n_h), 0.25, device="cuda")
+    outs = []
+    for _ in range(2):
+        dq = torch.zeros(len(sh[r].tokens), n_h, d, device="cuda")
+        dk = torch.zeros(k.shape, device="cuda")
+        dv = torch.zeros(k.shape, device="cuda")
+        cp.partial_attn_bwd(q, k, v, sh[r].segs, sh[s].segs, True, scale, lse, delta, d_o, dq, dk, dv,
+                            workspace=workspace(d))
+        outs.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
 
 
 def test_bwd_gqa_d64():
