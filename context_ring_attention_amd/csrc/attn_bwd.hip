@@ -243,14 +243,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
   using T = BwdTile<D>;
-  constexpr int kBR = 32;                          // query rows per block
+  constexpr int kBR = 64;                          // query rows per block (two MFMA row blocks)
   constexpr int kBlockBytes = kBR * T::kRowBytes;
   constexpr int kLoads = kBR * T::kChunks / 256;   // 16-byte loads per thread per operand
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBlockBytes + 2 * kBR * 4];
-  unsigned char* Qs = smem;
-  unsigned char* Gs = smem + kBlockBytes;
-  float* Ls = reinterpret_cast<float*>(smem + 2 * kBlockBytes);
-  float* Ds = Ls + kBR;
+  // two buffers, each: Q rows, dO rows, base-2 LSEs, deltas; block n is worked on in buffer n % 2
+  // while block n + 1 is staged into the other
+  constexpr int kBufBytes = 2 * kBlockBytes + 2 * kBR * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -319,7 +318,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
       }
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int buf) {
+    unsigned char* Qs = smem + buf * kBufBytes;
+    unsigned char* Gs = Qs + kBlockBytes;
+    float* Ls = reinterpret_cast<float*>(Gs + kBlockBytes);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int idx = i * 256 + tid;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
       *reinterpret_cast<u32x4*>(Qs + o) = qpre[i];
       *reinterpret_cast<u32x4*>(Gs + o) = gpre[i];
     }
-    if (tid < 2 * kBR) Ls[tid] = lpre;  // Ds follows Ls
+    if (tid < 2 * kBR) Ls[tid] = lpre;  // the deltas follow the LSEs
   };
 
   // the query blocks that see this workgroup's keys: runs of its sequence, from the first row
@@ -369,17 +371,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
       advance(j + 1, -1);
     }
   }
-  if (left > 0) load_block(p.qs[j], b);
-  while (left > 0) {
-    const Seg qs = p.qs[j];
-    const int cur_b = b;
-    __syncthreads();
-    store_block();
-    __syncthreads();
-    if (--left > 0) {
+  // (ja, ba): the block in buffer `cur`; (j, b): the block in the prefetch registers
+  int cur = 0, ja = j, ba = b;
+  if (left > 0) {
+    load_block(p.qs[j], b);
+    store_block(0);
+    if (left > 1) {
       advance(j, b + kBR);
       load_block(p.qs[j], b);
     }
+  }
+  while (left > 0) {
+    __syncthreads();  // buffer `cur` is staged; every wave is done with the other one
+    const int jn = j, bn = b;
+    if (left > 1) {
+      store_block(cur ^ 1);
+      if (left > 2) {
+        advance(j, b + kBR);
+        load_block(p.qs[j], b);
+      }
+    }
+    const Seg qs = p.qs[ja];
+    for (int h = 0; h < 2; ++h) {  // the two 32-row halves of the block
+    const int cur_b = ba + 32 * h;
+    const unsigned char* Qs = smem + cur * kBufBytes + 32 * h * T::kRowBytes;
+    const unsigned char* Gs = Qs + kBlockBytes;
+    const float* Ls = reinterpret_cast<const float*>(smem + cur * kBufBytes + 2 * kBlockBytes) + 32 * h;
+    const float* Ds = Ls + kBR;
 
     // S = Q K^T and dP = dO V^T: lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
     f32x16 s, dpm;
@@ -424,6 +442,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ps[t], lds_tr8<D>(Qs, 16 * t, db * 32, lane),
                                                          dk[db], 0, 0, 0);
       }
+    }
+    --left;
+    cur ^= 1;
+    ja = jn;
+    ba = bn;
   }
   // accumulators: lane (d = db*32 + col, half) holds keys key0 + 8 (v/4) + 4 half + v % 4
   if (sp.parts == 1) {

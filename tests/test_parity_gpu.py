@@ -311,6 +311,17 @@ def test_decode_batch_over_64():
     run_decode(lens, 8, 1, 64, 4, seed=3, check_splits=[0, 3])
 
 
+def test_decode_large_grids_with_empty_splits():
+    """Grids of several rounds of one-wave workgroups: 80 requests (above 64, so taken in request
+    order) with 20 heads per KV head (two head blocks), and 40 ranked requests at 256 splits, both
+    with empty splits; D_H 128 and 64, fp32 and bf16 workspaces."""
+    lens = [int(x) for x in np.random.default_rng(16).integers(0, 400, size=80)]
+    run_decode(lens, 40, 2, 128, 32, seed=16, check_splits=[0, 17, 31])
+    lens = [int(x) for x in np.random.default_rng(17).integers(0, 3000, size=40)]
+    run_decode(lens, 16, 1, 128, 256, seed=17, check_splits=[0, 1, 128, 255])
+    run_decode(lens, 16, 1, 64, 256, seed=17, check_splits=[0, 255], ws="bf16")
+
+
 # --------------------------------------------------------------------------- table and split limits
 def test_bf16_full_segment_tables():
     # 32 ragged sequences at CP = 1: each owns 2 chunks, so the Q and KV tables hold 64 runs each,
