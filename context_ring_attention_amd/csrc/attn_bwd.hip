@@ -251,7 +251,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
   constexpr int kBufBytes = 2 * kBlockBytes + 2 * kBR * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the mask branch is too
   const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
   const int tt = blockIdx.x / sp.parts;  // key tile in plan order
@@ -409,10 +410,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Qs, o), kreg[st], s, 0, 0, 0);
       dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Gs, o), vreg[st], dpm, 0, 0, 0);
     }
-    // the block's rows are all visible to all of this wave's keys, or the mask is needed
+    // the block's rows are all visible to all of this wave's keys, or the mask is needed (a
+    // wave-uniform branch around the whole mask)
     const bool masked = !wave_keys_whole ||
                         (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
-    bf16x8 pp[2], ps[2];
+    float pr[16], dl[16];
 #pragma unroll
     for (int vq = 0; vq < 4; ++vq) {
       const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
@@ -421,16 +423,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
       const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int v = 4 * vq + e;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[v], p.scale_log2, -lv[e]));
-        if (masked) {
-          const int rr = cur_b + 8 * vq + 4 * half + e;
-          const bool vis = kcol < ks.len && (!p.causal || qs.pos + rr / p.group >= kpos_lane);
-          pr = vis ? pr : 0.f;
-        }
-        pp[v >> 3][v & 7] = (__bf16)pr;
-        ps[v >> 3][v & 7] = (__bf16)(pr * (dpm[v] - dlv[e]));
+        pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
+        dl[4 * vq + e] = dlv[e];
       }
+    }
+    if (masked) {
+      // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with the
+      // causal mask, the token's position reaches the key's: rr >= row_min
+      const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
+      const bool key_ok = kcol < ks.len;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
+        pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
+      }
+    }
+    bf16x8 pp[2], ps[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      pp[v >> 3][v & 7] = (__bf16)pr[v];
+      ps[v >> 3][v & 7] = (__bf16)(pr[v] * (dpm[v] - dl[v]));
     }
     // dV += P^T dO and dK += dS^T Q: k-step t holds rows 16 t + 8 (e/4) + 4 half + e % 4
 #pragma unroll
