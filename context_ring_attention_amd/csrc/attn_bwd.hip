@@ -92,9 +92,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
   constexpr int kBN = 64;                           // keys per tile
   constexpr int kTileBytes = kBN * T::kRowBytes;
   constexpr int kLoads = kBN * T::kChunks / 512;    // 16-byte loads per thread per operand
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
-  unsigned char* Ks = smem;
-  unsigned char* Vs = smem + kTileBytes;
+  // two buffers of a K and a V tile: tile n is worked on in buffer n % 2 while tile n + 1 is
+  // staged into the other
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -151,7 +151,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
       vpre[i] = *reinterpret_cast<const u32x4*>(Vg + src);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    unsigned char* Ks = smem + buf * 2 * kTileBytes;
+    unsigned char* Vs = Ks + kTileBytes;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int idx = i * 512 + tid;
@@ -174,15 +176,26 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
     kt = tt;
   };
   advance(0, 0);
-  if (j < p.n_kv_segs) load_tile(p.ks[j], kt);
-  while (j < p.n_kv_segs) {
-    const Seg ks = p.ks[j];
-    const int cur_kt = kt;
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
+  // (ja, kta): the tile in buffer `cur`; (j, kt): the tile in the prefetch registers
+  int cur = 0, ja = j, kta = kt;
+  if (j < p.n_kv_segs) {
+    load_tile(p.ks[j], kt);
+    store_tile(0);
     advance(j, kt + kBN);
-    if (j < p.n_kv_segs) load_tile(p.ks[j], kt);  // in flight during this tile's math
+    if (j < p.n_kv_segs) load_tile(p.ks[j], kt);
+  }
+  while (ja < p.n_kv_segs) {
+    __syncthreads();  // buffer `cur` is staged; every wave is done with the other one
+    const int jn = j, ktn = kt;
+    if (j < p.n_kv_segs) {
+      store_tile(cur ^ 1);
+      advance(j, kt + kBN);
+      if (j < p.n_kv_segs) load_tile(p.ks[j], kt);  // in flight during this tile's math
+    }
+    const Seg ks = p.ks[ja];
+    const int cur_kt = kta;
+    const unsigned char* Ks = smem + cur * 2 * kTileBytes;
+    const unsigned char* Vs = Ks + kTileBytes;
 
     // S^T = K Q^T and dP^T = V dO^T: two 32-key halves
     f32x16 s[2], dpt[2];
@@ -203,24 +216,34 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
     const int lim = p.causal ? min(ks.len, qpos - ks.pos + 1) : ks.len;
     // dS^T in bf16 as the B operand of dQ^T += K^T dS^T: k-step t holds keys
     // 16 t + 8 (e / 4) + 4 half + e % 4 == entries 8 (t % 2) + e of score block t / 2
+    float pr[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pr[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
+    if (masked) {  // uniform: one branch around the whole mask
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int ko = cur_kt + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          pr[kb][v] = ko < lim ? pr[kb][v] : 0.f;
+        }
+    }
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
-        if (masked) {
-          const int ko = cur_kt + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          pr = ko < lim ? pr : 0.f;
-        }
-        pb[2 * kb + (v >> 3)][v & 7] = (__bf16)(pr * (dpt[kb][v] - dlt));
-      }
+      for (int v = 0; v < 16; ++v) pb[2 * kb + (v >> 3)][v & 7] = (__bf16)(pr[kb][v] * (dpt[kb][v] - dlt));
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr8<D>(Ks, 16 * t, db * 32, lane), pb[t],
                                                           acc[db], 0, 0, 0);
+    cur ^= 1;
+    ja = jn;
+    kta = ktn;
   }
   if (!live) return;
   // dQ^T accumulator: lane (row, half) holds d = db*32 + 8 (v/4) + 4 half + v % 4
