@@ -19,6 +19,8 @@ import torch
 
 BLOCK = 4096
 TID_Q, TID_K, TID_V, TID_LEN, TID_PO, TID_PL, TID_MISC, TID_DO = 1, 2, 3, 4, 5, 6, 7, 8
+# saved forward activations drawn directly (backward tests at sizes the oracle forward cannot redo)
+TID_SAVED_O, TID_SAVED_LSE = 9, 10
 
 K1 = 1024
 
