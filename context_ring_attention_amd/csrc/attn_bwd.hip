@@ -263,12 +263,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------ dK, dV
+// A workgroup of 8 waves owns 128 keys: waves 0-3 accumulate dV of keys 32 w .. 32 w + 31 and
+// waves 4-7 dK of the same keys, so each wave holds one accumulator set and the kernel fits two
+// waves per SIMD (each SIMD then runs one dV and one dK wave). Both recompute S = Q K^T; the dK
+// waves also form dP = dO V^T. The query rows are walked in blocks of 64 (two 32-row halves)
+// staged in two LDS buffers.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
   using T = BwdTile<D>;
+  constexpr int kThreads = 512;
   constexpr int kBR = 64;                          // query rows per block (two MFMA row blocks)
   constexpr int kBlockBytes = kBR * T::kRowBytes;
-  constexpr int kLoads = kBR * T::kChunks / 256;   // 16-byte loads per thread per operand
+  constexpr int kLoads = kBR * T::kChunks / kThreads;  // 16-byte loads per thread per operand
   // two buffers, each: Q rows, dO rows, base-2 LSEs, deltas; block n is worked on in buffer n % 2
   // while block n + 1 is staged into the other
   constexpr int kBufBytes = 2 * kBlockBytes + 2 * kBR * 4;
@@ -276,6 +282,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the mask branch is too
+  const bool dk_wave = wave >= 4;                              // else a dV wave
+  const int kw = wave & 3;                                     // which 32 keys of the tile
   const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
   const int tt = blockIdx.x / sp.parts;  // key tile in plan order
@@ -283,15 +291,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
   int seg, tile;
   bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, tt, false, seg, tile);
   const Seg ks = p.ks[seg];
-  const int key_wg = tile * 128;                    // the workgroup's first key in the run
-  const int key0 = key_wg + wave * 32;              // this wave's first key
+  const int key_wg = tile * kBwdKeys;               // the workgroup's first key in the run
+  const int key0 = key_wg + kw * 32;                // this wave's first key
   const int kcol = key0 + col;                      // this lane's key (operand column)
   const int kc = min(kcol, ks.len - 1);
   const int kpos_wg_first = ks.pos + key_wg;
   const int kpos_wave_last = ks.pos + min(key0 + 31, ks.len - 1);
   const int kpos_lane = ks.pos + kcol;
   const bool wave_keys_whole = key0 + 32 <= ks.len;
-  // K^T and V^T operands of this lane's key: k-step s covers d = 8 (half * D/16 + s) + e
+  // K^T operand of this lane's key (both roles) and V^T (dK waves): k-step s covers
+  // d = 8 (half * D/16 + s) + e
   bf16x8 kreg[D / 16], vreg[D / 16];
   {
     const int64_t krow = ((int64_t)(ks.loc + kc) * p.n_kv + g) * D + half * (D / 2);
@@ -300,26 +309,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kreg[s] = *reinterpret_cast<const bf16x8*>(kp + s * 8);
-      vreg[s] = *reinterpret_cast<const bf16x8*>(vp + s * 8);
+      vreg[s] = dk_wave ? *reinterpret_cast<const bf16x8*>(vp + s * 8) : bf16x8{};
     }
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];  // dK (dK waves) or dV (dV waves) of the wave's 32 keys
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dk[db][v] = dv[db][v] = 0.f;
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
 
   const __bf16* Qg = static_cast<const __bf16*>(p.q);
   const __bf16* Gg = static_cast<const __bf16*>(p.d_o);
   u32x4 qpre[kLoads], gpre[kLoads];
   float lpre = 0.f;
-  // loads of flattened rows [b, b + 32) of Q run qs (rows past the run repeat its last row and get
-  // LSE = +inf in the base-2 scale, hence P = 0); threads 0..31 load LSEs, 32..63 deltas
+  // loads of flattened rows [b, b + 64) of Q run qs (rows past the run repeat its last row and get
+  // LSE = +inf in the base-2 scale, hence P = 0); threads 0..63 load LSEs, 64..127 deltas
   auto load_block = [&](const Seg& qs, int b) {
     const int rows = qs.len * p.group;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int idx = i * 256 + tid;
+      const int idx = i * kThreads + tid;
       const int row = idx / T::kChunks, ch = idx % T::kChunks;
       const int rr = min(b + row, rows - 1);
       const int64_t src = ((int64_t)(qs.loc + rr / p.group) * p.n_h + g * p.group + rr % p.group) * D + ch * 8;
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
     float* Ls = reinterpret_cast<float*>(Gs + kBlockBytes);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int idx = i * 256 + tid;
+      const int idx = i * kThreads + tid;
       const int row = idx / T::kChunks, ch = idx % T::kChunks;
       const int o = T::off(row, ch * 8);
       *reinterpret_cast<u32x4*>(Qs + o) = qpre[i];
@@ -417,98 +426,105 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p, const 
     }
     const Seg qs = p.qs[ja];
     for (int h = 0; h < 2; ++h) {  // the two 32-row halves of the block
-    const int cur_b = ba + 32 * h;
-    const unsigned char* Qs = smem + cur * kBufBytes + 32 * h * T::kRowBytes;
-    const unsigned char* Gs = Qs + kBlockBytes;
-    const float* Ls = reinterpret_cast<const float*>(smem + cur * kBufBytes + 2 * kBlockBytes) + 32 * h;
-    const float* Ds = Ls + kBR;
+      const int cur_b = ba + 32 * h;
+      const unsigned char* Qs = smem + cur * kBufBytes + 32 * h * T::kRowBytes;
+      const unsigned char* Gs = smem + cur * kBufBytes + kBlockBytes + 32 * h * T::kRowBytes;
+      const float* Ls = reinterpret_cast<const float*>(smem + cur * kBufBytes + 2 * kBlockBytes) + 32 * h;
+      const float* Ds = Ls + kBR;
 
-    // S = Q K^T and dP = dO V^T: lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
-    f32x16 s, dpm;
+      // S = Q K^T (and dP = dO V^T in dK waves): lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
+      f32x16 s, dpm;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = dpm[v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[v] = dpm[v] = 0.f;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const int o = T::off(col, 8 * (half * (D / 16) + st));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Qs, o), kreg[st], s, 0, 0, 0);
-      dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Gs, o), vreg[st], dpm, 0, 0, 0);
-    }
-    // the block's rows are all visible to all of this wave's keys, or the mask is needed (a
-    // wave-uniform branch around the whole mask)
-    const bool masked = !wave_keys_whole ||
-                        (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
-    float pr[16], dl[16];
-#pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-      const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
-      const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * vq + 4 * half);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
-        dl[4 * vq + e] = dlv[e];
+      for (int st = 0; st < D / 16; ++st) {
+        const int o = T::off(col, 8 * (half * (D / 16) + st));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Qs, o), kreg[st], s, 0, 0, 0);
       }
-    }
-    if (masked) {
-      // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with the
-      // causal mask, the token's position reaches the key's: rr >= row_min
-      const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
-      const bool key_ok = kcol < ks.len;
+      if (dk_wave) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
-        pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
+        for (int st = 0; st < D / 16; ++st) {
+          const int o = T::off(col, 8 * (half * (D / 16) + st));
+          dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Gs, o), vreg[st], dpm, 0, 0, 0);
+        }
       }
-    }
-    bf16x8 pp[2], ps[2];
+      // the half's rows are all visible to all of this wave's keys, or the mask is needed (a
+      // wave-uniform branch around the whole mask)
+      const bool masked = !wave_keys_whole ||
+                          (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
+      float pr[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      pp[v >> 3][v & 7] = (__bf16)pr[v];
-      ps[v >> 3][v & 7] = (__bf16)(pr[v] * (dpm[v] - dl[v]));
-    }
-    // dV += P^T dO and dK += dS^T Q: k-step t holds rows 16 t + 8 (e/4) + 4 half + e % 4
+      for (int vq = 0; vq < 4; ++vq) {
+        const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pp[t], lds_tr8<D>(Gs, 16 * t, db * 32, lane),
-                                                         dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ps[t], lds_tr8<D>(Qs, 16 * t, db * 32, lane),
-                                                         dk[db], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+          pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
       }
+      if (masked) {
+        // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with the
+        // causal mask, the token's position reaches the key's: rr >= row_min
+        const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
+        const bool key_ok = kcol < ks.len;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
+          pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
+        }
+      }
+      // the A operand of dV += P^T dO, or of dK += dS^T Q with dS = P (dP - delta); k-step t
+      // holds rows 16 t + 8 (e/4) + 4 half + e % 4
+      bf16x8 pa[2];
+      if (dk_wave) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * vq + 4 * half);
+          const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * vq + e;
+            pa[v >> 3][v & 7] = (__bf16)(pr[v] * (dpm[v] - dlv[e]));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = (__bf16)pr[v];
+      }
+      const unsigned char* Bs = dk_wave ? Qs : Gs;  // Q for dK, dO for dV, read transposed
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], lds_tr8<D>(Bs, 16 * t, db * 32, lane),
+                                                            acc[db], 0, 0, 0);
     }
     --left;
     cur ^= 1;
     ja = jn;
     ba = bn;
   }
-  // accumulators: lane (d = db*32 + col, half) holds keys key0 + 8 (v/4) + 4 half + v % 4
+  // accumulator: lane (d = db*32 + col, half) holds keys key0 + 8 (v/4) + 4 half + v % 4
   if (sp.parts == 1) {
+    float* out = dk_wave ? p.dk : p.dv;
+    const float sc = dk_wave ? p.scale : 1.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
       if (key >= ks.len) continue;
       const int64_t base = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + col;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        p.dk[base + db * 32] = fmaf(p.scale, dk[db][v], p.dk[base + db * 32]);
-        p.dv[base + db * 32] += dv[db][v];
-      }
+      for (int db = 0; db < D / 32; ++db) out[base + db * 32] = fmaf(sc, acc[db][v], out[base + db * 32]);
     }
   } else {
     // this part's sums into its workspace slot: [128 keys][D] unscaled dK, then the same for dV
     // (keys past the run's end hold zeros: their probabilities were masked)
-    float* wk = sp.ws + ((int64_t)(g * p.kv_tiles + tt) * sp.parts + part) * (2 * kBwdKeys * D);
-    float* wv = wk + kBwdKeys * D;
+    float* w = sp.ws + ((int64_t)(g * p.kv_tiles + tt) * sp.parts + part) * (2 * kBwdKeys * D) +
+               (dk_wave ? 0 : kBwdKeys * D);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int kl = wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      const int kl = kw * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        wk[kl * D + db * 32 + col] = dk[db][v];
-        wv[kl * D + db * 32 + col] = dv[db][v];
-      }
+      for (int db = 0; db < D / 32; ++db) w[kl * D + db * 32 + col] = acc[db][v];
     }
   }
 }
@@ -588,9 +604,9 @@ hipError_t launch_bwd_split(const BwdParams& p, const BwdSplit& sp, int d_h, hip
   if (p.kv_tiles > 0) {
     const dim3 grid(p.kv_tiles * sp.parts, p.n_kv);
     if (d_h == 64)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p, sp);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(512), 0, stream, p, sp);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p, sp);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(512), 0, stream, p, sp);
     if (sp.parts > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
