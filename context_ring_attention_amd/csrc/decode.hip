@@ -301,25 +301,29 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
   if (grp == 0 && head_ok) p.ws_lse[prow0 + col] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-// Merge of the S split partials of each (request, head): one workgroup per (request, head),
-// whose partials are S rows of D values (fp32, or bf16 for the half-size workspace) and S fp32
-// LSEs, n_h rows apart. A lane loads 16 bytes of a row (4 fp32 or 8 bf16 values); D / (values per
-// lane) lanes cover a row and the 256 threads form kGroups lane groups that take every
-// kGroups-th split. A lane issues the loads of up to kBatch splits (their LSEs and O slices)
-// before combining any of them; batches are folded into a running max, weight and sum. The groups
-// are then combined through LDS in a fixed order (deterministic).
-template <int D, bool OUT_BF16, bool WS_BF16>
+// Merge of the S split partials of each (request, head): DS workgroups per (request, head), each
+// taking D / DS of the head dimension (DS > 1 for small batches: more workgroups, each with less
+// to read). The partials are S rows of D values (fp32, or bf16 for the half-size workspace) and S
+// fp32 LSEs, n_h rows apart. A lane loads 16 bytes of a row (4 fp32 or 8 bf16 values); D / DS /
+// (values per lane) lanes cover the workgroup's slice and the 256 threads form kGroups lane
+// groups that take every kGroups-th split. A lane issues the loads of up to kBatch splits (their
+// LSEs and O slices) before combining any of them; batches are folded into a running max, weight
+// and sum. The groups are then combined through LDS in a fixed order (deterministic), and every
+// workgroup of a row derives the same weights from the same LSEs.
+template <int D, int DS, bool OUT_BF16, bool WS_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
   constexpr int kVals = WS_BF16 ? 8 : 4;  // values per 16-byte load
-  constexpr int kLanes = D / kVals;
+  constexpr int kLanes = D / DS / kVals;
   constexpr int kGroups = 256 / kLanes;
   constexpr int kBatch = 16;
   __shared__ float red_m[kGroups];
   __shared__ float red_w[kGroups];
   __shared__ float red_o[kGroups][kLanes][kVals];
-  const int r = blockIdx.x;  // b * n_h + head
+  const int r = blockIdx.x / DS;  // b * n_h + head
+  const int piece = blockIdx.x % DS;
   const int grp = threadIdx.x / kLanes;
-  const int cv = threadIdx.x % kLanes;
+  const int cl = threadIdx.x % kLanes;  // 16-byte column within the slice
+  const int cv = piece * kLanes + cl;   // and within the row
   const int64_t row0 = (int64_t)(r / p.n_h) * p.n_splits * p.n_h + r % p.n_h;  // split 0's row
   const float* lse = p.ws_lse + row0;
   const unsigned char* o = static_cast<const unsigned char*>(p.ws_o) + (row0 * D + cv * kVals) * (WS_BF16 ? 2 : 4);
@@ -363,15 +367,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
       }
     }
   }
-  if (cv == 0) red_m[grp] = M;
+  if (cl == 0) red_m[grp] = M;
   __syncthreads();
   float Mt = red_m[0];
 #pragma unroll
   for (int i = 1; i < kGroups; ++i) Mt = fmaxf(Mt, red_m[i]);
   const float a = (M == -INFINITY) ? 0.f : expf(M - Mt);
 #pragma unroll
-  for (int e = 0; e < kVals; ++e) red_o[grp][cv][e] = acc[e] * a;
-  if (cv == 0) red_w[grp] = wsum * a;
+  for (int e = 0; e < kVals; ++e) red_o[grp][cl][e] = acc[e] * a;
+  if (cl == 0) red_w[grp] = wsum * a;
   __syncthreads();
   if (grp != 0) return;
   wsum = 0.f;
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   for (int i = 0; i < kGroups; ++i) {  // fixed order: deterministic
     wsum += red_w[i];
 #pragma unroll
-    for (int e = 0; e < kVals; ++e) acc[e] += red_o[i][cv][e];
+    for (int e = 0; e < kVals; ++e) acc[e] += red_o[i][cl][e];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t orow = (int64_t)r * D + cv * kVals;
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
       *reinterpret_cast<float4*>(out + e0) =
           make_float4(acc[e0] * inv, acc[e0 + 1] * inv, acc[e0 + 2] * inv, acc[e0 + 3] * inv);
   }
-  if (cv == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;
+  if (cv == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;  // piece 0
 }
 
 template <int D, bool WS_BF16>
@@ -409,10 +413,20 @@ void launch_decode_d(const DecodeParams& p, dim3 grid, dim3 mgrid, bool wide, hi
     hipLaunchKernelGGL((decode_split_kernel<D, 4, WS_BF16>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_split_kernel<D, 1, WS_BF16>), grid, dim3(64), 0, stream, p);
-  if (p.out_bf16)
-    hipLaunchKernelGGL((decode_merge_kernel<D, true, WS_BF16>), mgrid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, false, WS_BF16>), mgrid, dim3(256), 0, stream, p);
+  // Fewer (request, head) rows than CUs (e.g. one request's heads): four workgroups per row, each
+  // on a quarter of D. (With more rows, one workgroup per row measured faster.)
+  if (mgrid.x < 256) {
+    const dim3 g4(mgrid.x * 4);
+    if (p.out_bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 4, true, WS_BF16>), g4, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, 4, false, WS_BF16>), g4, dim3(256), 0, stream, p);
+  } else {
+    if (p.out_bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 1, true, WS_BF16>), mgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, 1, false, WS_BF16>), mgrid, dim3(256), 0, stream, p);
+  }
 }
 
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
