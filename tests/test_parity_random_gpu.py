@@ -72,3 +72,31 @@ DECODE_CASES = _draw_decode_cases(10)
 @pytest.mark.parametrize("kw", DECODE_CASES, ids=[f"decode-{i}" for i in range(len(DECODE_CASES))])
 def test_random_decode_config(kw):
     run_decode(**kw)
+
+
+def _draw_backward_cases(n_cases, seed=2028):
+    rng = np.random.default_rng(seed)
+    heads = [(16, 1), (8, 2), (4, 4), (12, 3)]
+    cases = []
+    for i in range(n_cases):
+        n_h, n_kv = heads[rng.integers(len(heads))]
+        n_seq = int(rng.integers(1, 4))
+        cases.append(dict(seqs=[int(x) for x in rng.integers(1, 900, size=n_seq)],
+                          N=int(rng.choice([1, 2, 3, 4])), n_h=n_h, n_kv=n_kv,
+                          d=int(rng.choice([64, 128])), seed=300 + i,
+                          causal=bool(rng.random() < 0.8),
+                          dtype="f32" if rng.random() < 0.2 else "bf16",
+                          ws=bool(rng.random() < 0.7)))
+    return cases
+
+
+BACKWARD_CASES = _draw_backward_cases(10)
+
+
+@pytest.mark.parametrize("kw", BACKWARD_CASES, ids=[f"backward-{i}" for i in range(len(BACKWARD_CASES))])
+def test_random_backward_config(kw):
+    """Every rank's ring backward (dQ per rank, dK/dV per shard over all ranks) against the oracle
+    ("Context Parallelism과 Expert Parallelism", §6), with and without the backward workspace."""
+    from test_parity_bwd_gpu import run_bwd
+    kw = dict(kw)
+    run_bwd(kw.pop("seqs"), kw.pop("N"), kw.pop("n_h"), kw.pop("n_kv"), kw.pop("d"), **kw)
