@@ -74,6 +74,23 @@ __device__ inline bf16x8 lds_tr8(const unsigned char* base, int r0, int col0, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Division by the GQA group size, fixed for a launch, by a multiply and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994): for 0 <= n < 2^31,
+// n / d = (mulhi(m, n) + n) >> l with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (the
+// sum fits in 32 bits). The row -> (token, head) split of every loaded row then costs a few
+// instructions instead of a full integer division.
+struct DivBy {
+  uint32_t m;
+  int l;
+  __device__ explicit DivBy(int d) {
+    l = d <= 1 ? 0 : 32 - __clz(d - 1);
+    m = (uint32_t)(((((uint64_t)1 << l) - (uint64_t)d) << 32) / (uint64_t)d) + 1u;
+  }
+  __device__ int operator()(int n) const {
+    return (int)((__umulhi(m, (uint32_t)n) + (uint32_t)n) >> l);
+  }
+};
+
 // Workgroup tile -> (run, tile index in the run) over a table ordered by `order`, prefix sums in
 // `prefix`; first_tile_last: the first workgroup of a run takes its last tile.
 __device__ inline void bwd_locate(const int32_t* prefix, const int8_t* order, int n_segs, int block,
@@ -324,6 +341,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
   float lpre = 0.f;
   // loads of flattened rows [b, b + 64) of Q run qs (rows past the run repeat its last row and get
   // LSE = +inf in the base-2 scale, hence P = 0); threads 0..63 load LSEs, 64..127 deltas
+  const DivBy by_group(p.group);
   auto load_block = [&](const Seg& qs, int b) {
     const int rows = qs.len * p.group;
 #pragma unroll
@@ -331,7 +349,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
       const int idx = i * kThreads + tid;
       const int row = idx / T::kChunks, ch = idx % T::kChunks;
       const int rr = min(b + row, rows - 1);
-      const int64_t src = ((int64_t)(qs.loc + rr / p.group) * p.n_h + g * p.group + rr % p.group) * D + ch * 8;
+      const int tq = by_group(rr);
+      const int64_t src = ((int64_t)(qs.loc + tq) * p.n_h + g * p.group + (rr - tq * p.group)) * D + ch * 8;
       qpre[i] = *reinterpret_cast<const u32x4*>(Qg + src);
       gpre[i] = *reinterpret_cast<const u32x4*>(Gg + src);
     }
@@ -339,7 +358,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
       const int row = tid & (kBR - 1);
       const int rr = b + row;
       if (rr < rows) {
-        const int64_t qrow = (int64_t)(qs.loc + rr / p.group) * p.n_h + g * p.group + rr % p.group;
+        const int tq = by_group(rr);
+        const int64_t qrow = (int64_t)(qs.loc + tq) * p.n_h + g * p.group + (rr - tq * p.group);
         if (tid < kBR) {
           const float L = p.lse[qrow];
           lpre = L == -INFINITY ? INFINITY : L * kLog2e;
