@@ -323,25 +323,37 @@ def run_persistent_kv(torch, cp, si, seed=0):
         for r in range(N):
             main.wait_stream(side[r])
     ms_kv_streams = time_reps(torch, pass_kv_streams, 5)
+    # Pass-KV keeping the partials: a rank's four steps are independent then and share one launch
+    # (512 workgroups), ranks one after another; merged per rank.
+    pk_o = [[torch.empty_like(o[r]) for _ in range(N)] for r in range(N)]
+    pk_l = [[torch.empty_like(l[r]) for _ in range(N)] for r in range(N)]
+
+    def pass_kv_partials():
+        for r in range(N):
+            cp.ring_pass_kv(qs[r], q_segs[r], r, ks, vs, kv_segs, True, scale, o_kv[r], l_kv[r],
+                            o_parts=pk_o[r], lse_parts=pk_l[r], check=False)
+    ms_kv_partials = time_reps(torch, pass_kv_partials, 5)
     pairs = sum(visible_pairs(q_segs[a], kv_segs[b]) for a in range(N) for b in range(N))
     flops = 4 * d * n_h * pairs
     tf_q, tf_kv = flops / (ms_q * 1e-3) / 1e12, flops / (ms_kv * 1e-3) / 1e12
     # Algorithm 1: condition 2 with the attention rate measured just now (the Pass-KV rate)
     choice, reason = cp.select_ring_variant(T, P, N, n_h, n_kv, d, 2, LINK_BYTES_PER_S, tf_kv * 1e12)
     log(f"persistent KV: pass-q {ms_q:.2f} ms ({tf_q:.1f} TFLOP/s), pass-kv {ms_kv:.2f} ms "
-        f"({tf_kv:.1f} TFLOP/s; ranks on four streams {ms_kv_streams:.2f} ms); selector: {choice} "
-        f"(reason {reason})")
+        f"({tf_kv:.1f} TFLOP/s; ranks on four streams {ms_kv_streams:.2f} ms; keeping partials "
+        f"{ms_kv_partials:.2f} ms); selector: {choice} (reason {reason})")
     out = {"metric": "causal-useful TFLOP/s", "value": round(tf_q, 1), "unit": "TFLOP/s",
            "ms_per_call": round(ms_q, 3), "useful_tflop": round(flops / 1e12, 3),
            "frac_of_bf16_peak": round(tf_q / PEAK_BF16_TFLOPS, 4),
            "pass_kv_same_workload": {"ms": round(ms_kv, 3), "tflops": round(tf_kv, 1),
                                      "ms_ranks_on_four_streams": round(ms_kv_streams, 3),
-                                     "tflops_ranks_on_four_streams": round(flops / (ms_kv_streams * 1e-3) / 1e12, 1)},
+                                     "tflops_ranks_on_four_streams": round(flops / (ms_kv_streams * 1e-3) / 1e12, 1),
+                                     "ms_partials_mode": round(ms_kv_partials, 3),
+                                     "tflops_partials_mode": round(flops / (ms_kv_partials * 1e-3) / 1e12, 1)},
            "selector": {"choice": choice, "reason": reason,
                         "miss_rate": round(T / (T + P), 5), "threshold_2nkv_over_nh": 2 * n_kv / n_h,
                         "attn_flops_per_s_measured": round(tf_kv * 1e12),
                         "link_bytes_per_s_assumed": LINK_BYTES_PER_S,
-                        "faster_measured_here": "pass_q" if ms_q < ms_kv_streams else "pass_kv"}}
+                        "faster_measured_here": "pass_q" if ms_q < min(ms_kv_streams, ms_kv_partials) else "pass_kv"}}
     return out, r0
 
 

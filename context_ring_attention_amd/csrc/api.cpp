@@ -756,14 +756,21 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
   else if (!fold_only)
     st = validate_merge(1, op, lp, rows, d_h, o_out, out_dtype);
   if (st) return st;
+  if (partials) {
+    // The steps write separate partials, so on one device (every shard resident) they are
+    // independent: they go to the GPU together, up to 8 problems per launch. A rank's small Q shard
+    // then fills the chip where one step alone would not.
+    st = partial_attn_problems(steps.data(), cp_world, n_h, n_kv, d_h, in_dtype, causal,
+                               softmax_scale, 0, stream, "cp_ring_pass_kv");
+    if (st) return st;
+    return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
+  }
+  // Running mode: each step folds into (o_acc, lse_acc), so the steps run in ring order.
   for (int t = 0; t < cp_world; ++t) {
-    const int acc = (!partials && t > 0) ? 1 : 0;
-    st = partial_attn_problems(&steps[t], 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale, acc,
-                               stream, "cp_ring_pass_kv");
+    st = partial_attn_problems(&steps[t], 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale,
+                               t > 0 ? 1 : 0, stream, "cp_ring_pass_kv");
     if (st) return st;
   }
-  if (partials)
-    return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
   if (fold_only) return ok();
   return cp_merge_lse(1, op, lp, rows, d_h, o_out, out_dtype, lse_out, stream);
 }

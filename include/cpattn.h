@@ -191,7 +191,8 @@ int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_
  * holds KV shard (rank - t) mod cp_world and runs cp_partial_attn on it.
  *   k_shards, v_shards, tk, kv_segs, n_kv_segs: host arrays indexed by shard id [cp_world].
  *   Mode "partials" (o_parts != NULL): step t writes o_parts[t] / lse_parts[t] (device fp32
- *     [tq*n_h*d_h] / [tq*n_h]); the N partials are then merged with cp_merge_lse into o_out.
+ *     [tq*n_h*d_h] / [tq*n_h]); the N partials are then merged with cp_merge_lse into o_out. The
+ *     steps are independent in this mode, so they share launches (up to 8 per launch).
  *   Mode "running" (o_parts == NULL): steps accumulate into o_acc / lse_acc (device fp32), and
  *     o_out receives the result in out_dtype (o_out may equal o_acc when out_dtype is fp32).
  *   lse_out may be NULL.
