@@ -103,12 +103,13 @@ __device__ inline void bwd_locate(const int32_t* prefix, const int8_t* order, in
 }
 
 // ------------------------------------------------------------------------------------------ dQ
+constexpr int kDqThreads = 2 * kBwdQRows;  // a wave per 32 query rows
 template <int D>
-__global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(const BwdParams p) {
   using T = BwdTile<D>;
   constexpr int kBN = 64;                           // keys per tile
   constexpr int kTileBytes = kBN * T::kRowBytes;
-  constexpr int kLoads = kBN * T::kChunks / 512;    // 16-byte loads per thread per operand
+  constexpr int kLoads = kBN * T::kChunks / kDqThreads;  // 16-byte loads per thread per operand
   // two buffers of a K and a V tile: tile n is worked on in buffer n % 2 while tile n + 1 is
   // staged into the other
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
@@ -120,8 +121,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
   bwd_locate(p.q_prefix, p.q_order, p.n_q_segs, blockIdx.x, true, seg, tile);
   const Seg qs = p.qs[seg];
   const int rows = qs.len * p.group;
-  const int row0 = tile * 256;
-  const int row_last = min(row0 + 256, rows) - 1;
+  const int row0 = tile * kBwdQRows;
+  const int row_last = min(row0 + kBwdQRows, rows) - 1;
   const int qpos_lo = qs.pos + row0 / p.group;
   const int qpos_hi = qs.pos + row_last / p.group;
 
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
   auto load_tile = [&](const Seg& ks, int kt) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int idx = i * 512 + tid;
+      const int idx = i * kDqThreads + tid;
       const int row = idx / T::kChunks, ch = idx % T::kChunks;
       const int key = min(kt + row, ks.len - 1);
       const int64_t src = ((int64_t)(ks.loc + key) * p.n_kv + g) * D + ch * 8;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const BwdParams p) {
     unsigned char* Vs = Ks + kTileBytes;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int idx = i * 512 + tid;
+      const int idx = i * kDqThreads + tid;
       const int row = idx / T::kChunks, ch = idx % T::kChunks;
       const int o = T::off(row, ch * 8);
       *reinterpret_cast<u32x4*>(Ks + o) = kpre[i];
@@ -615,9 +616,9 @@ hipError_t launch_bwd_split(const BwdParams& p, const BwdSplit& sp, int d_h, hip
   if (p.q_tiles > 0) {
     const dim3 grid(p.q_tiles, p.n_kv);
     if (d_h == 64)
-      hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(kDqThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(kDqThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
