@@ -286,10 +286,11 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(const BwdParams p
 
 // ------------------------------------------------------------------------------------ dK, dV
 // A workgroup of 8 waves owns 128 keys: waves 0-3 accumulate dV of keys 32 w .. 32 w + 31 and
-// waves 4-7 dK of the same keys, so each wave holds one accumulator set and the kernel fits two
-// waves per SIMD (each SIMD then runs one dV and one dK wave). Both recompute S = Q K^T; the dK
-// waves also form dP = dO V^T. The query rows are walked in blocks of 64 (two 32-row halves)
-// staged in two LDS buffers.
+// waves 4-7 dK of the same keys, so each wave holds one accumulator set and one operand set and
+// the kernel fits two waves per SIMD (each SIMD then runs one dV and one dK wave). Per 32-row half,
+// a dV wave forms S = Q K^T and P, hands P to its dK wave through LDS, and adds P^T dO; the dK wave
+// forms dP = dO V^T meanwhile, then dS = P (dP - delta) and adds dS^T Q: 16 MFMAs each. The query
+// rows are walked in blocks of 64 (two 32-row halves) staged in two LDS buffers.
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
   using T = BwdTile<D>;
@@ -300,7 +301,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
   // two buffers, each: Q rows, dO rows, base-2 LSEs, deltas; block n is worked on in buffer n % 2
   // while block n + 1 is staged into the other
   constexpr int kBufBytes = 2 * kBlockBytes + 2 * kBR * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes];
+  // P handed from each dV wave to the dK wave of the same keys: per 32-row half and key group,
+  // 16 fp32 values per lane stored [value quad][lane] (consecutive lanes, consecutive 16 bytes)
+  constexpr int kPBytes = 4 * 4 * 64 * 16;  // 4 key groups x 4 quads x 64 lanes x 16 B
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes + 2 * kPBytes];
+  float4* pex = reinterpret_cast<float4*>(smem + 2 * kBufBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the mask branch is too
@@ -321,18 +326,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
   const int kpos_wave_last = ks.pos + min(key0 + 31, ks.len - 1);
   const int kpos_lane = ks.pos + kcol;
   const bool wave_keys_whole = key0 + 32 <= ks.len;
-  // K^T operand of this lane's key (both roles) and V^T (dK waves): k-step s covers
-  // d = 8 (half * D/16 + s) + e
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // The B operand of this lane's key: K^T in dV waves (S = Q K^T), V^T in dK waves
+  // (dP = dO V^T); k-step s covers d = 8 (half * D/16 + s) + e
+  bf16x8 breg[D / 16];
   {
     const int64_t krow = ((int64_t)(ks.loc + kc) * p.n_kv + g) * D + half * (D / 2);
-    const __bf16* kp = static_cast<const __bf16*>(p.k) + krow;
-    const __bf16* vp = static_cast<const __bf16*>(p.v) + krow;
+    const __bf16* bp = static_cast<const __bf16*>(dk_wave ? p.v : p.k) + krow;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kreg[s] = *reinterpret_cast<const bf16x8*>(kp + s * 8);
-      vreg[s] = dk_wave ? *reinterpret_cast<const bf16x8*>(vp + s * 8) : bf16x8{};
-    }
+    for (int s = 0; s < D / 16; ++s) breg[s] = *reinterpret_cast<const bf16x8*>(bp + s * 8);
   }
   f32x16 acc[D / 32];  // dK (dK waves) or dV (dV waves) of the wave's 32 keys
 #pragma unroll
@@ -456,64 +457,68 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
       const unsigned char* Gs = smem + cur * kBufBytes + kBlockBytes + 32 * h * T::kRowBytes;
       const float* Ls = reinterpret_cast<const float*>(smem + cur * kBufBytes + 2 * kBlockBytes) + 32 * h;
       const float* Ds = Ls + kBR;
+      float4* ph = pex + (h * 4 + kw) * 4 * 64;  // this half's P of this key group
 
-      // S = Q K^T (and dP = dO V^T in dK waves): lane (key, half) holds rows 8 (v/4) + 4 half + v % 4
-      f32x16 s, dpm;
+      // S = Q K^T (dV waves) or dP = dO V^T (dK waves): lane (key, half) holds rows
+      // 8 (v/4) + 4 half + v % 4
+      f32x16 s;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = dpm[v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[v] = 0.f;
+      const unsigned char* As = dk_wave ? Gs : Qs;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
         const int o = T::off(col, 8 * (half * (D / 16) + st));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Qs, o), kreg[st], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(As, o), breg[st], s, 0, 0, 0);
       }
-      if (dk_wave) {
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          const int o = T::off(col, 8 * (half * (D / 16) + st));
-          dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(Gs, o), vreg[st], dpm, 0, 0, 0);
-        }
-      }
-      // the half's rows are all visible to all of this wave's keys, or the mask is needed (a
-      // wave-uniform branch around the whole mask)
-      const bool masked = !wave_keys_whole ||
-                          (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
-      float pr[16];
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
-      }
-      if (masked) {
-        // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with the
-        // causal mask, the token's position reaches the key's: rr >= row_min
-        const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
-        const bool key_ok = kcol < ks.len;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
-          pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
-        }
-      }
-      // the A operand of dV += P^T dO, or of dK += dS^T Q with dS = P (dP - delta); k-step t
-      // holds rows 16 t + 8 (e/4) + 4 half + e % 4
+      // the A operand of dV += P^T dO (dV waves) or of dK += dS^T Q with dS = P (dP - delta)
+      // (dK waves); k-step t holds rows 16 t + 8 (e/4) + 4 half + e % 4
       bf16x8 pa[2];
-      if (dk_wave) {
+      if (!dk_wave) {
+        // the half's rows are all visible to all of this wave's keys, or the mask is needed (a
+        // wave-uniform branch around the whole mask)
+        const bool masked = !wave_keys_whole ||
+                            (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
+        float pr[16];
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq) {
+          const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
+        }
+        if (masked) {
+          // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with
+          // the causal mask, the token's position reaches the key's: rr >= row_min
+          const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
+          const bool key_ok = kcol < ks.len;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
+            pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          ph[vq * 64 + lane] = make_float4(pr[4 * vq], pr[4 * vq + 1], pr[4 * vq + 2], pr[4 * vq + 3]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = (__bf16)pr[v];
+      }
+      __syncthreads();  // the dV waves' P of this half is in LDS
+      if (dk_wave) {
+        // the same lane of the paired dV wave holds P of the same (row, key) entries
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const float4 p4 = ph[vq * 64 + lane];
           const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * vq + 4 * half);
+          const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
           const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * vq + e;
-            pa[v >> 3][v & 7] = (__bf16)(pr[v] * (dpm[v] - dlv[e]));
+            pa[v >> 3][v & 7] = (__bf16)(pv[e] * (s[v] - dlv[e]));
           }
         }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = (__bf16)pr[v];
       }
       const unsigned char* Bs = dk_wave ? Qs : Gs;  // Q for dK, dO for dV, read transposed
 #pragma unroll
