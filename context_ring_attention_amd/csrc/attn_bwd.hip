@@ -108,21 +108,25 @@ __device__ inline void bwd_locate(const int32_t* prefix, const int8_t* order, in
 
 // ------------------------------------------------------------------------------------------ dQ
 constexpr int kDqThreads = 2 * kBwdQRows;  // a wave per 32 query rows
+constexpr int kDqKeys = 64;                // keys per K/V tile
+// LDS of a dQ workgroup: two buffers of a K and a V tile; tile n is worked on in buffer n % 2
+// while tile n + 1 is staged into the other
 template <int D>
-__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(const BwdParams p) {
+constexpr int dq_lds_bytes() { return 4 * kDqKeys * BwdTile<D>::kRowBytes; }
+
+// The dQ workgroup `bx` of the plan (heaviest row tile first).
+template <int D>
+__device__ __forceinline__ void bwd_dq_tile(const BwdParams& p, int bx, unsigned char* smem) {
   using T = BwdTile<D>;
-  constexpr int kBN = 64;                           // keys per tile
+  constexpr int kBN = kDqKeys;
   constexpr int kTileBytes = kBN * T::kRowBytes;
   constexpr int kLoads = kBN * T::kChunks / kDqThreads;  // 16-byte loads per thread per operand
-  // two buffers of a K and a V tile: tile n is worked on in buffer n % 2 while tile n + 1 is
-  // staged into the other
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
   int seg, tile;
-  bwd_locate(p.q_prefix, p.q_order, p.n_q_segs, blockIdx.x, true, seg, tile);
+  bwd_locate(p.q_prefix, p.q_order, p.n_q_segs, bx, true, seg, tile);
   const Seg qs = p.qs[seg];
   const int rows = qs.len * p.group;
   const int row0 = tile * kBwdQRows;
@@ -291,20 +295,27 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(const BwdParams p
 // a dV wave forms S = Q K^T and P, hands P to its dK wave through LDS, and adds P^T dO; the dK wave
 // forms dP = dO V^T meanwhile, then dS = P (dP - delta) and adds dS^T Q: 16 MFMAs each. The query
 // rows are walked in blocks of 64 (two 32-row halves) staged in two LDS buffers.
+constexpr int kDkdvRows = 64;  // query rows per block (two MFMA row blocks)
+// LDS of a dK/dV workgroup: two buffers, each holding a block's Q rows, dO rows, base-2 LSEs and
+// deltas (block n is worked on in buffer n % 2 while block n + 1 is staged into the other), then
+// the P handed from each dV wave to the dK wave of the same keys: per 32-row half and key group,
+// 16 fp32 values per lane stored [value quad][lane] (consecutive lanes, consecutive 16 bytes)
 template <int D>
-__global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const BwdSplit sp) {
+constexpr int dkdv_buf_bytes() { return 2 * kDkdvRows * BwdTile<D>::kRowBytes + 2 * kDkdvRows * 4; }
+constexpr int kDkdvPBytes = 4 * 4 * 64 * 16;  // 4 key groups x 4 quads x 64 lanes x 16 B
+template <int D>
+constexpr int dkdv_lds_bytes() { return 2 * dkdv_buf_bytes<D>() + 2 * kDkdvPBytes; }
+
+// The dK/dV workgroup `bx` of the plan: part bx % parts of key tile bx / parts.
+template <int D>
+__device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit& sp, int bx,
+                                              unsigned char* smem) {
   using T = BwdTile<D>;
   constexpr int kThreads = 512;
-  constexpr int kBR = 64;                          // query rows per block (two MFMA row blocks)
+  constexpr int kBR = kDkdvRows;
   constexpr int kBlockBytes = kBR * T::kRowBytes;
   constexpr int kLoads = kBR * T::kChunks / kThreads;  // 16-byte loads per thread per operand
-  // two buffers, each: Q rows, dO rows, base-2 LSEs, deltas; block n is worked on in buffer n % 2
-  // while block n + 1 is staged into the other
-  constexpr int kBufBytes = 2 * kBlockBytes + 2 * kBR * 4;
-  // P handed from each dV wave to the dK wave of the same keys: per 32-row half and key group,
-  // 16 fp32 values per lane stored [value quad][lane] (consecutive lanes, consecutive 16 bytes)
-  constexpr int kPBytes = 4 * 4 * 64 * 16;  // 4 key groups x 4 quads x 64 lanes x 16 B
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes + 2 * kPBytes];
+  constexpr int kBufBytes = dkdv_buf_bytes<D>();
   float4* pex = reinterpret_cast<float4*>(smem + 2 * kBufBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -313,8 +324,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
   const int kw = wave & 3;                                     // which 32 keys of the tile
   const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
-  const int tt = blockIdx.x / sp.parts;  // key tile in plan order
-  const int part = blockIdx.x - tt * sp.parts;
+  const int tt = bx / sp.parts;  // key tile in plan order
+  const int part = bx - tt * sp.parts;
   int seg, tile;
   bwd_locate(p.kv_prefix, p.kv_order, p.n_kv_segs, tt, false, seg, tile);
   const Seg ks = p.ks[seg];
@@ -489,14 +500,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
         }
         if (masked) {
           // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with
-          // the causal mask, the token's position reaches the key's: rr >= row_min
+          // the causal mask, the token's position reaches the key's: rr >= row_min. Entry v is
+          // row cur_b + 4 half + c(v) with c(v) = 8 (v/4) + v % 4, visible iff c(v) >= thr.
           const int row_min = p.causal ? min(max(kpos_lane - qs.pos, 0), qs.len) * p.group : 0;
-          const bool key_ok = kcol < ks.len;
+          const int thr = kcol < ks.len ? row_min - cur_b - 4 * half : INT_MAX;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rr = cur_b + 8 * (v >> 2) + 4 * half + (v & 3);
-            pr[v] = key_ok && rr >= row_min ? pr[v] : 0.f;
-          }
+          for (int v = 0; v < 16; ++v) pr[v] = 8 * (v >> 2) + (v & 3) >= thr ? pr[v] : 0.f;
         }
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq)
@@ -557,6 +566,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p, const 
       for (int db = 0; db < D / 32; ++db) w[kl * D + db * 32 + col] = acc[db][v];
     }
   }
+}
+
+// One launch per ring step for both halves of the backward: workgroups [0, n_dkdv) are the
+// dK/dV workgroups of the plan, the rest its dQ workgroups. The two kinds have the same shape
+// (8 waves, at most 256 VGPRs, one workgroup per CU), so the CUs that finish the longer dK/dV
+// workgroups take the dQ ones and neither half leaves a tail of idle CUs of its own.
+template <int D>
+__global__ __launch_bounds__(512, 2) void bwd_kernel(const BwdParams p, const BwdSplit sp, int n_dkdv) {
+  constexpr int kLds = dq_lds_bytes<D>() > dkdv_lds_bytes<D>() ? dq_lds_bytes<D>() : dkdv_lds_bytes<D>();
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  const int bx = blockIdx.x;
+  if (bx < n_dkdv)
+    bwd_dkdv_tile<D>(p, sp, bx, smem);
+  else
+    bwd_dq_tile<D>(p, bx - n_dkdv, smem);
 }
 
 // Sum of the parts of a split dK/dV launch, in part order, added into dk (times scale) and dv.
@@ -622,24 +646,19 @@ hipError_t launch_bwd(const BwdParams& p, int d_h, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_split(const BwdParams& p, const BwdSplit& sp, int d_h, hipStream_t stream) {
-  if (p.q_tiles > 0) {
-    const dim3 grid(p.q_tiles, p.n_kv);
+  static_assert(kDqThreads == 512, "dQ and dK/dV workgroups share one launch shape");
+  const int n_dkdv = p.kv_tiles * sp.parts;
+  if (p.q_tiles + n_dkdv > 0) {
+    const dim3 grid(n_dkdv + p.q_tiles, p.n_kv);
     if (d_h == 64)
-      hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(kDqThreads), 0, stream, p);
+      hipLaunchKernelGGL(bwd_kernel<64>, grid, dim3(512), 0, stream, p, sp, n_dkdv);
     else
-      hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(kDqThreads), 0, stream, p);
+      hipLaunchKernelGGL(bwd_kernel<128>, grid, dim3(512), 0, stream, p, sp, n_dkdv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.kv_tiles > 0) {
-    const dim3 grid(p.kv_tiles * sp.parts, p.n_kv);
-    if (d_h == 64)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(512), 0, stream, p, sp);
-    else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(512), 0, stream, p, sp);
     if (sp.parts > 1) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
       // kBwdKeys / (256 / (d_h / 4)) workgroups per tile
       const dim3 rgrid(p.kv_tiles * (kBwdKeys * d_h / 4 / 256), p.n_kv);
       if (d_h == 64)
