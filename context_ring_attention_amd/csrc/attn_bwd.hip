@@ -450,17 +450,10 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
       advance(j, b + kBR);
       load_block(p.qs[j], b);
     }
+    __syncthreads();  // block 0 is staged
   }
   while (left > 0) {
-    __syncthreads();  // buffer `cur` is staged; every wave is done with the other one
     const int jn = j, bn = b;
-    if (left > 1) {
-      store_block(cur ^ 1);
-      if (left > 2) {
-        advance(j, b + kBR);
-        load_block(p.qs[j], b);
-      }
-    }
     const Seg qs = p.qs[ja];
     for (int h = 0; h < 2; ++h) {  // the two 32-row halves of the block
       const int cur_b = ba + 32 * h;
@@ -514,6 +507,15 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
         for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = (__bf16)pr[v];
       }
       __syncthreads();  // the dV waves' P of this half is in LDS
+      if (h == 0 && left > 1) {
+        // Every wave is past its reads of the previous block (the barrier above), so the next
+        // block goes into the other buffer now; the second half's barrier makes it visible.
+        store_block(cur ^ 1);
+        if (left > 2) {
+          advance(j, b + kBR);
+          load_block(p.qs[j], b);
+        }
+      }
       if (dk_wave) {
         // the same lane of the paired dV wave holds P of the same (row, key) entries
 #pragma unroll
