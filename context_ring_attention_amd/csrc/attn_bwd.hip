@@ -44,6 +44,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// s_waitcnt immediate for "vmcnt(0)" on gfx9-family targets (expcnt and lgkmcnt left at max).
+constexpr int kBwdWaitVmcnt0 = 0x0F70;
+
 // An LDS tile of rows of D bf16 values, row-major without padding; the 16-byte chunk c of row r
 // sits in slot c ^ sw(r). Row reads (16 lanes, 16 consecutive rows, one chunk) and transposing
 // reads (a half-wave: 4 consecutive rows x 4 consecutive chunks) then touch 16 distinct slots.
@@ -346,6 +349,9 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) breg[s] = *reinterpret_cast<const bf16x8*>(bp + s * 8);
   }
+  // Retire these loads here: otherwise the wait analysis keeps them pending at the block loop's
+  // header and makes every block's first products wait for the next block's prefetch as well.
+  __builtin_amdgcn_s_waitcnt(kBwdWaitVmcnt0);
   f32x16 acc[D / 32];  // dK (dK waves) or dV (dV waves) of the wave's 32 keys
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
