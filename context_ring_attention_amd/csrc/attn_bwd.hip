@@ -9,23 +9,25 @@
 // accumulated into the caller's fp32 buffers. Summed over the ring steps (dQ) and over the ranks
 // that visit a KV shard (dK, dV) this is the exact gradient of the whole attention.
 //
-// Two kernels (three when the dK/dV work is split), none needing atomics:
-//  - bwd_dq_kernel: a workgroup of 8 waves owns 256 query rows (GQA rows = token * G + head, as
-//    in the forward) and walks the KV tiles they see. S^T = K Q^T and dP^T = V dO^T run on
-//    v_mfma_f32_32x32x16_bf16 with K and V rows from LDS and Q^T, dO^T in registers, so each lane
-//    holds 16 keys of one row: P, dS and the row's LSE and delta are per-lane values. dS^T,
-//    rounded to bf16, is then directly the B operand of dQ^T += K^T dS^T, whose K^T operand comes
-//    from the same K tile through the transposing ds_read_b64_tr_b16.
-//  - bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys; waves 0-3 accumulate dV of 32 keys
-//    each and waves 4-7 dK of the same keys (K, and V for dK, kept in registers as B operands),
-//    walking the blocks of 64 query rows that see them. S = Q K^T and dP = dO V^T leave each lane
-//    with 16 rows of one key, which is the A operand layout of dV += P^T dO and dK += dS^T Q; dO
-//    and Q come from LDS through the transposing read. With a workspace, the query blocks of a
-//    key tile may be divided into parts worked on by separate workgroups, whose sums
-//    bwd_dkdv_reduce_kernel then adds in part order.
+// One launch per ring step (two when the dK/dV work is split), nothing needing atomics. Its first
+// workgroups are dK/dV workgroups, the rest dQ workgroups (same shape: 8 waves, one per CU):
+//  - dQ: a workgroup owns 256 query rows (GQA rows = token * G + head, as in the forward) and
+//    walks the KV tiles they see. S^T = K Q^T and dP^T = V dO^T run on v_mfma_f32_32x32x16_bf16
+//    with K and V rows from LDS and Q^T, dO^T in registers, so each lane holds 16 keys of one row:
+//    P, dS and the row's LSE and delta are per-lane values. dS^T, rounded to bf16, is then
+//    directly the B operand of dQ^T += K^T dS^T, whose K^T operand comes from the same K tile
+//    through the transposing ds_read_b64_tr_b16.
+//  - dK/dV: a workgroup owns 128 keys; waves 0-3 accumulate dV of 32 keys each and waves 4-7 dK
+//    of the same keys (K, or V for dK, kept in registers as B operands), walking the blocks of 64
+//    query rows that see them in 32-row halves. A dV wave forms S = Q K^T and P and hands P to
+//    its dK wave through LDS; the dK wave forms dP = dO V^T and then dS. Each lane holds 16 rows
+//    of one key, the A operand layout of dV += P^T dO and dK += dS^T Q; dO and Q come from LDS
+//    through the transposing read. With a workspace, the query blocks of a key tile may be
+//    divided into parts worked on by separate workgroups, whose sums bwd_dkdv_reduce_kernel
+//    then adds in part order.
 // Both stage their shared operands through two LDS buffers (the next tile or block prefetched
-// into registers and stored into the other buffer, one barrier per tile), and swizzle 16-byte
-// chunks so that row reads and transposing reads of one tile are conflict-free.
+// into registers and stored into the other buffer once no wave reads it any more), and swizzle
+// 16-byte chunks so that row reads and transposing reads of one tile are conflict-free.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
