@@ -43,6 +43,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -296,20 +297,21 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdParams& p, int bx, unsigned
 // ------------------------------------------------------------------------------------ dK, dV
 // A workgroup of 8 waves owns 128 keys: waves 0-3 accumulate dV of keys 32 w .. 32 w + 31 and
 // waves 4-7 dK of the same keys, so each wave holds one accumulator set and one operand set and
-// the kernel fits two waves per SIMD (each SIMD then runs one dV and one dK wave). Per 32-row half,
-// a dV wave forms S = Q K^T and P, hands P to its dK wave through LDS, and adds P^T dO; the dK wave
-// forms dP = dO V^T meanwhile, then dS = P (dP - delta) and adds dS^T Q: 16 MFMAs each. The query
-// rows are walked in blocks of 64 (two 32-row halves) staged in two LDS buffers.
+// the kernel fits two waves per SIMD (each SIMD then runs one dV and one dK wave). Per block of 64
+// query rows, a dV wave forms S = Q K^T and P, hands P to its dK wave through LDS, and adds P^T dO;
+// the dK wave forms dP = dO V^T meanwhile, then dS = P (dP - delta) and adds dS^T Q: 32 MFMAs each,
+// one barrier per block. The blocks are staged in three LDS buffers.
 constexpr int kDkdvRows = 64;  // query rows per block (two MFMA row blocks)
-// LDS of a dK/dV workgroup: two buffers, each holding a block's Q rows, dO rows, base-2 LSEs and
-// deltas (block n is worked on in buffer n % 2 while block n + 1 is staged into the other), then
-// the P handed from each dV wave to the dK wave of the same keys: per 32-row half and key group,
-// 16 fp32 values per lane stored [value quad][lane] (consecutive lanes, consecutive 16 bytes)
+// LDS of a dK/dV workgroup: three buffers, each holding a block's Q rows, dO rows, base-2 LSEs and
+// deltas (block n is worked on in buffer n % 3 while block n + 1 is staged into the next one),
+// then the P handed from each dV wave to the dK wave of the same keys, in fp16, in two slots
+// (block n uses slot n % 2): per slot, 32-row half and key group, 16 values per lane stored as
+// [8-value chunk][lane] (consecutive lanes, consecutive 16 bytes)
 template <int D>
 constexpr int dkdv_buf_bytes() { return 2 * kDkdvRows * BwdTile<D>::kRowBytes + 2 * kDkdvRows * 4; }
-constexpr int kDkdvPBytes = 4 * 4 * 64 * 16;  // 4 key groups x 4 quads x 64 lanes x 16 B
+constexpr int kDkdvPBytes = 2 * 2 * 4 * 2 * 64 * 16;  // slots x halves x key groups x chunks x lanes x 16 B
 template <int D>
-constexpr int dkdv_lds_bytes() { return 2 * dkdv_buf_bytes<D>() + 2 * kDkdvPBytes; }
+constexpr int dkdv_lds_bytes() { return 3 * dkdv_buf_bytes<D>() + kDkdvPBytes; }
 
 // The dK/dV workgroup `bx` of the plan: part bx % parts of key tile bx / parts.
 template <int D>
@@ -321,7 +323,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
   constexpr int kBlockBytes = kBR * T::kRowBytes;
   constexpr int kLoads = kBR * T::kChunks / kThreads;  // 16-byte loads per thread per operand
   constexpr int kBufBytes = dkdv_buf_bytes<D>();
-  float4* pex = reinterpret_cast<float4*>(smem + 2 * kBufBytes);
+  uint4* pex = reinterpret_cast<uint4*>(smem + 3 * kBufBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the mask branch is too
@@ -449,8 +451,14 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
       advance(j + 1, -1);
     }
   }
-  // (ja, ba): the block in buffer `cur`; (j, b): the block in the prefetch registers
-  int cur = 0, ja = j, ba = b;
+  // (ja, ba): the block in buffer `cur`; (j, b): the block in the prefetch registers. A block is
+  // worked on in two phases split by one barrier. Phase 1: the next block is stored into the next
+  // buffer (whose last reads, two blocks back, preceded the previous barrier); a dV wave forms
+  // S = Q K^T of both halves and the masked P, and hands P over; a dK wave forms dP = dO V^T of
+  // both halves. Phase 2: the dK wave forms dS = P (dP - delta) from the handed-over P; the dV wave
+  // adds P^T dO and the dK wave dS^T Q. The P slot of block n is written again by block n + 2,
+  // after the barrier of block n + 1.
+  int cur = 0, slot = 0, ja = j, ba = b;
   if (left > 0) {
     load_block(p.qs[j], b);
     store_block(0);
@@ -462,42 +470,53 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
   }
   while (left > 0) {
     const int jn = j, bn = b;
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    if (left > 1) {
+      store_block(nxt);
+      if (left > 2) {
+        advance(j, b + kBR);
+        load_block(p.qs[j], b);
+      }
+    }
     const Seg qs = p.qs[ja];
-    for (int h = 0; h < 2; ++h) {  // the two 32-row halves of the block
-      const int cur_b = ba + 32 * h;
-      const unsigned char* Qs = smem + cur * kBufBytes + 32 * h * T::kRowBytes;
-      const unsigned char* Gs = smem + cur * kBufBytes + kBlockBytes + 32 * h * T::kRowBytes;
-      const float* Ls = reinterpret_cast<const float*>(smem + cur * kBufBytes + 2 * kBlockBytes) + 32 * h;
-      const float* Ds = Ls + kBR;
-      float4* ph = pex + (h * 4 + kw) * 4 * 64;  // this half's P of this key group
-
-      // S = Q K^T (dV waves) or dP = dO V^T (dK waves): lane (key, half) holds rows
-      // 8 (v/4) + 4 half + v % 4
-      f32x16 s;
+    const unsigned char* Qb = smem + cur * kBufBytes;
+    const unsigned char* Gb = Qb + kBlockBytes;
+    const float* Lb = reinterpret_cast<const float*>(Gb + kBlockBytes);
+    // S = Q K^T (dV waves) or dP = dO V^T (dK waves) of both 32-row halves: lane (key, half)
+    // holds rows 32 h + 8 (v/4) + 4 half + v % 4
+    f32x16 s[2];
+    // the A operands of dV += P^T dO (dV waves) or of dK += dS^T Q with dS = P (dP - delta)
+    // (dK waves); for half h, k-step t holds rows 32 h + 16 t + 8 (e/4) + 4 half + e % 4
+    bf16x8 pa[2][2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.f;
-      const unsigned char* As = dk_wave ? Gs : Qs;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
+      const unsigned char* As = (dk_wave ? Gb : Qb) + 32 * h * T::kRowBytes;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
         const int o = T::off(col, 8 * (half * (D / 16) + st));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(As, o), breg[st], s, 0, 0, 0);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(As, o), breg[st], s[h], 0, 0, 0);
       }
-      // the A operand of dV += P^T dO (dV waves) or of dK += dS^T Q with dS = P (dP - delta)
-      // (dK waves); k-step t holds rows 16 t + 8 (e/4) + 4 half + e % 4
-      bf16x8 pa[2];
-      if (!dk_wave) {
+    }
+    if (!dk_wave) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cur_b = ba + 32 * h;
+        const float* Ls = Lb + 32 * h;
+        uint4* ph = pex + ((slot * 2 + h) * 4 + kw) * 2 * 64;  // this half's P of this key group
         // the half's rows are all visible to all of this wave's keys, or the mask is needed (a
         // wave-uniform branch around the whole mask)
         const bool masked = !wave_keys_whole ||
                             (p.causal && qs.pos + cur_b / p.group < kpos_wave_last);
-        float pr[16];
+        f32x16 pr;
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq) {
           const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * vq + 4 * half);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * vq + e], p.scale_log2, -lv[e]));
+            pr[4 * vq + e] = __builtin_amdgcn_exp2f(fmaf(s[h][4 * vq + e], p.scale_log2, -lv[e]));
         }
         if (masked) {
           // key kcol is visible to row rr (token rr / G of the run) iff kcol < len and, with
@@ -508,47 +527,47 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdParams& p, const BwdSplit
 #pragma unroll
           for (int v = 0; v < 16; ++v) pr[v] = 8 * (v >> 2) + (v & 3) >= thr ? pr[v] : 0.f;
         }
+        ph[lane] = __builtin_bit_cast(uint4, __builtin_convertvector(
+            __builtin_shufflevector(pr, pr, 0, 1, 2, 3, 4, 5, 6, 7), f16x8));
+        ph[64 + lane] = __builtin_bit_cast(uint4, __builtin_convertvector(
+            __builtin_shufflevector(pr, pr, 8, 9, 10, 11, 12, 13, 14, 15), f16x8));
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq)
-          ph[vq * 64 + lane] = make_float4(pr[4 * vq], pr[4 * vq + 1], pr[4 * vq + 2], pr[4 * vq + 3]);
+        for (int v = 0; v < 16; ++v) pa[h][v >> 3][v & 7] = (__bf16)pr[v];
+      }
+    }
+    __syncthreads();  // the dV waves' P of the block is in LDS; the next block is staged
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pa[v >> 3][v & 7] = (__bf16)pr[v];
-      }
-      __syncthreads();  // the dV waves' P of this half is in LDS
-      if (h == 0 && left > 1) {
-        // Every wave is past its reads of the previous block (the barrier above), so the next
-        // block goes into the other buffer now; the second half's barrier makes it visible.
-        store_block(cur ^ 1);
-        if (left > 2) {
-          advance(j, b + kBR);
-          load_block(p.qs[j], b);
-        }
-      }
+    for (int h = 0; h < 2; ++h) {
       if (dk_wave) {
         // the same lane of the paired dV wave holds P of the same (row, key) entries
+        const float* Ds = Lb + kBR + 32 * h;
+        const uint4* ph = pex + ((slot * 2 + h) * 4 + kw) * 2 * 64;
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq) {
-          const float4 p4 = ph[vq * 64 + lane];
-          const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * vq + 4 * half);
-          const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
-          const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int c = 0; c < 2; ++c) {
+          const f16x8 p8 = __builtin_bit_cast(f16x8, ph[c * 64 + lane]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * vq + e;
-            pa[v >> 3][v & 7] = (__bf16)(pv[e] * (s[v] - dlv[e]));
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * (2 * c + q2) + 4 * half);
+            const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 8 * c + 4 * q2 + e;
+              pa[h][v >> 3][v & 7] = (__bf16)((float)p8[4 * q2 + e] * (s[h][v] - dlv[e]));
+            }
           }
         }
       }
-      const unsigned char* Bs = dk_wave ? Qs : Gs;  // Q for dK, dO for dV, read transposed
+      const unsigned char* Bs = (dk_wave ? Qb : Gb) + 32 * h * T::kRowBytes;  // Q for dK, dO for dV
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], lds_tr8<D>(Bs, 16 * t, db * 32, lane),
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][t], lds_tr8<D>(Bs, 16 * t, db * 32, lane),
                                                             acc[db], 0, 0, 0);
     }
     --left;
-    cur ^= 1;
+    cur = nxt;
+    slot ^= 1;
     ja = jn;
     ba = bn;
   }
