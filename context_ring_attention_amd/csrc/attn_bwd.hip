@@ -19,15 +19,16 @@
 //    through the transposing ds_read_b64_tr_b16.
 //  - dK/dV: a workgroup owns 128 keys; waves 0-3 accumulate dV of 32 keys each and waves 4-7 dK
 //    of the same keys (K, or V for dK, kept in registers as B operands), walking the blocks of 64
-//    query rows that see them in 32-row halves. A dV wave forms S = Q K^T and P and hands P to
-//    its dK wave through LDS; the dK wave forms dP = dO V^T and then dS. Each lane holds 16 rows
+//    query rows that see them. A dV wave forms S = Q K^T and P and hands P (fp16) to its dK wave
+//    through LDS; the dK wave forms dP = dO V^T and then dS. Each lane holds 16 rows
 //    of one key, the A operand layout of dV += P^T dO and dK += dS^T Q; dO and Q come from LDS
 //    through the transposing read. With a workspace, the query blocks of a key tile may be
 //    divided into parts worked on by separate workgroups, whose sums bwd_dkdv_reduce_kernel
 //    then adds in part order.
-// Both stage their shared operands through two LDS buffers (the next tile or block prefetched
-// into registers and stored into the other buffer once no wave reads it any more), and swizzle
-// 16-byte chunks so that row reads and transposing reads of one tile are conflict-free.
+// Both stage their shared operands through LDS buffers (the next tile or block prefetched into
+// registers and stored into a buffer no wave reads any more: two buffers for dQ, three for dK/dV,
+// whose workgroups pass one barrier per 64-row block), and swizzle 16-byte chunks so that row
+// reads and transposing reads of one tile are conflict-free.
 //
 // Pages cited: [CPEP] "Context Parallelism과 Expert Parallelism: Long Context와 MoE를 쪼개는 두
 // 축"; [CPMTI] "Context Parallelism for Scalable Million-Token Inference" (paper review).
