@@ -90,7 +90,7 @@ def _draw_backward_cases(n_cases, seed=2028):
     return cases
 
 
-BACKWARD_CASES = _draw_backward_cases(10)
+BACKWARD_CASES = _draw_backward_cases(20)
 
 
 @pytest.mark.parametrize("kw", BACKWARD_CASES, ids=[f"backward-{i}" for i in range(len(BACKWARD_CASES))])
