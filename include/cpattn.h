@@ -257,7 +257,7 @@ size_t cp_attn_bwd_workspace_bytes(int d_h);
  * shard, ADDED into dq, dk and dv (callers zero them first).
  *   q, k, v, tq, tk, n_h, n_kv, d_h, segment tables, causal, softmax_scale: as cp_partial_attn.
  *     bf16 inputs run the products on bf16 MFMA with fp32 accumulation (probabilities and score
- *     gradients rounded to bf16 as operands; the score gradient of dK and dV is formed from the
+ *     gradients rounded to bf16 as operands; the score gradient that dK sums is formed from the
  *     probability rounded to fp16); fp32 inputs run in fp32 arithmetic throughout.
  *   lse: device fp32 [tq, n_h], the final natural-log LSE of each row (-inf: the row saw no key);
  *   delta: device fp32 [tq, n_h] from cp_attn_bwd_delta; d_o: device [tq, n_h, d_h] in in_dtype.
