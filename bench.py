@@ -305,16 +305,21 @@ def run_persistent_kv(torch, cp, si, seed=0):
     r0["o"], r0["lse"] = o[0][idx].cpu().numpy(), l[0][idx].cpu().numpy()
     o_kv = [torch.empty_like(x) for x in o]
     l_kv = [torch.empty_like(x) for x in l]
+    # Each rank's running ring as a rank of its own GPU would run it, ranks one after another. A
+    # step's 2048-token Q shard alone makes 128 workgroups of 256 rows; with the ring workspace the
+    # step is split over its keys (256 workgroups and an in-place merge).
+    ws_kv = [cp.ring_workspace(x.shape[0], n_h, d) for x in qs]
 
-    def pass_kv():
+    def pass_kv(use_ws=True):
         for r in range(N):
             cp.ring_pass_kv(qs[r], q_segs[r], r, ks, vs, kv_segs, True, scale, o_kv[r], l_kv[r],
-                            o_acc=o_kv[r], lse_acc=l_kv[r], check=False)
+                            o_acc=o_kv[r], lse_acc=l_kv[r], workspace=ws_kv[r] if use_ws else None,
+                            check=False)
     ms_kv = time_reps(torch, pass_kv, 5)
-    # The same four rings, each rank on a stream of its own (default priority), as four ranks that
-    # share one GPU: a rank's launch (a 2048-token Q shard, 128 workgroups) leaves half the CUs
-    # idle, which the other ranks' launches fill. This is the like-for-like comparison with the
-    # Pass-Q figure above, which batches a ring step's four ranks into one launch.
+    ms_kv_nows = time_reps(torch, lambda: pass_kv(False), 5)
+    # The same four rings (without the workspace), each rank on a stream of its own (default
+    # priority), as four ranks that share one GPU: the other ranks' launches fill the CUs that one
+    # rank's 128 workgroups leave idle.
     side = [torch.cuda.Stream() for _ in range(N)]
 
     def pass_kv_streams():
@@ -342,12 +347,14 @@ def run_persistent_kv(torch, cp, si, seed=0):
     # Algorithm 1: condition 2 with the attention rate measured just now (the Pass-KV rate)
     choice, reason = cp.select_ring_variant(T, P, N, n_h, n_kv, d, 2, LINK_BYTES_PER_S, tf_kv * 1e12)
     log(f"persistent KV: pass-q {ms_q:.2f} ms ({tf_q:.1f} TFLOP/s), pass-kv {ms_kv:.2f} ms "
-        f"({tf_kv:.1f} TFLOP/s; ranks on four streams {ms_kv_streams:.2f} ms; keeping partials "
-        f"{ms_kv_partials:.2f} ms); selector: {choice} (reason {reason})")
+        f"({tf_kv:.1f} TFLOP/s; without the ring workspace {ms_kv_nows:.2f} ms; ranks on four streams "
+        f"{ms_kv_streams:.2f} ms; keeping partials {ms_kv_partials:.2f} ms); selector: {choice} "
+        f"(reason {reason})")
     out = {"metric": "causal-useful TFLOP/s", "value": round(tf_q, 1), "unit": "TFLOP/s",
            "ms_per_call": round(ms_q, 3), "useful_tflop": round(flops / 1e12, 3),
            "frac_of_bf16_peak": round(tf_q / PEAK_BF16_TFLOPS, 4),
            "pass_kv_same_workload": {"ms": round(ms_kv, 3), "tflops": round(tf_kv, 1),
+                                     "ms_without_ring_workspace": round(ms_kv_nows, 3),
                                      "ms_ranks_on_four_streams": round(ms_kv_streams, 3),
                                      "tflops_ranks_on_four_streams": round(flops / (ms_kv_streams * 1e-3) / 1e12, 1),
                                      "ms_partials_mode": round(ms_kv_partials, 3),
@@ -356,7 +363,7 @@ def run_persistent_kv(torch, cp, si, seed=0):
                         "miss_rate": round(T / (T + P), 5), "threshold_2nkv_over_nh": 2 * n_kv / n_h,
                         "attn_flops_per_s_measured": round(tf_kv * 1e12),
                         "link_bytes_per_s_assumed": LINK_BYTES_PER_S,
-                        "faster_measured_here": "pass_q" if ms_q < min(ms_kv_streams, ms_kv_partials) else "pass_kv"}}
+                        "faster_measured_here": "pass_q" if ms_q < min(ms_kv, ms_kv_streams, ms_kv_partials) else "pass_kv"}}
     return out, r0
 
 

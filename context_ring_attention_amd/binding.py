@@ -28,8 +28,8 @@ EXPORTED = ("cp_shard_map", "cp_partial_attn", "cp_merge_lse", "cp_decode_splitk
             "cp_decode_workspace_bytes", "cp_decode_splitkv_ex", "cp_decode_workspace_bytes_ex",
             "cp_decode_splitkv_noalloc", "cp_attn_bwd_delta", "cp_attn_bwd_workspace_bytes",
             "cp_partial_attn_bwd", "cp_ring_pass_kv_bwd",
-            "cp_ring_pass_kv", "cp_ring_pass_q", "cp_select_ring_variant", "cp_status_string",
-            "cp_last_error")
+            "cp_ring_pass_kv", "cp_ring_workspace_bytes", "cp_ring_pass_q", "cp_select_ring_variant",
+            "cp_status_string", "cp_last_error")
 
 
 class CpSegment(ctypes.Structure):
@@ -91,7 +91,9 @@ def load():
     lib.cp_ring_pass_kv.argtypes = [vp, i64, segp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
                                     i32, i32, i32, f, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
-                                    vp, i32, vp, vp]
+                                    vp, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.cp_ring_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.cp_ring_workspace_bytes.restype = ctypes.c_size_t
     lib.cp_ring_pass_q.argtypes = [i32, ctypes.POINTER(vp), i64p, ctypes.POINTER(segp),
                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    i64p, ctypes.POINTER(segp), ctypes.POINTER(ctypes.c_int), i32, i32,
@@ -374,10 +376,23 @@ def decode_splitkv_noalloc(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int
                                          _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
 
 
+def ring_workspace_bytes(tq: int, n_h: int, d_h: int) -> int:
+    """cp_ring_workspace_bytes: size of the optional running-mode workspace of ring_pass_kv."""
+    return int(load().cp_ring_workspace_bytes(int(tq), int(n_h), int(d_h)))
+
+
+def ring_workspace(tq: int, n_h: int, d_h: int, device="cuda"):
+    """A device workspace of cp_ring_workspace_bytes(tq, n_h, d_h) bytes (uint8)."""
+    import torch
+    return torch.empty(ring_workspace_bytes(tq, n_h, d_h), dtype=torch.uint8, device=device)
+
+
 def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,
                  softmax_scale: float, o_out, lse_out=None, o_parts=None, lse_parts=None,
-                 o_acc=None, lse_acc=None, stream=None, check: bool = True):
-    """cp_ring_pass_kv for one rank. k_shards/v_shards/kv_segs: per shard id."""
+                 o_acc=None, lse_acc=None, workspace=None, stream=None, check: bool = True):
+    """cp_ring_pass_kv for one rank. k_shards/v_shards/kv_segs: per shard id. workspace: optional
+    device tensor (see ring_workspace) that lets a running-mode step of a small Q shard split over
+    its keys."""
     lib = load()
     N = len(k_shards)
     qa, nq = _segarg(q_segs)
@@ -412,10 +427,11 @@ def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool
     nkv = (ctypes.c_int * N)(*[n for _, n in seg_objs])
     op = (vp * N)(*[_ptr(t) for t in o_parts]) if o_parts is not None else None
     lp = (vp * N)(*[_ptr(t) for t in lse_parts]) if lse_parts is not None else None
+    wp, wb = _ws(workspace)
     _check(lib.cp_ring_pass_kv(_ptr(q), tq, qa, nq, N, rank, ks, vs, tk, kvs, nkv, n_h, n_kv, d,
                                _dtype_code(q), int(causal), float(softmax_scale), op, lp,
                                _ptr(o_acc), _ptr(lse_acc), _ptr(o_out), _dtype_code(o_out),
-                               _ptr(lse_out), _stream(stream)))
+                               _ptr(lse_out), wp, wb, _stream(stream)))
 
 
 def select_ring_variant(new_tokens: int, cached_tokens: int, cp_world: int, n_h: int, n_kv: int,

@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -39,6 +40,7 @@ int ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int64_t kI32Max = 0x7fffffff;
 
@@ -722,13 +724,60 @@ int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int
 
 // Ring Pass-KV ([CPMTI §3 "核心公式"; Fig. 3]): the rank keeps its Q shard; at step t it holds the
 // KV shard that started on rank (rank - t) mod N.
+size_t cp_ring_workspace_bytes(int64_t tq, int n_h, int d_h) {
+  if (tq < 0 || n_h <= 0 || d_h <= 0) return 0;
+  const size_t rows = (size_t)tq * (size_t)n_h;
+  return round_up256(rows * (size_t)d_h * sizeof(float)) + round_up256(rows * sizeof(float));
+}
+
+namespace {
+
+// CUs of the current device (looked up once per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  cache[dev] = cus;
+  return cus;
+}
+
+// The keys of one ring step divided in two: every KV run longer than 128 keys is cut after a
+// whole number of 64-key tiles near its middle (first parts in `a`, second parts in `b`); shorter
+// runs stay whole in `a`.
+void halve_kv_runs(const cp_segment* runs, int n, std::vector<cp_segment>& a, std::vector<cp_segment>& b) {
+  for (int j = 0; j < n; ++j) {
+    const cp_segment& r = runs[j];
+    if (r.len <= 128) {
+      a.push_back(r);
+      continue;
+    }
+    const int64_t first = (r.len / 2 + 63) / 64 * 64;
+    cp_segment x = r, y = r;
+    x.len = first;
+    y.pos_start = r.pos_start + first;
+    y.local_start = r.local_start + first;
+    y.len = r.len - first;
+    a.push_back(x);
+    b.push_back(y);
+  }
+}
+
+}  // namespace
+
 int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
                     int cp_world, int rank, const void* const* k_shards,
                     const void* const* v_shards, const int64_t* tk,
                     const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
                     int d_h, cp_dtype in_dtype, int causal, float softmax_scale,
                     float* const* o_parts, float* const* lse_parts, float* o_acc, float* lse_acc,
-                    void* o_out, cp_dtype out_dtype, float* lse_out, void* stream) {
+                    void* o_out, cp_dtype out_dtype, float* lse_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (cp_world < 1 || cp_world > cpk::kMaxParts) return fail(CP_E_ARG, "cp_world=%d", cp_world);
   if (rank < 0 || rank >= cp_world) return fail(CP_E_ARG, "rank=%d", rank);
   if (!k_shards || !v_shards || !tk || !kv_segs || !n_kv_segs) return fail(CP_E_ARG, "shard arrays are NULL");
@@ -736,6 +785,7 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
   if (partials && !lse_parts) return fail(CP_E_ARG, "lse_parts is NULL");
   if (!partials && (!o_acc || !lse_acc)) return fail(CP_E_ARG, "running mode needs o_acc and lse_acc");
   if (!o_out) return fail(CP_E_ARG, "o_out is NULL");
+  if (workspace && !aligned16(workspace)) return fail(CP_E_ARG, "workspace must be 16-byte aligned");
   // Step t holds KV shard (rank - t) mod N. Every step and the final merge are validated before
   // the first launch, so a failing call launches nothing.
   std::vector<Problem> steps(cp_world);
@@ -765,10 +815,55 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
     if (st) return st;
     return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
   }
-  // Running mode: each step folds into (o_acc, lse_acc), so the steps run in ring order.
+  // Running mode: each step folds into (o_acc, lse_acc), so the steps run in ring order. A step
+  // whose Q tiles cannot fill the CUs is split over its keys when a workspace is given: both
+  // halves go to the GPU in one launch, each folding into an empty or the running result, and
+  // the workspace half is then merged into (o_acc, lse_acc) in place.
+  const bool ws_fits = workspace && workspace_bytes >= cp_ring_workspace_bytes(tq, n_h, d_h);
+  int64_t q_tiles = 0;
+  for (int i = 0; i < n_q_segs; ++i)
+    q_tiles += (q_segs[i].len * (n_h / n_kv) + cpk::kTileRowsBf16 - 1) / cpk::kTileRowsBf16;
+  q_tiles *= n_kv;
+  const int cus = ws_fits && in_dtype == CP_BF16 ? device_cus() : 0;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_fits ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                                     round_up256((size_t)rows * d_h * sizeof(float)))
+                          : nullptr;
+  bool filled = false;  // (o_acc, lse_acc) holds a result (or the empty one)
   for (int t = 0; t < cp_world; ++t) {
-    st = partial_attn_problems(&steps[t], 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale,
-                               t > 0 ? 1 : 0, stream, "cp_ring_pass_kv");
+    const Problem& pr = steps[t];
+    int64_t keys = 0;
+    for (int j = 0; j < pr.n_kv_segs; ++j) keys += pr.kv_segs[j].len;
+    if (!(cus > 0 && q_tiles < cus && keys >= 4096)) {
+      st = partial_attn_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale,
+                                 filled ? 1 : 0, stream, "cp_ring_pass_kv");
+      if (st) return st;
+      filled = true;
+      continue;
+    }
+    std::vector<cp_segment> ka, kb;
+    halve_kv_runs(pr.kv_segs, pr.n_kv_segs, ka, kb);
+    Problem two[2] = {pr, pr};
+    two[0].kv_segs = ka.data();
+    two[0].n_kv_segs = (int)ka.size();
+    two[1].kv_segs = kb.data();
+    two[1].n_kv_segs = (int)kb.size();
+    two[1].o = ws_o;
+    two[1].lse = ws_lse;
+    if (!filled) {
+      st = launch_status(cpk::launch_fill_running(o_acc, lse_acc, rows, d_h, hs), "cp_ring_pass_kv");
+      if (st) return st;
+      filled = true;
+    }
+    st = launch_status(cpk::launch_fill_running(ws_o, ws_lse, rows, d_h, hs), "cp_ring_pass_kv");
+    if (st) return st;
+    st = partial_attn_problems(two, 2, n_h, n_kv, d_h, in_dtype, causal, softmax_scale, 1, stream,
+                               "cp_ring_pass_kv");
+    if (st) return st;
+    const float* mo[2] = {o_acc, ws_o};
+    const float* ml[2] = {lse_acc, ws_lse};
+    st = cp_merge_lse(2, mo, ml, rows, d_h, o_acc, CP_F32, lse_acc, stream);
     if (st) return st;
   }
   if (fold_only) return ok();

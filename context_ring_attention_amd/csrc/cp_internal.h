@@ -126,6 +126,8 @@ constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup
 hipError_t launch_attn_f32(const AttnParams& p, int d_h, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int d_h, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+// O = 0, LSE = -inf for `rows` rows of d_h fp32 values (o 16-byte aligned).
+hipError_t launch_fill_running(float* o, float* lse, int64_t rows, int d_h, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream);
 // Device address of the allocation-free decode workspace (CP_DECODE_NOALLOC_MAX_BYTES) on the
 // current device; looked up once per device, then cached.

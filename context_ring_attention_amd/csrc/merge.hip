@@ -86,6 +86,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   }
 }
 
+// An empty running result: O = 0 and LSE = -inf for `rows` rows of d_h values (folding a partial
+// into it leaves the partial unchanged). A kernel rather than a memset, so that the fill can sit
+// in a captured graph.
+__global__ __launch_bounds__(256) void fill_running_kernel(float4* o, int64_t n4, float* lse, int64_t rows) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows; i += (int64_t)gridDim.x * 256)
+    lse[i] = -INFINITY;
+}
+
+hipError_t launch_fill_running(float* o, float* lse, int64_t rows, int d_h, hipStream_t stream) {
+  const int64_t n4 = rows * d_h / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_running_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0,
+                     stream, reinterpret_cast<float4*>(o), n4, lse, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int rows_per_block = 256 / (p.d_h / 4);
   // at most 64K workgroups (256 per CU); larger merges loop inside the kernel

@@ -185,6 +185,11 @@ int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_
                               float softmax_scale, cp_dtype ws_dtype, void* o_out,
                               cp_dtype out_dtype, float* lse_out, void* stream);
 
+/* cp_ring_workspace_bytes -- size of the optional workspace of cp_ring_pass_kv's running mode for
+ * a Q shard of tq tokens: one partial (O, then LSE at the next 256-byte boundary) of tq * n_h rows
+ * of d_h fp32 values. Host-only. */
+size_t cp_ring_workspace_bytes(int64_t tq, int n_h, int d_h);
+
 /* ---------------------------------------------------------------------------------------------
  * cp_ring_pass_kv -- one rank's ring Pass-KV on one device ([CPMTI §3 "核心公式": each rank keeps
  * its Q shard while KV shards travel the ring for N-1 rounds; §3 Fig. 3). At step t the rank
@@ -196,6 +201,14 @@ int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_
  *   Mode "running" (o_parts == NULL): steps accumulate into o_acc / lse_acc (device fp32), and
  *     o_out receives the result in out_dtype (o_out may equal o_acc when out_dtype is fp32).
  *   lse_out may be NULL.
+ *   workspace, workspace_bytes: optional device scratch for the running mode (NULL or too small:
+ *     none; 16-byte aligned; ignored in the partials mode), caller-owned, at most
+ *     cp_ring_workspace_bytes(tq, n_h, d_h) of it used. With bf16 inputs, a step whose Q shard
+ *     has fewer 256-row tiles (over all KV heads) than the device has CUs, and at least 4096 keys,
+ *     is split over its keys: the first half of every KV run folds into (o_acc, lse_acc), the
+ *     second half goes to the workspace in the same launch, and the two are then merged in
+ *     place. The split depends only on the shapes, the device's CU count and workspace_bytes.
+ *     Calls sharing one workspace must be ordered on one stream.
  * ------------------------------------------------------------------------------------------- */
 int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
                     int cp_world, int rank, const void* const* k_shards,
@@ -203,7 +216,8 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
                     const cp_segment* const* kv_segs, const int* n_kv_segs, int n_h, int n_kv,
                     int d_h, cp_dtype in_dtype, int causal, float softmax_scale,
                     float* const* o_parts, float* const* lse_parts, float* o_acc, float* lse_acc,
-                    void* o_out, cp_dtype out_dtype, float* lse_out, void* stream);
+                    void* o_out, cp_dtype out_dtype, float* lse_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * cp_ring_pass_q -- ring Pass-Q over all cp_world ranks on one device ([CPMTI §3 "核心公式": KV

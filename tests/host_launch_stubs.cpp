@@ -17,6 +17,9 @@ static hipError_t unexpected(const char* what) {
 hipError_t launch_attn_f32(const AttnParams&, int, hipStream_t) { return unexpected("launch_attn_f32"); }
 hipError_t launch_attn_bf16(const AttnParams&, int, hipStream_t) { return unexpected("launch_attn_bf16"); }
 hipError_t launch_merge(const MergeParams&, hipStream_t) { return unexpected("launch_merge"); }
+hipError_t launch_fill_running(float*, float*, int64_t, int, hipStream_t) {
+  return unexpected("launch_fill_running");
+}
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return unexpected("launch_decode"); }
 hipError_t decode_scratch(void**) { return unexpected("decode_scratch"); }
 hipError_t launch_bwd(const BwdParams&, int, hipStream_t) { return unexpected("launch_bwd"); }

@@ -257,7 +257,7 @@ def test_ring_drivers_validate_every_step_and_merge_before_launching():
         a = _ring_arrays(N, bad_kv=bad)
         st = lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"], a["kv_segs"],
                                  a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, None, None, 0x7000000,
-                                 0x7100000, 0x7200000, cp.CP_BF16, None, None)
+                                 0x7100000, 0x7200000, cp.CP_BF16, None, None, 0, None)
         assert st == cp.CP_E_SHAPE and "kv_segs" in cp.last_error()
     # Pass-KV partials mode with a NULL part: caught by the merge check, before any launch
     a = _ring_arrays(N)
@@ -265,7 +265,7 @@ def test_ring_drivers_validate_every_step_and_merge_before_launching():
     parts[2] = None
     st = lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"], a["kv_segs"],
                              a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, parts, a["l_parts"], None, None,
-                             0x7200000, cp.CP_F32, None, None)
+                             0x7200000, cp.CP_F32, None, None, 0, None)
     assert st == cp.CP_E_ARG
     # Pass-Q: a bad KV shard, and a NULL output of the last Q shard's merge
     for kw, code in (({"bad_kv": 2}, cp.CP_E_SHAPE), ({"bad_o_out": True}, cp.CP_E_ARG)):
@@ -281,7 +281,16 @@ def test_ring_drivers_validate_every_step_and_merge_before_launching():
                               a["l_parts"], a["o_out"], cp.CP_F32, None, None) == cp.CP_E_ARG
     assert lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, N, a["k"], a["v"], a["tk"], a["kv_segs"],
                                a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, a["o_parts"], a["l_parts"], None,
-                               None, 0x7200000, cp.CP_F32, None, None) == cp.CP_E_ARG
+                               None, 0x7200000, cp.CP_F32, None, None, 0, None) == cp.CP_E_ARG
+    # a misaligned running-mode workspace is refused before any launch
+    assert lib.cp_ring_pass_kv(a["q"][0], 16, a["q_segs"][0], 1, N, 0, a["k"], a["v"], a["tk"], a["kv_segs"],
+                               a["nk"], 16, 1, 128, cp.CP_BF16, 1, 0.1, None, None, 0x7000000,
+                               0x7100000, 0x7000000, cp.CP_F32, None, 0x7300008, 1 << 20,
+                               None) == cp.CP_E_ARG
+    assert "workspace" in cp.last_error()
+    # the running-mode workspace holds one partial: O, then the LSEs at the next 256-byte boundary
+    assert cp.ring_workspace_bytes(100, 16, 128) == 100 * 16 * 128 * 4 + 6400
+    assert cp.ring_workspace_bytes(3, 1, 64) == 768 + 256
 
 
 def test_binding_rejects_host_tensors_before_calling_the_library():

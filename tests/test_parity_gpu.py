@@ -53,7 +53,7 @@ def _oracle_keys(ranges, N, shard_ids, seed, n_kv, d, std, dtype, gen=None):
 
 
 def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, mode="partials",
-                check_partials=True, n_sample=None, std=None, gen=None):
+                check_partials=True, n_sample=None, std=None, gen=None, ws=False):
     from context_ring_attention_amd import binding as cp
     ranges = [(i, 0, L) for i, L in enumerate(seqs)]
     std = std if std is not None else (1.0 / np.sqrt(d) if dtype == "f32" else 1.0)
@@ -65,7 +65,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         s.v = device_tensor(seed, si.TID_V, s.tokens, (n_kv, d), std, dtype, gen=gen)
     all_keys = _oracle_keys(ranges, N, range(N), seed, n_kv, d, std, dtype, gen)
     for r in ranks:
-        log(f"pass-kv seqs={seqs} N={N} rank={r} n_h={n_h} n_kv={n_kv} d={d} {dtype} mode={mode} causal={causal}")
+        log(f"pass-kv seqs={seqs} N={N} rank={r} n_h={n_h} n_kv={n_kv} d={d} {dtype} mode={mode} causal={causal} ws={ws}")
         q = device_tensor(seed, si.TID_Q, sh[r].tokens, (n_h, d), std, dtype, gen=gen)
         tq = q.shape[0]
         o_out = torch.empty(tq, n_h, d, dtype=torch.float32, device="cuda")
@@ -79,6 +79,8 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
         else:                            # separate running buffers, final copy through the merge
             kw["o_acc"] = torch.empty(tq, n_h, d, device="cuda")
             kw["lse_acc"] = torch.empty(tq, n_h, device="cuda")
+        if ws:                           # lets a small Q shard's steps split over their keys
+            kw["workspace"] = cp.ring_workspace(tq, n_h, d)
         cp.ring_pass_kv(q, sh[r].segs, r, [sh[s].k for s in range(N)], [sh[s].v for s in range(N)],
                         [sh[s].segs for s in range(N)], causal, scale, o_out, lse_out, **kw)
         torch.cuda.synchronize()
@@ -122,6 +124,19 @@ def test_bf16_ring_ragged_two_sequences():
 
 def test_bf16_ring_running_merge_bf16_d64_gqa4():
     run_pass_kv([700, 1500], 4, 8, 2, 64, "bf16", seed=2, mode="running", ranks=[1, 2])
+
+
+def test_bf16_running_mode_steps_split_over_keys():
+    """Running-mode steps whose Q tiles cannot fill the CUs split over their keys when a ring
+    workspace is given (the second half of every KV run in the workspace, merged in place): ranks
+    of an 8192-token-per-rank ring at 4:1 and 2:1 head ratios, causal and not, against the oracle on
+    sampled rows; a small ring where no step splits, with the workspace, every element."""
+    run_pass_kv([32768], 4, 4, 1, 128, "bf16", mode="running", ranks=[0, 3], ws=True, n_sample=384)
+    run_pass_kv([20000, 12768], 4, 2, 1, 64, "bf16", seed=3, mode="running_out", ranks=[1], ws=True,
+                n_sample=384)
+    run_pass_kv([16384, 16384], 4, 4, 1, 128, "bf16", seed=4, causal=False, mode="running", ranks=[2],
+                ws=True, n_sample=384)
+    run_pass_kv([700, 1500], 4, 8, 2, 64, "bf16", seed=2, mode="running", ranks=[1], ws=True)
 
 
 def test_bf16_degenerate_shapes():
