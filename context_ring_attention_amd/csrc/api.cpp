@@ -835,15 +835,15 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
     const Problem& pr = steps[t];
     int64_t keys = 0;
     for (int j = 0; j < pr.n_kv_segs; ++j) keys += pr.kv_segs[j].len;
-    if (!(cus > 0 && q_tiles < cus && keys >= 4096)) {
+    std::vector<cp_segment> ka, kb;
+    if (cus > 0 && q_tiles < cus && keys >= 4096) halve_kv_runs(pr.kv_segs, pr.n_kv_segs, ka, kb);
+    if (kb.empty()) {  // not split
       st = partial_attn_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale,
                                  filled ? 1 : 0, stream, "cp_ring_pass_kv");
       if (st) return st;
       filled = true;
       continue;
     }
-    std::vector<cp_segment> ka, kb;
-    halve_kv_runs(pr.kv_segs, pr.n_kv_segs, ka, kb);
     Problem two[2] = {pr, pr};
     two[0].kv_segs = ka.data();
     two[0].n_kv_segs = (int)ka.size();
