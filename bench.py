@@ -315,7 +315,8 @@ def run_persistent_kv(torch, cp, si, seed=0):
             cp.ring_pass_kv(qs[r], q_segs[r], r, ks, vs, kv_segs, True, scale, o_kv[r], l_kv[r],
                             o_acc=o_kv[r], lse_acc=l_kv[r], workspace=ws_kv[r] if use_ws else None,
                             check=False)
-    ms_kv = time_reps(torch, pass_kv, 5)
+    # (more warm-up calls: the first calls of the split path in a process run slower)
+    ms_kv = time_reps(torch, pass_kv, 5, warm=6)
     ms_kv_nows = time_reps(torch, lambda: pass_kv(False), 5)
     # The same four rings (without the workspace), each rank on a stream of its own (default
     # priority), as four ranks that share one GPU: the other ranks' launches fill the CUs that one

@@ -377,14 +377,14 @@ def decode_splitkv_noalloc(q, k_cache, v_cache, kv_offset, kv_len, n_splits: int
 
 
 def ring_workspace_bytes(tq: int, n_h: int, d_h: int) -> int:
-    """cp_ring_workspace_bytes: size of the optional running-mode workspace of ring_pass_kv."""
+    """cp_ring_workspace_bytes: one partial of the optional running-mode workspace of ring_pass_kv."""
     return int(load().cp_ring_workspace_bytes(int(tq), int(n_h), int(d_h)))
 
 
-def ring_workspace(tq: int, n_h: int, d_h: int, device="cuda"):
-    """A device workspace of cp_ring_workspace_bytes(tq, n_h, d_h) bytes (uint8)."""
+def ring_workspace(tq: int, n_h: int, d_h: int, partials: int = 1, device="cuda"):
+    """A device workspace of `partials` partials (uint8): a step may split into partials + 1 parts."""
     import torch
-    return torch.empty(ring_workspace_bytes(tq, n_h, d_h), dtype=torch.uint8, device=device)
+    return torch.empty(partials * ring_workspace_bytes(tq, n_h, d_h), dtype=torch.uint8, device=device)
 
 
 def ring_pass_kv(q, q_segs, rank: int, k_shards, v_shards, kv_segs, causal: bool,

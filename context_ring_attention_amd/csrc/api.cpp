@@ -724,6 +724,9 @@ int cp_ring_pass_kv_bwd(const void* q, int64_t tq, const cp_segment* q_segs, int
 
 // Ring Pass-KV ([CPMTI §3 "核心公式"; Fig. 3]): the rank keeps its Q shard; at step t it holds the
 // KV shard that started on rank (rank - t) mod N.
+// Most parts one running-mode ring step is split into (and one launch carries).
+constexpr int kMaxRingSplit = 8;
+
 size_t cp_ring_workspace_bytes(int64_t tq, int n_h, int d_h) {
   if (tq < 0 || n_h <= 0 || d_h <= 0) return 0;
   const size_t rows = (size_t)tq * (size_t)n_h;
@@ -747,24 +750,23 @@ int device_cus() {
   return cus;
 }
 
-// The keys of one ring step divided in two: every KV run longer than 128 keys is cut after a
-// whole number of 64-key tiles near its middle (first parts in `a`, second parts in `b`); shorter
-// runs stay whole in `a`.
-void halve_kv_runs(const cp_segment* runs, int n, std::vector<cp_segment>& a, std::vector<cp_segment>& b) {
+// The keys of one ring step divided into `parts` pieces: every KV run is cut at whole numbers
+// of 64-key tiles near i/parts of its length; piece i of every run goes to out[i] (empty pieces
+// are dropped, so a run of fewer than 64 * parts keys lands in fewer pieces).
+void split_kv_runs(const cp_segment* runs, int n, int parts, std::vector<std::vector<cp_segment>>& out) {
+  out.assign(parts, std::vector<cp_segment>());
   for (int j = 0; j < n; ++j) {
     const cp_segment& r = runs[j];
-    if (r.len <= 128) {
-      a.push_back(r);
-      continue;
+    for (int i = 0; i < parts; ++i) {
+      const int64_t b0 = i == 0 ? 0 : r.len * i / parts / 64 * 64;
+      const int64_t b1 = i == parts - 1 ? r.len : r.len * (i + 1) / parts / 64 * 64;
+      if (b1 <= b0) continue;
+      cp_segment x = r;
+      x.pos_start = r.pos_start + b0;
+      x.local_start = r.local_start + b0;
+      x.len = b1 - b0;
+      out[i].push_back(x);
     }
-    const int64_t first = (r.len / 2 + 63) / 64 * 64;
-    cp_segment x = r, y = r;
-    x.len = first;
-    y.pos_start = r.pos_start + first;
-    y.local_start = r.local_start + first;
-    y.len = r.len - first;
-    a.push_back(x);
-    b.push_back(y);
   }
 }
 
@@ -816,54 +818,75 @@ int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q
     return cp_merge_lse(cp_world, o_parts, lse_parts, rows, d_h, o_out, out_dtype, lse_out, stream);
   }
   // Running mode: each step folds into (o_acc, lse_acc), so the steps run in ring order. A step
-  // whose Q tiles cannot fill the CUs is split over its keys when a workspace is given: both
-  // halves go to the GPU in one launch, each folding into an empty or the running result, and
-  // the workspace half is then merged into (o_acc, lse_acc) in place.
-  const bool ws_fits = workspace && workspace_bytes >= cp_ring_workspace_bytes(tq, n_h, d_h);
+  // whose Q tiles cannot fill the CUs is split over its keys when a workspace is given: its parts
+  // go to the GPU in one launch, the first folding into the running result and each other one
+  // into a workspace partial (both from an empty result), and the partials are then merged into
+  // (o_acc, lse_acc) in place.
+  const size_t part_bytes = cp_ring_workspace_bytes(tq, n_h, d_h);
+  const int64_t ws_parts = workspace && part_bytes > 0 ? (int64_t)(workspace_bytes / part_bytes) : 0;
   int64_t q_tiles = 0;
   for (int i = 0; i < n_q_segs; ++i)
     q_tiles += (q_segs[i].len * (n_h / n_kv) + cpk::kTileRowsBf16 - 1) / cpk::kTileRowsBf16;
   q_tiles *= n_kv;
-  const int cus = ws_fits && in_dtype == CP_BF16 ? device_cus() : 0;
+  const int cus = ws_parts > 0 && in_dtype == CP_BF16 ? device_cus() : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = ws_fits ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                                     round_up256((size_t)rows * d_h * sizeof(float)))
-                          : nullptr;
+  auto ws_o = [&](int i) {  // O of workspace partial i (i >= 1), then its LSEs
+    return reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + (size_t)(i - 1) * part_bytes);
+  };
+  auto ws_lse = [&](int i) {
+    return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws_o(i)) +
+                                    round_up256((size_t)rows * d_h * sizeof(float)));
+  };
   bool filled = false;  // (o_acc, lse_acc) holds a result (or the empty one)
   for (int t = 0; t < cp_world; ++t) {
     const Problem& pr = steps[t];
     int64_t keys = 0;
     for (int j = 0; j < pr.n_kv_segs; ++j) keys += pr.kv_segs[j].len;
-    std::vector<cp_segment> ka, kb;
-    if (cus > 0 && q_tiles < cus && keys >= 4096) halve_kv_runs(pr.kv_segs, pr.n_kv_segs, ka, kb);
-    if (kb.empty()) {  // not split
+    // parts: enough to fill the CUs, at least 2048 keys each, at most kMaxRingSplit
+    int64_t parts = 1;
+    if (cus > 0 && q_tiles > 0 && q_tiles < cus)
+      parts = std::min<int64_t>({(int64_t)kMaxRingSplit, (cus + q_tiles - 1) / q_tiles, keys / 2048,
+                                 ws_parts + 1});
+    std::vector<std::vector<cp_segment>> pk;
+    if (parts > 1) split_kv_runs(pr.kv_segs, pr.n_kv_segs, (int)parts, pk);
+    int used = 0;  // non-empty parts, in order
+    for (const auto& v : pk) used += v.empty() ? 0 : 1;
+    if (used < 2) {  // not split
       st = partial_attn_problems(&pr, 1, n_h, n_kv, d_h, in_dtype, causal, softmax_scale,
                                  filled ? 1 : 0, stream, "cp_ring_pass_kv");
       if (st) return st;
       filled = true;
       continue;
     }
-    Problem two[2] = {pr, pr};
-    two[0].kv_segs = ka.data();
-    two[0].n_kv_segs = (int)ka.size();
-    two[1].kv_segs = kb.data();
-    two[1].n_kv_segs = (int)kb.size();
-    two[1].o = ws_o;
-    two[1].lse = ws_lse;
+    std::vector<Problem> probs;
+    std::vector<const float*> mo, ml;
+    for (const auto& v : pk) {
+      if (v.empty()) continue;
+      Problem x = pr;
+      x.kv_segs = v.data();
+      x.n_kv_segs = (int)v.size();
+      const int i = (int)probs.size();
+      if (i > 0) {
+        x.o = ws_o(i);
+        x.lse = ws_lse(i);
+      }
+      probs.push_back(x);
+      mo.push_back(x.o);
+      ml.push_back(x.lse);
+    }
     if (!filled) {
       st = launch_status(cpk::launch_fill_running(o_acc, lse_acc, rows, d_h, hs), "cp_ring_pass_kv");
       if (st) return st;
       filled = true;
     }
-    st = launch_status(cpk::launch_fill_running(ws_o, ws_lse, rows, d_h, hs), "cp_ring_pass_kv");
+    for (int i = 1; i < (int)probs.size(); ++i) {
+      st = launch_status(cpk::launch_fill_running(ws_o(i), ws_lse(i), rows, d_h, hs), "cp_ring_pass_kv");
+      if (st) return st;
+    }
+    st = partial_attn_problems(probs.data(), (int)probs.size(), n_h, n_kv, d_h, in_dtype, causal,
+                               softmax_scale, 1, stream, "cp_ring_pass_kv");
     if (st) return st;
-    st = partial_attn_problems(two, 2, n_h, n_kv, d_h, in_dtype, causal, softmax_scale, 1, stream,
-                               "cp_ring_pass_kv");
-    if (st) return st;
-    const float* mo[2] = {o_acc, ws_o};
-    const float* ml[2] = {lse_acc, ws_lse};
-    st = cp_merge_lse(2, mo, ml, rows, d_h, o_acc, CP_F32, lse_acc, stream);
+    st = cp_merge_lse((int)probs.size(), mo.data(), ml.data(), rows, d_h, o_acc, CP_F32, lse_acc, stream);
     if (st) return st;
   }
   if (fold_only) return ok();

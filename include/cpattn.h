@@ -185,9 +185,10 @@ int cp_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_
                               float softmax_scale, cp_dtype ws_dtype, void* o_out,
                               cp_dtype out_dtype, float* lse_out, void* stream);
 
-/* cp_ring_workspace_bytes -- size of the optional workspace of cp_ring_pass_kv's running mode for
- * a Q shard of tq tokens: one partial (O, then LSE at the next 256-byte boundary) of tq * n_h rows
- * of d_h fp32 values. Host-only. */
+/* cp_ring_workspace_bytes -- size of one partial of the optional workspace of cp_ring_pass_kv's
+ * running mode for a Q shard of tq tokens: O, then the LSEs at the next 256-byte boundary, of
+ * tq * n_h rows of d_h fp32 values. A workspace of k such partials lets a step split into up to
+ * k + 1 parts. Host-only. */
 size_t cp_ring_workspace_bytes(int64_t tq, int n_h, int d_h);
 
 /* ---------------------------------------------------------------------------------------------
@@ -201,14 +202,16 @@ size_t cp_ring_workspace_bytes(int64_t tq, int n_h, int d_h);
  *   Mode "running" (o_parts == NULL): steps accumulate into o_acc / lse_acc (device fp32), and
  *     o_out receives the result in out_dtype (o_out may equal o_acc when out_dtype is fp32).
  *   lse_out may be NULL.
- *   workspace, workspace_bytes: optional device scratch for the running mode (NULL or too small:
- *     none; 16-byte aligned; ignored in the partials mode), caller-owned, at most
- *     cp_ring_workspace_bytes(tq, n_h, d_h) of it used. With bf16 inputs, a step whose Q shard
- *     has fewer 256-row tiles (over all KV heads) than the device has CUs, and at least 4096 keys,
- *     is split over its keys: the first half of every KV run folds into (o_acc, lse_acc), the
- *     second half goes to the workspace in the same launch, and the two are then merged in
- *     place. The split depends only on the shapes, the device's CU count and workspace_bytes.
- *     Calls sharing one workspace must be ordered on one stream.
+ *   workspace, workspace_bytes: optional device scratch for the running mode (NULL or smaller
+ *     than one partial: none; 16-byte aligned; ignored in the partials mode), caller-owned, in
+ *     partials of cp_ring_workspace_bytes(tq, n_h, d_h) bytes. With bf16 inputs, a step whose Q
+ *     shard has fewer 256-row tiles (over all KV heads) than the device has CUs is split over its
+ *     keys into p parts: as many as fill the CUs, at most 8, at most one more than the workspace
+ *     holds partials, and at least 2048 keys each (every KV run is cut at whole 64-key tiles near
+ *     i/p of its length). The parts run in one launch, the first folding into (o_acc, lse_acc),
+ *     the others into workspace partials, which are then merged in place. The split depends only
+ *     on the shapes, the device's CU count and workspace_bytes. Calls sharing one workspace must
+ *     be ordered on one stream.
  * ------------------------------------------------------------------------------------------- */
 int cp_ring_pass_kv(const void* q, int64_t tq, const cp_segment* q_segs, int n_q_segs,
                     int cp_world, int rank, const void* const* k_shards,

@@ -80,7 +80,7 @@ def run_pass_kv(seqs, N, n_h, n_kv, d, dtype, seed=0, causal=True, ranks=None, m
             kw["o_acc"] = torch.empty(tq, n_h, d, device="cuda")
             kw["lse_acc"] = torch.empty(tq, n_h, device="cuda")
         if ws:                           # lets a small Q shard's steps split over their keys
-            kw["workspace"] = cp.ring_workspace(tq, n_h, d)
+            kw["workspace"] = cp.ring_workspace(tq, n_h, d, partials=int(ws))
         cp.ring_pass_kv(q, sh[r].segs, r, [sh[s].k for s in range(N)], [sh[s].v for s in range(N)],
                         [sh[s].segs for s in range(N)], causal, scale, o_out, lse_out, **kw)
         torch.cuda.synchronize()
@@ -137,6 +137,10 @@ def test_bf16_running_mode_steps_split_over_keys():
     run_pass_kv([16384, 16384], 4, 4, 1, 128, "bf16", seed=4, causal=False, mode="running", ranks=[2],
                 ws=True, n_sample=384)
     run_pass_kv([700, 1500], 4, 8, 2, 64, "bf16", seed=2, mode="running", ranks=[1], ws=True)
+    # 8192 tokens per rank at 1:1 heads (32 Q tiles): up to 4 parts of 2048 keys with 7 partials
+    run_pass_kv([32768], 4, 1, 1, 128, "bf16", seed=5, mode="running", ranks=[0, 2], ws=7, n_sample=512)
+    run_pass_kv([24000, 8768], 4, 2, 2, 64, "bf16", seed=6, causal=False, mode="running_out", ranks=[3],
+                ws=3, n_sample=512)
 
 
 def test_bf16_degenerate_shapes():
