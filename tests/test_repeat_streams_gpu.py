@@ -120,6 +120,34 @@ def test_ring_merge_and_decode_are_bitwise_repeatable():
         _same(x, y, f"decode {name}")
 
 
+def test_split_ring_steps_are_bitwise_repeatable():
+    """Running-mode Pass-KV steps split over their keys (four parts through a ring workspace of
+    three partials): two calls whose workspaces start with different garbage give the same bits
+    (the partials start from a filled empty result, the merge order is fixed)."""
+    from context_ring_attention_amd import binding as cp
+    N, r, n_h, n_kv, d = 4, 1, 1, 1, 128
+    sh = product_shards([(0, 0, 32768)], N)
+    for s in sh.values():
+        s.k = device_tensor(7, si.TID_K, s.tokens, (n_kv, d), 1.0, "bf16")
+        s.v = device_tensor(7, si.TID_V, s.tokens, (n_kv, d), 1.0, "bf16")
+    q = device_tensor(7, si.TID_Q, sh[r].tokens, (n_h, d), 1.0, "bf16")
+    outs = []
+    for fill in (0, 255):
+        ws = cp.ring_workspace(q.shape[0], n_h, d, partials=3)
+        ws.fill_(fill)
+        o = torch.full((q.shape[0], n_h, d), float("nan"), device="cuda")
+        lse = torch.full((q.shape[0], n_h), 7.0, device="cuda")
+        log(f"split running pass-kv, workspace filled with {fill}")
+        cp.ring_pass_kv(q, sh[r].segs, r, [sh[s].k for s in range(N)], [sh[s].v for s in range(N)],
+                        [sh[s].segs for s in range(N)], True, scale_of(d), o, lse, o_acc=o, lse_acc=lse,
+                        workspace=ws)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for x, y, name in zip(outs[0], outs[1], ("O", "LSE")):
+        _same(x, y, f"split pass-kv {name}")
+    assert torch.isfinite(outs[0][0]).all()
+
+
 def test_concurrent_streams_match_serial_results():
     ring, dec = Ring(seed=2, rank=3), Decode(seed=3)
     ref_ring = ring.run("running")
