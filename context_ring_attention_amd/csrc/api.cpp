@@ -907,9 +907,11 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
       !n_kv_segs || !o_parts || !lse_parts || !o_out)
     return fail(CP_E_ARG, "NULL array argument");
   const int N = cp_world;
-  // Step t: the rank holding KV shard s computes Q shard (s - t) mod N against it. The N partials
-  // of a step are independent and go to the GPU as one launch. All N*N partials and the N merges
-  // are validated before the first launch.
+  // Step t: the rank holding KV shard s computes Q shard (s - t) mod N against it. Every one of the
+  // N*N partials lands in a slot of its own, so on one GPU they are all independent: they go to the
+  // GPU in ring-step order, as many problems per launch as the kernel's tables take (two steps of
+  // a 4-rank ring per launch). All N*N partials and the N merges are validated before the first
+  // launch.
   std::vector<Problem> all((size_t)N * N);
   for (int t = 0; t < N; ++t)
     for (int s = 0; s < N; ++s) {
@@ -926,9 +928,9 @@ int cp_ring_pass_q(int cp_world, const void* const* q_shards, const int64_t* tq,
                          d_h, o_out[qi], out_dtype);
     if (vst) return vst;
   }
-  for (int t = 0; t < N; ++t) {
-    const int st = partial_attn_problems(all.data() + (size_t)t * N, N, n_h, n_kv, d_h, in_dtype,
-                                         causal, softmax_scale, 0, stream, "cp_ring_pass_q");
+  {
+    const int st = partial_attn_problems(all.data(), N * N, n_h, n_kv, d_h, in_dtype, causal,
+                                         softmax_scale, 0, stream, "cp_ring_pass_q");
     if (st) return st;
   }
   for (int qi = 0; qi < N; ++qi) {
