@@ -92,6 +92,19 @@ def test_pass_kv_rescale_paths(name, d, n_h, n_kv, mode):
         run_pass_kv(seqs, N, n_h, n_kv, d, "bf16", seed=21, mode=mode, ranks=[rank], std=1.0, gen=gen)
 
 
+@pytest.mark.parametrize("name", ["wide_std6", "late_spike", "sink_later_run", "early_dominant"])
+def test_split_running_steps_with_rescale_inputs(name):
+    """Running-mode steps split over their keys (8192 tokens per rank at 2:1 heads: 64 Q tiles,
+    four parts with a workspace of three partials), on inputs whose parts differ by tens of nats
+    in LSE, so the in-place merge of the parts weighs one part almost alone."""
+    seqs, N = [20000, 12768], 4
+    for rank in (0, N - 1):
+        gen = _profile(name, seqs, N, rank, 128)
+        log(f"split rescale case {name} rank={rank}")
+        run_pass_kv(seqs, N, 2, 1, 128, "bf16", seed=24, mode="running", ranks=[rank], std=1.0,
+                    gen=gen, ws=3, n_sample=512)
+
+
 @pytest.mark.parametrize("name", ["wide_std6", "late_spike", "ramp"])
 def test_pass_kv_rescale_paths_without_causal_mask(name):
     seqs, N = [1100], 2
