@@ -473,11 +473,59 @@ def run_decode_step_graph(torch, cp, si, seed=0, L=131072, reps=50):
     log(f"decode step B=1 L={L}: back to back eager {eager_ms * 1e3:.1f} us, graph "
         f"{graph_ms * 1e3:.1f} us; host-synced eager {eager_sync_ms * 1e3:.1f} us, graph "
         f"{graph_sync_ms * 1e3:.1f} us")
+
+    # One token through a stack of layers, each with a cache of its own (the layers' caches are
+    # the first one rotated by different offsets): eager, 2 launches per layer; or one replay of
+    # a graph holding every layer's launches.
+    n_layers = 16
+    kcs = [kc.roll(977 * i, 0) for i in range(n_layers)]
+    vcs = [vc.roll(977 * i, 0) for i in range(n_layers)]
+    wss = [cp.decode_workspace(1, n_h, d, S) for _ in range(n_layers)]
+    outs = [(torch.empty(1, n_h, d, device="cuda"), torch.empty(1, n_h, device="cuda"))
+            for _ in range(n_layers)]
+
+    def stack():
+        for i in range(n_layers):
+            cp.decode_splitkv(q, kcs[i], vcs[i], offs, lens, S, scale, wss[i][0], wss[i][1],
+                              outs[i][0], outs[i][1], check=False)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_stack = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_stack):
+        stack()
+    stack_ms = time_reps(torch, stack, 20)
+    stack_graph_ms = time_reps(torch, graph_stack.replay, 20)
+    stack_sync_ms, stack_graph_sync_ms = synced(stack), synced(graph_stack.replay)
+    stack()
+    ref = [(x.clone(), y.clone()) for x, y in outs]
+    same = True
+    for _ in range(3):  # replays with the program's own eager work in between
+        for x, y in outs:
+            x.fill_(float("nan"))
+            y.fill_(float("nan"))
+        graph_stack.replay()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(x, a) and torch.equal(y, b) for (x, y), (a, b) in zip(outs, ref))
+    log(f"decode token through {n_layers} layers (B=1, L={L} each): back to back eager "
+        f"{stack_ms * 1e3:.1f} us, graph {stack_graph_ms * 1e3:.1f} us; host-synced eager "
+        f"{stack_sync_ms * 1e3:.1f} us, graph {stack_graph_sync_ms * 1e3:.1f} us; replays match "
+        f"eager: {same}")
+    del kcs, vcs, wss, outs, graph_stack
     return {"metric": "decode step latency", "unit": "us", "higher_is_better": False,
             "back_to_back": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3, 2)},
             "host_synced": {"eager_us": round(eager_sync_ms * 1e3, 2),
                             "graph_us": round(graph_sync_ms * 1e3, 2)},
-            "eager_GBps": round(alg / (eager_ms * 1e-3) / 1e9, 1), "cached_keys": L, "n_splits": S}
+            "eager_GBps": round(alg / (eager_ms * 1e-3) / 1e9, 1), "cached_keys": L, "n_splits": S,
+            "token_through_layers": {
+                "layers": n_layers, "launches_per_token_eager": 2 * n_layers,
+                "back_to_back": {"eager_us": round(stack_ms * 1e3, 2),
+                                 "graph_us": round(stack_graph_ms * 1e3, 2)},
+                "host_synced": {"eager_us": round(stack_sync_ms * 1e3, 2),
+                                "graph_us": round(stack_graph_sync_ms * 1e3, 2)},
+                "graph_replays_match_eager": bool(same)}}
 
 
 def run_tiny_ring(torch, cp, si):
