@@ -3,7 +3,8 @@
 Each case draws sequence lengths (ragged, down to one token), a CP world, a head ratio, D_H,
 input dtype, the causal flag and the ring variant (Pass-KV with partials or a running merge, or
 Pass-Q over a cached prefix), then checks one rank's merged result, and its partials where the
-mode keeps them, element by element against the oracle ("Context Parallelism for Scalable
+mode keeps them, element by element against the oracle (larger running-mode rings with a ring
+workspace on sampled rows) ("Context Parallelism for Scalable
 Million-Token Inference", §3 core formulas; the oracle's readings are the ones the other parity
 tests use).
 """
@@ -49,6 +50,34 @@ def test_random_config(kind, kw):
         run_pass_q(**kw)
     else:
         run_pass_kv(**kw)
+
+
+def _draw_split_cases(n_cases, seed=2029):
+    """Running-mode rings with a ring workspace, large enough that steps of the smaller head ratios
+    split over their keys; checked on sampled rows."""
+    rng = np.random.default_rng(seed)
+    heads = [(4, 1), (2, 1), (1, 1), (8, 2), (4, 4), (16, 1)]
+    cases = []
+    for i in range(n_cases):
+        n_h, n_kv = heads[rng.integers(len(heads))]
+        N = int(rng.choice([2, 4]))
+        total = int(rng.integers(16000, 64000))
+        cuts = sorted(int(x) for x in rng.integers(1, total, size=int(rng.integers(0, 3))))
+        seqs = [b - a for a, b in zip([0] + cuts, cuts + [total]) if b > a]
+        cases.append(dict(seqs=seqs, N=N, n_h=n_h,
+                          n_kv=n_kv, d=int(rng.choice([64, 128])), dtype="bf16", seed=400 + i,
+                          causal=bool(rng.random() < 0.8), ranks=[int(rng.integers(N))],
+                          mode=str(rng.choice(["running", "running_out"])),
+                          ws=int(rng.choice([1, 2, 3, 7])), n_sample=256))
+    return cases
+
+
+SPLIT_CASES = _draw_split_cases(8)
+
+
+@pytest.mark.parametrize("kw", SPLIT_CASES, ids=[f"split-{i}" for i in range(len(SPLIT_CASES))])
+def test_random_split_ring_config(kw):
+    run_pass_kv(**kw)
 
 
 def _draw_decode_cases(n_cases, seed=2027):
