@@ -516,6 +516,8 @@ size_t cp_decode_workspace_bytes(int batch, int n_h, int d_h, int n_splits) {
 
 namespace {
 
+int device_cus();
+
 // Argument checks of a decode call, apart from the workspace (nothing is launched).
 int validate_decode(int batch, int n_h, int n_kv, int d_h, cp_dtype in_dtype, int n_splits,
                     float softmax_scale, cp_dtype ws_dtype, cp_dtype out_dtype) {
@@ -571,6 +573,13 @@ int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache
   p.ws_bf16 = ws_dtype == CP_BF16;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  // Large batches take the persistent split kernel: one one-wave workgroup per SIMD (four per CU,
+  // one round), each walking 4 to kDecodeMaxUnits (request, split, head block) units and storing
+  // their partials at its end. Requests are ranked by lanes, so at most 64 of them.
+  const int64_t units = (int64_t)batch * n_splits * n_kv * ((p.group + 15) / 16);
+  const int64_t slots = 4 * (int64_t)device_cus();
+  const int64_t per_wave = slots > 0 ? (units + slots - 1) / slots : 0;
+  p.units_per_wave = (batch <= 64 && per_wave >= 4 && per_wave <= cpk::kDecodeMaxUnits) ? (int)per_wave : 0;
   return launch_status(cpk::launch_decode(p, d_h, static_cast<hipStream_t>(stream)), "cp_decode_splitkv");
 }
 

@@ -85,7 +85,12 @@ struct DecodeParams {
   int32_t ws_bf16;
   float scale;
   float scale_log2;
+  // > 0: the persistent split kernel, each wave walking up to this many units (host-chosen)
+  int32_t units_per_wave;
 };
+
+// Units a persistent decode wave can hold finished partials of (registers).
+constexpr int kDecodeMaxUnits = 8;
 
 // Arguments of one backward launch pair (dQ kernel, then dK/dV kernel) for one Q shard against
 // one KV shard. Q tiles (256 rows) are numbered over the Q runs in `q_order`, the last tile of a run

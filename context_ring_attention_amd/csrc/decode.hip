@@ -53,54 +53,36 @@ struct DecCfg {
   static constexpr int kVLoads = kBK * kChunks / 64;
 };
 
-// W waves share one (request, split, 16-head block): wave w takes the w-th of W equal parts of
-// the split's keys with LDS of its own, and the W partial results are combined in LDS before
-// the split's partial is written. W = 1 for large batches (enough workgroups to fill the chip);
-// W = 4 for small ones, where one wave per split would leave most of each CU idle.
-template <int D, int W, bool WS_BF16>
-__global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams p) {
-  using C = DecCfg<D>;
-  // combine area: per wave 16 heads x (D values of O + m + l), in fp32
-  constexpr int kCombineBytes = W > 1 ? W * 16 * (D + 2) * 4 : 0;
-  constexpr int kLdsBytes = W * C::kStageBytes > kCombineBytes ? W * C::kStageBytes : kCombineBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-
-  const int wave = W > 1 ? (int)(threadIdx.x / 64) : 0;
-  const int lane = threadIdx.x & 63;
-  unsigned char* ks = smem + wave * C::kStageBytes;
-  unsigned char* vs = ks + C::kBK * C::kStrideK;
-
-  const int c = blockIdx.x % p.n_splits;  // split (fastest: neighbours stream adjacent keys)
-  // Requests are taken longest first, so the last workgroups to be dispatched are the shortest
-  // splits and the tail of the launch stays short. For batches of up to 64 requests, lane i ranks
-  // request i by length (ties by index) and the workgroup picks the request of rank blockIdx/S.
-  int b = blockIdx.x / p.n_splits;
-  if (p.batch <= 64) {
-    const int want = b;
-    const int i = lane;
-    const int64_t li = i < p.batch ? p.kv_len[i] : -1;
-    int rank = 0;
-    for (int j = 0; j < p.batch; ++j) {
-      const int64_t lj = p.kv_len[j];
-      rank += (lj > li) || (lj == li && j < i);
-    }
-    const unsigned long long hit = __ballot(i < p.batch && rank == want);
-    b = __ffsll(hit) - 1;
+// Rank of request i by cached length, longest first (ties by index); batch <= 64, one request per
+// lane.
+__device__ __forceinline__ int request_rank(const DecodeParams& p, int i) {
+  const int64_t li = i < p.batch ? p.kv_len[i] : -1;
+  int rank = 0;
+  for (int j = 0; j < p.batch; ++j) {
+    const int64_t lj = p.kv_len[j];
+    rank += (lj > li) || (lj == li && j < i);
   }
-  const int hblocks = (p.group + 15) / 16;
-  const int g = blockIdx.y / hblocks;
-  const int h0 = (blockIdx.y % hblocks) * 16;
+  return rank;
+}
+
+// The request of rank `want`, from every lane's request_rank (wave-uniform call; batch <= 64).
+__device__ __forceinline__ int request_of_rank(const DecodeParams& p, int lane, int lane_rank, int want) {
+  const unsigned long long hit = __ballot(lane < p.batch && lane_rank == want);
+  return __ffsll(hit) - 1;
+}
+
+// One wave walks keys [wlo, wlo + n) of request b for the 16 query heads h0.. of KV head g and
+// leaves the running max m (base-2 units, the same in every lane of a head column), the lane's
+// part of the row sum l, and the unnormalised O^T accumulators. ks / vs: the wave's own staging
+// LDS (its accesses are ordered among themselves, so no barrier is needed).
+template <int D>
+__device__ __forceinline__ void decode_walk(const DecodeParams& p, unsigned char* ks, unsigned char* vs,
+                                            int lane, int b, int g, int h0, int64_t wlo, int n,
+                                            float& m, float& l, f32x4 (&oacc)[D / 16]) {
+  using C = DecCfg<D>;
   const int col = lane & 15;  // head column of the 16x16 blocks
   const int grp = lane >> 4;  // 0..3: k slice of the operands, row group of the accumulator
-  const int64_t L = p.kv_len[b] > 0 ? p.kv_len[b] : 0;  // a negative length reads as an empty cache
   const int64_t base = p.kv_offset[b];
-  const int64_t lo = ((int64_t)c * L) / p.n_splits;
-  const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;
-  // this wave's part of the split
-  const int64_t wlo = lo + ((hi - lo) * wave) / W;
-  const int64_t whi = lo + ((hi - lo) * (wave + 1)) / W;
-  const int n = (int)(whi - wlo);
-
   const __bf16* __restrict__ Kc = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ Vc = static_cast<const __bf16*>(p.v);
 
@@ -141,8 +123,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
     *reinterpret_cast<u32x4*>(ks + row * C::kStrideK + c16) = kr[i];                 \
   }
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 oacc[C::kDBlocks];
+  m = -INFINITY;
+  l = 0.f;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -151,8 +133,6 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
   const int tr_row = 4 * grp + (j16 >> 2);
   const int tr_col = 4 * (j16 & 3);
 
-  // The staging LDS is this wave's own: the wave's LDS accesses are ordered among themselves, so
-  // the loop needs no workgroup barrier (and waves with different key counts never meet one).
   if (n > 0) CP_DEC_LOAD(0);
   // retire the q and first-block loads together before the block loop (keeps the loop's
   // prefetch out of its waits)
@@ -221,6 +201,89 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
   }
 #undef CP_DEC_LOAD
 #undef CP_DEC_STORE
+}
+
+// Stores the partial of (request b, split c, 16-head block h0 of KV head g): the normalised O
+// (a lane holds 4-value pieces of head column col's row) and the lane's LSE (natural log), for
+// the heads that exist. The workspace layout [batch][n_splits][n_h][D] makes those heads' rows
+// one contiguous block. Stored directly, every instruction would write 16 separate pieces; the
+// tile goes through the wave's staging LDS `tile` instead (no longer read; the wave's LDS
+// accesses are in order) and leaves as whole rows, 16 bytes per lane, each instruction covering
+// 1 KB of consecutive bytes.
+template <int D, bool WS_BF16>
+__device__ __forceinline__ void decode_store(const DecodeParams& p, unsigned char* tile, int lane, int b,
+                                             int c, int g, int h0, const f32x4 (&o)[D / 16], float lse) {
+  using C = DecCfg<D>;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  constexpr int kElt = WS_BF16 ? 2 : 4;        // bytes per stored value
+  constexpr int kRowBytes = D * kElt;
+  // padded LDS rows: the 16 head rows written by one instruction land on distinct banks
+  constexpr int kTStride = kRowBytes + (WS_BF16 ? 32 : 16);
+  static_assert(16 * kTStride <= C::kStageBytes, "the tile fits the wave's staging LDS");
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db) {
+    unsigned char* dst = tile + col * kTStride + (db * 16 + 4 * grp) * kElt;
+    if constexpr (WS_BF16) {
+      const bf16x4 o4 = {(__bf16)o[db][0], (__bf16)o[db][1], (__bf16)o[db][2], (__bf16)o[db][3]};
+      *reinterpret_cast<bf16x4*>(dst) = o4;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = o[db];
+    }
+  }
+  const int n_valid = min(16, p.group - h0);  // heads of this block that exist
+  const int64_t prow0 = ((int64_t)b * p.n_splits + c) * p.n_h + g * p.group + h0;
+  unsigned char* wo = static_cast<unsigned char*>(p.ws_o) + prow0 * kRowBytes;
+  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += kRowsPerStore) {
+    const int r = r0 + lane / kLanesPerRow;
+    const int c16 = (lane % kLanesPerRow) * 16;
+    if (r < n_valid)
+      *reinterpret_cast<u32x4*>(wo + r * kRowBytes + c16) = *reinterpret_cast<const u32x4*>(tile + r * kTStride + c16);
+  }
+  if (grp == 0 && h0 + col < p.group) p.ws_lse[prow0 + col] = lse;
+}
+
+// W waves share one (request, split, 16-head block): wave w takes the w-th of W equal parts of
+// the split's keys with LDS of its own, and the W partial results are combined in LDS before
+// the split's partial is written. W = 1 for large batches (enough workgroups to fill the chip);
+// W = 4 for small ones, where one wave per split would leave most of each CU idle.
+template <int D, int W, bool WS_BF16>
+__global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams p) {
+  using C = DecCfg<D>;
+  // combine area: per wave 16 heads x (D values of O + m + l), in fp32
+  constexpr int kCombineBytes = W > 1 ? W * 16 * (D + 2) * 4 : 0;
+  constexpr int kLdsBytes = W * C::kStageBytes > kCombineBytes ? W * C::kStageBytes : kCombineBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+
+  const int wave = W > 1 ? (int)(threadIdx.x / 64) : 0;
+  const int lane = threadIdx.x & 63;
+  unsigned char* ks = smem + wave * C::kStageBytes;
+  unsigned char* vs = ks + C::kBK * C::kStrideK;
+
+  const int c = blockIdx.x % p.n_splits;  // split (fastest: neighbours stream adjacent keys)
+  // Requests are taken longest first, so the last workgroups to be dispatched are the shortest
+  // splits and the tail of the launch stays short (for batches of up to 64 requests; the
+  // workgroup takes the request of rank blockIdx / S).
+  int b = blockIdx.x / p.n_splits;
+  if (p.batch <= 64) b = request_of_rank(p, lane, request_rank(p, lane), b);
+  const int hblocks = (p.group + 15) / 16;
+  const int g = blockIdx.y / hblocks;
+  const int h0 = (blockIdx.y % hblocks) * 16;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t L = p.kv_len[b] > 0 ? p.kv_len[b] : 0;  // a negative length reads as an empty cache
+  const int64_t lo = ((int64_t)c * L) / p.n_splits;
+  const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;
+  // this wave's part of the split
+  const int64_t wlo = lo + ((hi - lo) * wave) / W;
+  const int64_t whi = lo + ((hi - lo) * (wave + 1)) / W;
+
+  float m, l;
+  f32x4 oacc[C::kDBlocks];
+  decode_walk<D>(p, ks, vs, lane, b, g, h0, wlo, (int)(whi - wlo), m, l, oacc);
 
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
@@ -263,42 +326,95 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(const DecodeParams
       }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // The partial O of this (request, split, head block) is a [heads][D] tile, and the workspace
-  // layout [batch][n_splits][n_h][D] makes its valid heads one contiguous block. A lane holds
-  // 4-value pieces of one head's row; stored directly, every instruction would write 16 separate
-  // pieces. The tile goes through this wave's staging LDS instead (no longer read; the wave's LDS
-  // accesses are in order) and leaves as whole rows, 16 bytes per lane, each instruction covering
-  // 1 KB of consecutive bytes.
-  constexpr int kElt = WS_BF16 ? 2 : 4;        // bytes per stored value
-  constexpr int kRowBytes = D * kElt;
-  // padded LDS rows: the 16 head rows written by one instruction land on distinct banks
-  constexpr int kTStride = kRowBytes + (WS_BF16 ? 32 : 16);
-  static_assert(16 * kTStride <= C::kStageBytes, "the tile fits the wave's staging LDS");
-  unsigned char* tile = ks;
+  f32x4 o[C::kDBlocks];
 #pragma unroll
-  for (int db = 0; db < C::kDBlocks; ++db) {
-    unsigned char* dst = tile + col * kTStride + (db * 16 + 4 * grp) * kElt;
-    if constexpr (WS_BF16) {
-      const bf16x4 o4 = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
-                         (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
-      *reinterpret_cast<bf16x4*>(dst) = o4;
-    } else {
-      *reinterpret_cast<f32x4*>(dst) = oacc[db] * inv;
+  for (int db = 0; db < C::kDBlocks; ++db) o[db] = oacc[db] * inv;
+  decode_store<D, WS_BF16>(p, ks, lane, b, c, g, h0, o, lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY);
+}
+
+// Unit `pos` of the persistent split kernel: units are numbered request rank major (longest
+// request first), then KV head and head block, then split.
+__device__ __forceinline__ void decode_unit_coords(const DecodeParams& p, int lane, int lane_rank, int pos,
+                                                   int per_req, int hblocks, int& b, int& c, int& g,
+                                                   int& h0) {
+  const int r = pos / per_req;
+  const int rem = pos - r * per_req;
+  const int y = rem / p.n_splits;
+  c = rem - y * p.n_splits;
+  b = request_of_rank(p, lane, lane_rank, r);
+  g = y / hblocks;
+  h0 = (y - g * hblocks) * 16;
+}
+
+// Large batches (batch <= 64, 4 to kDecodeMaxUnits units per SIMD): one wave per SIMD walks
+// p.units_per_wave (request, split, 16-head block) units in turn, each as decode_split_kernel's
+// one-wave walk, and keeps every finished partial (normalised O and LSE) in registers; it stores
+// them all when it is done. Units are dealt in a zigzag over the longest-first numbering (wave w
+// takes units w, 2G-1-w, 2G+w, ... of a grid of G waves), which gives every wave about the same
+// number of keys. The splits and their partials are those of decode_split_kernel; only when the
+// partials reach HBM changes: the waves finish together, so the partial writes leave in one burst
+// at the end instead of mixing with the K/V stream throughout the launch (interleaved writes slow
+// the read stream far more than their own bytes cost).
+template <int D, bool WS_BF16>
+__global__ __launch_bounds__(64) void decode_split_persist_kernel(const DecodeParams p) {
+  using C = DecCfg<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStageBytes];
+  const int lane = threadIdx.x;
+  unsigned char* ks = smem;
+  unsigned char* vs = smem + C::kBK * C::kStrideK;
+  const int G = (int)gridDim.x, w = (int)blockIdx.x;
+  const int hblocks = (p.group + 15) / 16;
+  const int per_req = p.n_splits * p.n_kv * hblocks;  // the host bounds the unit count to int
+  const int units = per_req * p.batch;
+  const int lane_rank = request_rank(p, lane);
+
+  f32x4 park[kDecodeMaxUnits][C::kDBlocks];
+  float park_lse[kDecodeMaxUnits];
+  int park_pos[kDecodeMaxUnits];
+#pragma unroll
+  for (int s = 0; s < kDecodeMaxUnits; ++s) {
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) park[s][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    park_lse[s] = -INFINITY;
+    park_pos[s] = 0;
+  }
+  int done = 0;
+  for (int k = 0; k < p.units_per_wave; ++k) {
+    const int pos = k * G + ((k & 1) ? G - 1 - w : w);
+    if (pos >= units) break;  // later units of this wave lie further on
+    int b, c, g, h0;
+    decode_unit_coords(p, lane, lane_rank, pos, per_req, hblocks, b, c, g, h0);
+    const int64_t L = p.kv_len[b] > 0 ? p.kv_len[b] : 0;
+    const int64_t lo = ((int64_t)c * L) / p.n_splits;
+    const int64_t hi = ((int64_t)(c + 1) * L) / p.n_splits;
+    float m, l;
+    f32x4 oacc[C::kDBlocks];
+    decode_walk<D>(p, ks, vs, lane, b, g, h0, lo, (int)(hi - lo), m, l, oacc);
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // park: slot 0 takes this unit, the others move up one (static register indices)
+#pragma unroll
+    for (int s = kDecodeMaxUnits - 1; s > 0; --s) {
+#pragma unroll
+      for (int db = 0; db < C::kDBlocks; ++db) park[s][db] = park[s - 1][db];
+      park_lse[s] = park_lse[s - 1];
+      park_pos[s] = park_pos[s - 1];
+    }
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) park[0][db] = oacc[db] * inv;
+    park_lse[0] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    park_pos[0] = pos;
+    ++done;
+  }
+#pragma unroll
+  for (int s = 0; s < kDecodeMaxUnits; ++s) {
+    if (s < done) {
+      int b, c, g, h0;
+      decode_unit_coords(p, lane, lane_rank, park_pos[s], per_req, hblocks, b, c, g, h0);
+      decode_store<D, WS_BF16>(p, ks, lane, b, c, g, h0, park[s], park_lse[s]);
     }
   }
-  const int n_valid = min(16, p.group - h0);  // heads of this block that exist
-  const int64_t prow0 = ((int64_t)b * p.n_splits + c) * p.n_h + g * p.group + h0;
-  unsigned char* wo = static_cast<unsigned char*>(p.ws_o) + prow0 * kRowBytes;
-  constexpr int kLanesPerRow = kRowBytes / 16;
-  constexpr int kRowsPerStore = 64 / kLanesPerRow;
-#pragma unroll
-  for (int r0 = 0; r0 < 16; r0 += kRowsPerStore) {
-    const int r = r0 + lane / kLanesPerRow;
-    const int c16 = (lane % kLanesPerRow) * 16;
-    if (r < n_valid)
-      *reinterpret_cast<u32x4*>(wo + r * kRowBytes + c16) = *reinterpret_cast<const u32x4*>(tile + r * kTStride + c16);
-  }
-  if (grp == 0 && head_ok) p.ws_lse[prow0 + col] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // Merge of the S split partials of each (request, head): DS workgroups per (request, head), each
@@ -407,9 +523,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   if (cv == 0 && p.lse_out) p.lse_out[r] = wsum > 0.f ? Mt + logf(wsum) : -INFINITY;  // piece 0
 }
 
+// Split kernel variants: one wave per split, four waves per split (small grids), or the
+// persistent walkers of decode_split_persist_kernel (large batches).
+enum DecodeSplitMode { kSplitOneWave, kSplitFourWaves, kSplitPersistent };
+
 template <int D, bool WS_BF16>
-void launch_decode_d(const DecodeParams& p, dim3 grid, dim3 mgrid, bool wide, hipStream_t stream) {
-  if (wide)
+void launch_decode_d(const DecodeParams& p, DecodeSplitMode mode, dim3 grid, dim3 mgrid, hipStream_t stream) {
+  if (mode == kSplitPersistent)
+    hipLaunchKernelGGL((decode_split_persist_kernel<D, WS_BF16>), grid, dim3(64), 0, stream, p);
+  else if (mode == kSplitFourWaves)
     hipLaunchKernelGGL((decode_split_kernel<D, 4, WS_BF16>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_split_kernel<D, 1, WS_BF16>), grid, dim3(64), 0, stream, p);
@@ -432,16 +554,23 @@ void launch_decode_d(const DecodeParams& p, dim3 grid, dim3 mgrid, bool wide, hi
 hipError_t launch_decode(const DecodeParams& p, int d_h, hipStream_t stream) {
   // grid sizes are checked on the host (api.cpp) to fit these 32-bit dimensions
   const int hblocks = (p.group + 15) / 16;
-  const dim3 grid(p.n_splits * p.batch, p.n_kv * hblocks);
+  dim3 grid(p.n_splits * p.batch, p.n_kv * hblocks);
   const dim3 mgrid(p.batch * p.n_h);
-  // Fewer workgroups than 8 per CU: four waves share each split.
-  const bool wide = (int64_t)grid.x * grid.y < 2048;
+  DecodeSplitMode mode = kSplitOneWave;
+  if (p.units_per_wave > 0) {
+    // the host sets units_per_wave only where the unit count fits int and one round of waves
+    const int units = p.batch * p.n_splits * p.n_kv * hblocks;
+    grid = dim3((units + p.units_per_wave - 1) / p.units_per_wave);
+    mode = kSplitPersistent;
+  } else if ((int64_t)grid.x * grid.y < 2048) {
+    mode = kSplitFourWaves;  // fewer workgroups than 8 per CU: four waves share each split
+  }
   if (d_h == 64) {
-    if (p.ws_bf16) launch_decode_d<64, true>(p, grid, mgrid, wide, stream);
-    else launch_decode_d<64, false>(p, grid, mgrid, wide, stream);
+    if (p.ws_bf16) launch_decode_d<64, true>(p, mode, grid, mgrid, stream);
+    else launch_decode_d<64, false>(p, mode, grid, mgrid, stream);
   } else {
-    if (p.ws_bf16) launch_decode_d<128, true>(p, grid, mgrid, wide, stream);
-    else launch_decode_d<128, false>(p, grid, mgrid, wide, stream);
+    if (p.ws_bf16) launch_decode_d<128, true>(p, mode, grid, mgrid, stream);
+    else launch_decode_d<128, false>(p, mode, grid, mgrid, stream);
   }
   return hipGetLastError();
 }

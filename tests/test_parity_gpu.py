@@ -390,3 +390,53 @@ def test_bf16_group_sizes_that_straddle_tiles():
 def test_decode_group_sizes_that_straddle_head_blocks():
     run_decode([1500, 37, 0], 21, 7, 128, 256, seed=14, check_splits=[0, 255])
     run_decode([800, 2049], 10, 2, 64, 32, seed=15, out="bf16", check_splits=[5])
+
+
+# Shapes whose (request, split, head block) units number 4 to 8 per SIMD of a 256-CU device take
+# the persistent split kernel (one wave per SIMD walking several units, partials stored at its end).
+@pytest.mark.parametrize("ws", ["f32", "bf16"])
+def test_decode_persistent_walkers_ragged(ws):
+    # 16 requests x 256 splits: 4 units per wave; empty requests, requests shorter than the split
+    # count (empty splits) and lengths that do not divide
+    lens = [0, 1, 255, 257, 3000, 40000, 12345, 0, 999, 65536, 31, 5000, 20000, 2, 777, 100000]
+    run_decode(lens, 16, 1, 128, 256, seed=21, check_splits=[0, 1, 128, 255], ws=ws)
+
+
+def test_decode_persistent_walkers_d64_head_blocks_and_kv_heads():
+    # D_H 64, 16 requests x 512 splits: 8 units per wave
+    lens = [int(x) for x in np.random.default_rng(22).integers(0, 20000, size=16)]
+    run_decode(lens, 8, 1, 64, 512, seed=22, check_splits=[0, 511], out="bf16")
+    # two head blocks per KV head (20 query heads per KV head): 4 units per wave
+    run_decode([3000, 0, 777, 12000, 64, 5000, 1, 9000], 20, 1, 128, 256, seed=23, check_splits=[0, 255])
+    # two KV heads of 8 query heads each: 4 units per wave
+    run_decode([2500, 1, 0, 7000, 300, 4096, 4097, 60], 16, 2, 128, 256, seed=24, check_splits=[7, 200])
+
+
+@pytest.mark.parametrize("ws", ["f32", "bf16"])
+def test_decode_persistent_walkers_equal_one_wave_splits_bitwise(ws):
+    """The persistent walkers run each split as the one-wave kernel does, so their partials and
+    merged results are bit-identical: 32 requests x 256 splits (8 units per wave, persistent)
+    against the same 32 requests inside a 65-request call (over 64 requests: one wave per split)."""
+    from context_ring_attention_amd import binding as cp
+    rng = np.random.default_rng(25)
+    lens65 = rng.integers(0, 6000, size=65).astype(np.int64)
+    lens65[[3, 17]] = 0
+    d, n_h, S = 128, 16, 256
+    res = []
+    for lens in (lens65[:32], lens65):
+        B = len(lens)
+        offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+        toks = np.arange(int(lens.sum()))
+        kc = device_tensor(25, si.TID_K, toks, (1, d), 1.0, "bf16")
+        vc = device_tensor(25, si.TID_V, toks, (1, d), 1.0, "bf16")
+        q = device_tensor(25, si.TID_Q, np.arange(B), (n_h, d), 1.0, "bf16")
+        ws_o, ws_l = cp.decode_workspace(B, n_h, d, S, ws_dtype=ws)
+        o = torch.empty(B, n_h, d, device="cuda")
+        l = torch.empty(B, n_h, device="cuda")
+        log(f"decode B={B} n_splits={S} ws={ws} (bitwise comparison of the two split kernels)")
+        cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lens).cuda(), S,
+                          scale_of(d), ws_o, ws_l, o, l)
+        torch.cuda.synchronize()
+        res.append((ws_o[:32].clone(), ws_l[:32].clone(), o[:32].clone(), l[:32].clone()))
+    for a, b, what in zip(res[0], res[1], ("split O", "split LSE", "O", "LSE")):
+        assert torch.equal(a, b), f"{what} differs between the persistent and one-wave split kernels"
