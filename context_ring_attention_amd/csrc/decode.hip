@@ -8,7 +8,10 @@
 // The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
 // against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
 // 16-head block) and walks its keys in blocks of 32; for small batches four waves share a split,
-// each taking a quarter of its keys, and combine their results in LDS:
+// each taking a quarter of its keys, and combine their results in LDS; for large batches (4 to 8
+// such units per SIMD) one wave per SIMD walks several units in turn, keeps their partials in
+// registers and stores them all at its end, so that the partial writes do not mix with the K/V
+// read stream. The walk of a unit is the same in all three forms:
 //  - K and V blocks are loaded with whole-row 16-byte non-temporal accesses (the cache is read
 //    once; the loads must not evict the split partials the merge reads back) and staged in LDS
 //    in their row-major layout;
