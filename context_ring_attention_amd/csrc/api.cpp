@@ -573,13 +573,19 @@ int cp_decode_splitkv_ex(const void* q, const void* k_cache, const void* v_cache
   p.ws_bf16 = ws_dtype == CP_BF16;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  // Large batches take the persistent split kernel: one one-wave workgroup per SIMD (four per CU,
-  // one round), each walking 4 to kDecodeMaxUnits (request, split, head block) units and storing
-  // their partials at its end. Requests are ranked by lanes, so at most 64 of them.
+  // Large batches take the persistent split kernel: one-wave workgroups, one per SIMD in each of
+  // as many rounds as needed for at most kDecodeMaxUnits (request, split, head block) units per
+  // wave, the units spread evenly over whole rounds; each wave stores its partials at its end.
+  // Used from 4 units per wave up (fewer measured no faster). Requests are ranked by lanes, so at
+  // most 64 of them; the unit count stays far inside int.
   const int64_t units = (int64_t)batch * n_splits * n_kv * ((p.group + 15) / 16);
   const int64_t slots = 4 * (int64_t)device_cus();
-  const int64_t per_wave = slots > 0 ? (units + slots - 1) / slots : 0;
-  p.units_per_wave = (batch <= 64 && per_wave >= 4 && per_wave <= cpk::kDecodeMaxUnits) ? (int)per_wave : 0;
+  int64_t per_wave = 0;
+  if (slots > 0) {
+    const int64_t rounds = (units + cpk::kDecodeMaxUnits * slots - 1) / (cpk::kDecodeMaxUnits * slots);
+    per_wave = (units + rounds * slots - 1) / (rounds * slots);
+  }
+  p.units_per_wave = (batch <= 64 && per_wave >= 4 && units <= (1 << 24)) ? (int)per_wave : 0;
   return launch_status(cpk::launch_decode(p, d_h, static_cast<hipStream_t>(stream)), "cp_decode_splitkv");
 }
 

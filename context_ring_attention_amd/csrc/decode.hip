@@ -8,10 +8,10 @@
 // The split kernel streams K and V once from HBM (the work is bandwidth-bound: 16 query heads
 // against one KV head give 16 flops per byte of cache). One wave owns one (request, split,
 // 16-head block) and walks its keys in blocks of 32; for small batches four waves share a split,
-// each taking a quarter of its keys, and combine their results in LDS; for large batches (4 to 8
-// such units per SIMD) one wave per SIMD walks several units in turn, keeps their partials in
-// registers and stores them all at its end, so that the partial writes do not mix with the K/V
-// read stream. The walk of a unit is the same in all three forms:
+// each taking a quarter of its keys, and combine their results in LDS; for large batches (4 or
+// more such units per SIMD) one wave per SIMD, in one or more rounds, walks up to 8 units in
+// turn, keeps their partials in registers and stores them all at its end, so that the partial
+// writes do not mix with the K/V read stream. The walk of a unit is the same in all three forms:
 //  - K and V blocks are loaded with whole-row 16-byte non-temporal accesses (the cache is read
 //    once; the loads must not evict the split partials the merge reads back) and staged in LDS
 //    in their row-major layout;
@@ -349,15 +349,16 @@ __device__ __forceinline__ void decode_unit_coords(const DecodeParams& p, int la
   h0 = (y - g * hblocks) * 16;
 }
 
-// Large batches (batch <= 64, 4 to kDecodeMaxUnits units per SIMD): one wave per SIMD walks
-// p.units_per_wave (request, split, 16-head block) units in turn, each as decode_split_kernel's
+// Large batches (batch <= 64, 4 or more units per SIMD): one-wave workgroups, one per SIMD in each
+// of one or more rounds, each walking p.units_per_wave (at most kDecodeMaxUnits) (request, split,
+// 16-head block) units in turn, each as decode_split_kernel's
 // one-wave walk, and keeps every finished partial (normalised O and LSE) in registers; it stores
 // them all when it is done. Units are dealt in a zigzag over the longest-first numbering (wave w
 // takes units w, 2G-1-w, 2G+w, ... of a grid of G waves), which gives every wave about the same
 // number of keys. The splits and their partials are those of decode_split_kernel; only when the
-// partials reach HBM changes: the waves finish together, so the partial writes leave in one burst
-// at the end instead of mixing with the K/V stream throughout the launch (interleaved writes slow
-// the read stream far more than their own bytes cost).
+// partials reach HBM changes: the waves of a round finish together, so the partial writes leave in
+// one burst per round instead of mixing with the K/V stream throughout the launch (interleaved
+// writes slow the read stream far more than their own bytes cost).
 template <int D, bool WS_BF16>
 __global__ __launch_bounds__(64) void decode_split_persist_kernel(const DecodeParams p) {
   using C = DecCfg<D>;

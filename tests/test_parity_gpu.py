@@ -410,20 +410,25 @@ def test_decode_persistent_walkers_d64_head_blocks_and_kv_heads():
     run_decode([3000, 0, 777, 12000, 64, 5000, 1, 9000], 20, 1, 128, 256, seed=23, check_splits=[0, 255])
     # two KV heads of 8 query heads each: 4 units per wave
     run_decode([2500, 1, 0, 7000, 300, 4096, 4097, 60], 16, 2, 128, 256, seed=24, check_splits=[7, 200])
+    # 64 requests: two rounds of waves with 8 units each
+    lens = [int(x) for x in np.random.default_rng(26).integers(0, 3000, size=64)]
+    run_decode(lens, 16, 1, 128, 256, seed=26, check_splits=[0, 255])
 
 
 @pytest.mark.parametrize("ws", ["f32", "bf16"])
-def test_decode_persistent_walkers_equal_one_wave_splits_bitwise(ws):
+@pytest.mark.parametrize("n_sub", [32, 48, 64])
+def test_decode_persistent_walkers_equal_one_wave_splits_bitwise(ws, n_sub):
     """The persistent walkers run each split as the one-wave kernel does, so their partials and
-    merged results are bit-identical: 32 requests x 256 splits (8 units per wave, persistent)
-    against the same 32 requests inside a 65-request call (over 64 requests: one wave per split)."""
+    merged results are bit-identical: n_sub requests x 256 splits (32: one round of waves with 8
+    units each; 48 and 64: two rounds with 6 and 8) against the same requests inside a
+    65-request call (over 64 requests: one wave per split)."""
     from context_ring_attention_amd import binding as cp
     rng = np.random.default_rng(25)
     lens65 = rng.integers(0, 6000, size=65).astype(np.int64)
     lens65[[3, 17]] = 0
     d, n_h, S = 128, 16, 256
     res = []
-    for lens in (lens65[:32], lens65):
+    for lens in (lens65[:n_sub], lens65):
         B = len(lens)
         offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
         toks = np.arange(int(lens.sum()))
@@ -437,6 +442,6 @@ def test_decode_persistent_walkers_equal_one_wave_splits_bitwise(ws):
         cp.decode_splitkv(q, kc, vc, torch.from_numpy(offs).cuda(), torch.from_numpy(lens).cuda(), S,
                           scale_of(d), ws_o, ws_l, o, l)
         torch.cuda.synchronize()
-        res.append((ws_o[:32].clone(), ws_l[:32].clone(), o[:32].clone(), l[:32].clone()))
+        res.append((ws_o[:n_sub].clone(), ws_l[:n_sub].clone(), o[:n_sub].clone(), l[:n_sub].clone()))
     for a, b, what in zip(res[0], res[1], ("split O", "split LSE", "O", "LSE")):
         assert torch.equal(a, b), f"{what} differs between the persistent and one-wave split kernels"
