@@ -428,6 +428,28 @@ def run_decode(torch, cp, si, seed=0):
            "workspace": "f32", "algorithmic_bytes": alg_bytes, "cached_keys": total, "batch": B,
            "n_splits": S, "by_workspace": res}
     kept = {"o": o.cpu().numpy(), "lse": l.cpu().numpy(), "lens": lens, "offs": offs}
+    del kc, vc
+    # larger batches of the same length mix (fp32 workspace)
+    out["larger_batches"] = {}
+    for Bx in (48, 64):
+        lx = si.decode_lengths(seed, Bx, cfg["len_lo"], cfg["len_hi"])
+        ox = np.concatenate([[0], np.cumsum(lx)[:-1]]).astype(np.int64)
+        tx = int(lx.sum())
+        kx = tokens_bf16(torch, si, seed, si.TID_K, np.arange(tx), (n_kv, d))[0]
+        vx = tokens_bf16(torch, si, seed, si.TID_V, np.arange(tx), (n_kv, d))[0]
+        qx = tokens_bf16(torch, si, seed, si.TID_Q, np.arange(Bx), (n_h, d))[0]
+        o_x = torch.empty(Bx, n_h, d, device="cuda")
+        l_x = torch.empty(Bx, n_h, device="cuda")
+        od, ld = torch.from_numpy(ox).cuda(), torch.from_numpy(lx).cuda()
+        ws_o, ws_l = cp.decode_workspace(Bx, n_h, d, S, ws_dtype="f32")
+        fn = lambda: cp.decode_splitkv(qx, kx, vx, od, ld, S, scale, ws_o, ws_l, o_x, l_x, check=False)
+        ms = time_reps(torch, fn, 20)
+        bx = tx * n_kv * d * 2 * 2 + Bx * n_h * d * 2 + Bx * n_h * (d * 4 + 4)
+        out["larger_batches"][str(Bx)] = {"us_per_call": round(ms * 1e3, 2), "cached_keys": tx,
+                                          "GBps": round(bx / (ms * 1e-3) / 1e9, 1),
+                                          "frac_of_hbm_peak": round(bx / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"decode B={Bx} (f32 workspace): {ms * 1e3:.1f} us, {bx / (ms * 1e-3) / 1e9:.0f} GB/s")
+        del kx, vx, ws_o, ws_l
     return out, kept
 
 
